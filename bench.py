@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Benchmark: AnchorAttention forward + backward on one MI355X.
+
+One step = one full pass of the hot path over one packed batch: position IDs,
+tile plans, RoPE, forward attention, backward preprocess, dK/dV, dQ and the
+anchor-key reduction (the library's anchor_attn_fwd + anchor_attn_bwd).
+
+Prints ONE JSON line.  `value` is fwd+bwd TFLOP/s counting only unmasked
+(query, key) pairs (14*D flops per pair and query head); inputs are resident
+in HBM before the timed region starts.  `roofline` reports the dominant
+kernel's achieved rate from HIP events recorded by the library around each of
+its launches on the call's stream during the timed steps.  `cpu_baseline`
+times the float64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (vendor figure, no sparsity)
+PEAK_HBM_GBS = 8000.0
+
+# Algorithmic flops per unmasked (query, key) pair and query head, per kernel:
+# forward: S = QK^T, O = PV (2 products); dK/dV kernel: S, dP, dV, dK (4);
+# dQ kernel: S, dP, dQ (3).  The headline counts 4 + 10 = 14 per pair.
+KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 6.0}
+KERNEL_SOURCE = {"fwd": "fwd.hip", "bwd_dkdv": "bwd.hip", "bwd_dq": "bwd.hip"}
+
+
+def _src_hash(kernel: str) -> str:
+    p = os.path.join(ROOT, "long_context_attention_doc_amd", "csrc", KERNEL_SOURCE[kernel])
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"source_sha256_16:\s*(\w+)", txt)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_bytes or m_hash.group(1) != _src_hash(kernel):
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, q, k, v, do, budget_s: float) -> dict:
+    """The float64 oracle on whole documents at the start of row 0, one query
+    head at a time until about `budget_s` seconds of CPU work.  Key gradients
+    are taken for the documents' keys; the anchor key is left out because its
+    gradient sums over every query of the row."""
+    import numpy as np
+    import oracle
+    from long_context_attention_doc_amd.accounting import unmasked_pairs_closed_form
+    lens = list(w.doc_rows[0])
+    take, tot = [], 0
+    for L in lens:
+        if tot + L > 6144 and take:
+            break
+        take.append(L)
+        tot += L
+    rows = np.arange(0, 1 + tot)
+    pairs = unmasked_pairs_closed_form([take])
+    t0 = time.perf_counter()
+    heads = 0
+    for h in range(w.Hq):
+        oracle.forward(q, k, v, w.cu_doc_lens, w.rope_base, heads=[h], rows=rows)
+        oracle.backward(q, k, v, do, w.cu_doc_lens, w.rope_base, heads=[h], q_rows=rows,
+                        k_cols=rows[1:])
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 14.0 * w.D * pairs * heads
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:   # threadpoolctl missing: report the affinity count only
+        blas = None
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas or cores, "kind": "oracle",
+        "sample": (f"row 0, anchor + first {len(take)} documents ({tot} tokens), {heads} of {w.Hq} "
+                   f"query heads, forward + backward, {dt:.1f} s; {cores} host cores visible, "
+                   f"BLAS threads {blas}"),
+        "seconds": dt,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="64k",
+                    help="tiny | 8k | 64k | 128k_gqa | short_docs (default: 64k, the headline)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+    from long_context_attention_doc_amd import api
+    from long_context_attention_doc_amd.accounting import flops_fwd_bwd
+
+    w = workloads.get(args.workload)
+    dev = torch.device("cuda:0")
+    q, k, v, do = workloads.make_tensors(w.B, w.S, w.Hq, w.Hkv, w.D, w.tensor_seed)
+    qc, kc, vc, doc = (t.to(dev) for t in (q, k, v, do))
+    cu = torch.from_numpy(w.cu_doc_lens).to(dev)
+    ws_f = torch.empty(api.workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, False), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(api.workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, True), dtype=torch.uint8, device=dev)
+
+    def step():
+        o, lse = api.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base, True, None, ws_f)
+        if w.backward:
+            api.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base, True, None, ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    api.profile_begin(64 * max(1, args.steps))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    prof = api.profile_end()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    fl = flops_fwd_bwd(w.doc_rows, w.Hq, w.D)
+    total_flops = fl["total"] if w.backward else fl["fwd"]
+    tflops = total_flops / (ms * 1e-3) / 1e12
+    tokens = w.B * w.S
+    per_kernel_ms = {k_: v_[0] / max(1, args.steps) for k_, v_ in prof.items()}
+    fwd_ms = sum(per_kernel_ms[k_] for k_ in ("status", "positions", "plan", "rope_table", "rope", "fwd")) \
+        if not w.backward else None
+
+    # dominant kernel and its roofline
+    cand = [k_ for k_ in KERNEL_FLOPS_PER_PAIR_D if prof[k_][1] > 0]
+    dom = max(cand, key=lambda k_: prof[k_][0])
+    launches = prof[dom][1]
+    avg_ms = prof[dom][0] / launches
+    algo = KERNEL_FLOPS_PER_PAIR_D[dom] * w.D * w.Hq * fl["pairs_per_head"]
+    achieved = algo / (avg_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": f"k_{dom}", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": _traffic(dom, w.name), "avg_launch_ms": avg_ms,
+                "algorithmic_flops_per_launch": algo}
+
+    out = {
+        "metric": "AnchorAttention fwd+bwd unmasked TFLOP/s at 64K (also tokens/s, % of dense bf16 MFMA peak)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "seq_len": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "rope_base": w.rope_base, "documents_per_row": len(w.doc_rows[0]),
+                   "backward": w.backward, "unmasked_pairs_per_head": fl["pairs_per_head"]},
+        "tokens_per_s": tokens / (ms * 1e-3),
+        "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "kernel_ms_per_step": {k_: round(v_, 4) for k_, v_ in per_kernel_ms.items()},
+        "roofline": roofline,
+    }
+    if fwd_ms is not None:
+        out["fwd_ms"] = fwd_ms
+    if args.cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

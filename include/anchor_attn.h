@@ -1,0 +1,173 @@
+/*
+ * anchor_attn.h -- C ABI of the AnchorAttention library for AMD MI355X (gfx950).
+ *
+ * The operation is the attention pattern of "When Precision Meets Position:
+ * BFloat16 Breaks Down RoPE in Long-Context Training" (arXiv 2411.13476), as
+ * summarised on the paper-graph architecture page of that paper ("arch page"
+ * below), section 3.4:
+ *   - "Intra-document attention with position ID reset (Figure 2, middle)":
+ *     position IDs restart at every document; the first token of a document
+ *     has ID 1.
+ *   - "Rotary Positional Embedding (RoPE)", Eq. 6: adjacent pairs (2p, 2p+1) of
+ *     q and k are rotated by pos * theta_p, theta_p = base^(-2p/D).
+ *   - "Implementation detail: where precision matters": the rotation is done
+ *     in float32 outside the attention kernel and the rotated vectors are
+ *     rounded to bfloat16 before the inner products.
+ *   - "AnchorAttention: The Shared Anchor Design", "Mask construction": every
+ *     query sees the shared anchor (the row's first token, position ID 0);
+ *     inside a document attention is causal; documents never see each other;
+ *     the anchor sees only itself.
+ *   - "Standard attention": O = softmax(scale * Q K^T + M) V; the page leaves
+ *     the 1/sqrt(D) scale out of its notation, the library applies it.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a device pointer unless its comment says "host".
+ *   - q, o, dout, dq: [B, S, Hq, D] bfloat16, contiguous.
+ *     k, v, dk, dv:   [B, S, Hkv, D] bfloat16, contiguous.
+ *     lse:            [B, Hq, S] float32 (natural log of the softmax sum,
+ *                     logits already scaled).
+ *   - D is 64 or 128; Hq is a multiple of Hkv; query head h reads kv head
+ *     h / (Hq / Hkv) (contiguous grouped-query groups).
+ *   - cu_doc_lens: int32 [n_seg + 1] segment offsets over the flattened B*S
+ *     token stream: cu[0] = 0, cu[n_seg] = B*S, strictly increasing; every
+ *     row b starts with the one-token anchor segment [b*S, b*S + 1); no
+ *     segment crosses a row.  Example for one row of 256 tokens holding
+ *     documents of 80, 100 and 75 tokens: {0, 1, 81, 181, 256}.
+ *   - causal = 1 is the method.  causal = 0 drops only the "key not after
+ *     query" rule inside a document (anchor rules unchanged).
+ *   - softmax_scale <= 0 selects 1/sqrt(D).
+ *   - All work is enqueued on `stream`; no call synchronises the device
+ *     (except anchor_attn_device_status) and no call allocates memory.  The
+ *     caller owns every buffer, including the workspace, which must be at
+ *     least the size reported by the matching *_workspace_size call and
+ *     256-byte aligned; tensors must be 16-byte aligned.
+ *   - Argument errors are reported synchronously through the return value
+ *     before anything is launched.  The content of the device-resident
+ *     cu_doc_lens is validated on the device: a violation sets the status
+ *     word in the workspace (read it with anchor_attn_device_status), every
+ *     kernel then stays in bounds and the attention outputs are filled with
+ *     NaN so that misuse is visible.
+ *   - Calls sharing one workspace on different streams race.
+ */
+#ifndef ANCHOR_ATTN_H
+#define ANCHOR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AA_OK = 0,
+  AA_EINVAL = 1,        /* null pointer, bad size, bad alignment, Hq % Hkv != 0 */
+  AA_EDOCS = 2,         /* cu_doc_lens violates the layout above (device status word) */
+  AA_EUNSUPPORTED = 3,  /* D or tile size not supported */
+  AA_EWORKSPACE = 4,    /* workspace smaller than required */
+  AA_EHIP = 5           /* a HIP runtime call or kernel launch failed */
+} aa_status;
+
+/* Tile kinds in a tile plan (uint8 values). */
+enum {
+  AA_TILE_FULL = 1,     /* every element of the tile exists and is allowed */
+  AA_TILE_PARTIAL = 2,  /* live, some elements masked, not anchor-only */
+  AA_TILE_ANCHOR = 3    /* key tile 0 whose only allowed key is the anchor column */
+};
+
+/* Human-readable text for a status code (static storage). */
+const char* anchor_attn_strerror(aa_status s);
+
+/* Library version string, e.g. "anchor_attn 0.1 gfx950" (static storage). */
+const char* anchor_attn_version(void);
+
+/* Workspace bytes needed by anchor_attn_fwd / anchor_attn_bwd for this shape.
+ * for_bwd = 0 sizes the forward, 1 the backward.  Returns 0 on bad shape. */
+size_t anchor_attn_workspace_size(int B, int S, int Hq, int Hkv, int D, int for_bwd);
+
+/* Forward pass (arch page §3.4: reset position IDs, Eq. 6 RoPE in float32
+ * rounded to bf16, Mask construction, flash-style softmax attention).
+ * Writes o [B,S,Hq,D] bf16 and lse [B,Hq,S] float32. */
+aa_status anchor_attn_fwd(const void* q, const void* k, const void* v,
+                          const int32_t* cu_doc_lens, int n_seg, double rope_base, int causal,
+                          int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+                          void* o, float* lse, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Backward pass of the same operation: given q, k, v, the forward's o and lse,
+ * and dout = dL/dO, writes dq [B,S,Hq,D], dk and dv [B,S,Hkv,D] (bf16).  Key
+ * gradients sum over the query heads of a group.  Self-contained: it rebuilds
+ * the position IDs, tile plan and rotated q/k itself. */
+aa_status anchor_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout,
+                          const int32_t* cu_doc_lens, int n_seg, double rope_base, int causal,
+                          int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+                          void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Position IDs (arch page §3.4, Figure 2 middle: reset per document; the
+ * anchor has ID 0, a document's first token ID 1).  pos: int32 [B*S].
+ * mode 0 = reset, 1 = continuous (document tokens count on across documents,
+ * Figure 2 right as the arch page describes it).  workspace needs
+ * anchor_attn_plan_workspace_size(B, S, 64, 64) bytes (for the status word). */
+aa_status anchor_attn_position_ids(const int32_t* cu_doc_lens, int n_seg, int B, int S, int mode,
+                                   int32_t* pos, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* Workspace bytes needed by anchor_attn_tile_plan. */
+size_t anchor_attn_plan_workspace_size(int B, int S, int BM, int BN);
+
+/* Upper bound on the number of live tiles of a plan: B * ceil(S/BM) * ceil(S/BN). */
+size_t anchor_attn_plan_capacity(int B, int S, int BM, int BN);
+
+/* Block-sparse tile plan (arch page §3.4, "Reduction in attention
+ * computations": only in-document pairs plus the anchor column are computed).
+ * A (query tile, key tile) pair of BM x BN elements is live when the mask
+ * allows at least one of its elements; key tile 0 is live for every query
+ * tile because every query sees the anchor.  Kinds as AA_TILE_*.
+ *   query-major: qptr int32 [B*nq + 1]; entries qptr[b*nq+qt] .. qptr[b*nq+qt+1]
+ *                of kidx int32 / kkind uint8 list the live key tiles ascending.
+ *   key-major:   kptr int32 [B*nk + 1]; qidx int32 / qkind uint8 likewise.
+ * nq = ceil(S/BM), nk = ceil(S/BN); kidx/kkind/qidx/qkind must hold
+ * anchor_attn_plan_capacity() entries; n_live (device int32) receives the
+ * number of live tiles.  BM and BN are powers of two in [16, 256]. */
+aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, int S, int BM, int BN,
+                                int causal,
+                                int32_t* qptr, int32_t* kidx, uint8_t* kkind,
+                                int32_t* kptr, int32_t* qidx, uint8_t* qkind,
+                                int32_t* n_live, void* workspace, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* RoPE stage alone (Eq. 6; angle pos*theta_p formed and reduced in float64,
+ * cos/sin rounded to float32, pair rotated in float32, result rounded to
+ * bf16 to nearest even).  x, x_rot: [B,S,H,D] bf16; pos: int32 [B*S] with
+ * 0 <= pos < S.  table: float32 scratch of S * D floats. */
+aa_status anchor_attn_rope(const void* x, const int32_t* pos, int B, int S, int H, int D,
+                           double rope_base, void* x_rot, float* table, hipStream_t stream);
+
+/* Reads the device status word of a workspace used by the calls above (this
+ * call synchronises `stream`).  *out (host) receives AA_OK or AA_EDOCS. */
+aa_status anchor_attn_device_status(const void* workspace, hipStream_t stream, int32_t* out);
+
+/* ---- optional per-kernel timing (diagnostics; not thread-safe) ----------
+ * Between anchor_attn_profile_begin() and anchor_attn_profile_end(), every
+ * kernel the calls above enqueue is bracketed by HIP events recorded on the
+ * call's stream.  begin() creates the events (it allocates; call it outside
+ * any graph capture); end() waits for them and writes, for each kernel id
+ * below, the summed milliseconds (ms[id], host) and launch count (count[id],
+ * host) for ids < n, then releases the events.  At most `max_launches`
+ * launches are recorded; later ones run untimed. */
+enum {
+  AA_K_STATUS = 0, AA_K_POSITIONS = 1, AA_K_PLAN = 2, AA_K_ROPE_TABLE = 3, AA_K_ROPE = 4,
+  AA_K_FWD = 5, AA_K_BWD_PRE = 6, AA_K_BWD_DKDV = 7, AA_K_BWD_DQ = 8, AA_K_BWD_ANCHOR = 9,
+  AA_K_COUNT = 10
+};
+aa_status anchor_attn_profile_begin(int max_launches);
+aa_status anchor_attn_profile_end(double* ms, int32_t* count, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ANCHOR_ATTN_H */

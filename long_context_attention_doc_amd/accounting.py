@@ -1,0 +1,31 @@
+"""Work accounting for the benchmark (host arithmetic on document lengths).
+
+Counting rule (paper-graph architecture page of arXiv 2411.13476, section
+3.4, "Reduction in attention computations": each token attends within its own
+document plus the anchor): in one packed row the anchor sees itself, and a
+document of N tokens contributes N(N+1)/2 causal in-document pairs plus N
+pairs with the anchor.  FLOPs count only these unmasked pairs: 4*D per pair
+and query head for the forward (two products), 10*D for the backward (five
+products, the usual flash-attention convention that includes recomputing the
+scores), 14*D in total.
+"""
+from __future__ import annotations
+
+
+def unmasked_pairs_closed_form(doc_rows, causal: bool = True) -> int:
+    total = 0
+    for lens in doc_rows:
+        total += 1
+        for n in lens:
+            total += (n * (n + 1) // 2 if causal else n * n) + n
+    return total
+
+
+def flops_fwd_bwd(doc_rows, Hq: int, D: int, causal: bool = True) -> dict:
+    pairs = unmasked_pairs_closed_form(doc_rows, causal)
+    return {
+        "pairs_per_head": pairs,
+        "fwd": 4.0 * D * Hq * pairs,
+        "bwd": 10.0 * D * Hq * pairs,
+        "total": 14.0 * D * Hq * pairs,
+    }

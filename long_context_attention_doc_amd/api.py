@@ -1,0 +1,260 @@
+"""Python binding of the AnchorAttention C ABI (include/anchor_attn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  PyTorch supplies device memory and the current stream.  The
+library must be built (``python -m long_context_attention_doc_amd.build``);
+if it is missing, every call raises instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libanchor_attn.so")
+
+AA_OK, AA_EINVAL, AA_EDOCS, AA_EUNSUPPORTED, AA_EWORKSPACE, AA_EHIP = range(6)
+TILE_FULL, TILE_PARTIAL, TILE_ANCHOR = 1, 2, 3
+
+# Tile shapes the attention kernels run with (query tile x key tile).
+FWD_TILE = (128, 64)
+DKV_TILE = (64, 128)
+
+EXPORTS = (
+    "anchor_attn_strerror", "anchor_attn_version", "anchor_attn_workspace_size",
+    "anchor_attn_fwd", "anchor_attn_bwd", "anchor_attn_position_ids",
+    "anchor_attn_plan_workspace_size", "anchor_attn_plan_capacity", "anchor_attn_tile_plan",
+    "anchor_attn_rope", "anchor_attn_device_status", "anchor_attn_profile_begin",
+    "anchor_attn_profile_end",
+)
+KERNEL_IDS = ("status", "positions", "plan", "rope_table", "rope", "fwd", "bwd_pre", "bwd_dkdv",
+              "bwd_dq", "bwd_anchor")
+
+_lib = None
+
+
+class AnchorAttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = _lib.anchor_attn_strerror(code).decode() if _lib is not None else str(code)
+        super().__init__(f"{where}: {msg} (status {code})")
+        self.code = code
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"AnchorAttention HIP library not built: {path} is missing "
+                          "(run `python -m long_context_attention_doc_amd.build`)")
+    lib = ctypes.CDLL(path)
+    P, I, D, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "anchor_attn_strerror": (ctypes.c_char_p, [I]),
+        "anchor_attn_version": (ctypes.c_char_p, []),
+        "anchor_attn_workspace_size": (Z, [I, I, I, I, I, I]),
+        "anchor_attn_fwd": (I, [P, P, P, P, I, D, I, I, I, I, I, I, F, P, P, P, Z, P]),
+        "anchor_attn_bwd": (I, [P, P, P, P, P, P, P, I, D, I, I, I, I, I, I, F, P, P, P, P, Z, P]),
+        "anchor_attn_position_ids": (I, [P, I, I, I, I, P, P, Z, P]),
+        "anchor_attn_plan_workspace_size": (Z, [I, I, I, I]),
+        "anchor_attn_plan_capacity": (Z, [I, I, I, I]),
+        "anchor_attn_tile_plan": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P]),
+        "anchor_attn_rope": (I, [P, P, I, I, I, I, D, P, P, P]),
+        "anchor_attn_device_status": (I, [P, P, P]),
+        "anchor_attn_profile_begin": (I, [I]),
+        "anchor_attn_profile_end": (I, [P, P, I]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(code: int, where: str) -> None:
+    if code != AA_OK:
+        raise AnchorAttnError(code, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev_cu(cu, device) -> torch.Tensor:
+    if not isinstance(cu, torch.Tensor):
+        cu = torch.as_tensor(cu, dtype=torch.int32)
+    return cu.to(device=device, dtype=torch.int32).contiguous()
+
+
+def _need_bf16(name: str, t: torch.Tensor, ndim: int = 4) -> None:
+    if t.dtype != torch.bfloat16 or t.dim() != ndim or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor with {ndim} dims")
+
+
+def version() -> str:
+    return load().anchor_attn_version().decode()
+
+
+def workspace_size(B: int, S: int, Hq: int, Hkv: int, D: int, for_bwd: bool) -> int:
+    n = load().anchor_attn_workspace_size(B, S, Hq, Hkv, D, int(for_bwd))
+    if n == 0:
+        raise ValueError("unsupported shape")
+    return int(n)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def anchor_attn_fwd(q, k, v, cu_doc_lens, rope_base: float, causal: bool = True,
+                    softmax_scale: float | None = None, workspace: torch.Tensor | None = None):
+    """Forward pass; returns (o [B,S,Hq,D] bf16, lse [B,Hq,S] fp32)."""
+    lib = load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_bf16(n, t)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B,S,Hkv,D] matching q")
+    cu = _dev_cu(cu_doc_lens, q.device)
+    ws_n = workspace_size(B, S, Hq, Hkv, D, False)
+    if workspace is None or workspace.numel() < ws_n:
+        workspace = _workspace(ws_n, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _check(lib.anchor_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), cu.numel() - 1,
+                               float(rope_base), int(bool(causal)), B, S, Hq, Hkv, D,
+                               float(softmax_scale or 0.0), _ptr(o), _ptr(lse), _ptr(workspace),
+                               workspace.numel(), _stream(q.device)), "anchor_attn_fwd")
+    return o, lse
+
+
+def anchor_attn_bwd(q, k, v, o, lse, dout, cu_doc_lens, rope_base: float, causal: bool = True,
+                    softmax_scale: float | None = None, workspace: torch.Tensor | None = None):
+    """Backward pass; returns (dq, dk, dv) bf16."""
+    lib = load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need_bf16(n, t)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, S) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B,Hq,S]")
+    cu = _dev_cu(cu_doc_lens, q.device)
+    ws_n = workspace_size(B, S, Hq, Hkv, D, True)
+    if workspace is None or workspace.numel() < ws_n:
+        workspace = _workspace(ws_n, q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    _check(lib.anchor_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(cu),
+                               cu.numel() - 1, float(rope_base), int(bool(causal)), B, S, Hq, Hkv,
+                               D, float(softmax_scale or 0.0), _ptr(dq), _ptr(dk), _ptr(dv),
+                               _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "anchor_attn_bwd")
+    return dq, dk, dv
+
+
+def anchor_attn_position_ids(cu_doc_lens, B: int, S: int, mode: int = 0, device="cuda"):
+    """Position IDs int32 [B*S] (mode 0 reset, 1 continuous)."""
+    lib = load()
+    cu = _dev_cu(cu_doc_lens, device)
+    pos = torch.empty(B * S, dtype=torch.int32, device=device)
+    ws = _workspace(lib.anchor_attn_plan_workspace_size(B, S, 64, 64), device)
+    _check(lib.anchor_attn_position_ids(_ptr(cu), cu.numel() - 1, B, S, mode, _ptr(pos), _ptr(ws),
+                                        ws.numel(), _stream(pos.device)),
+           "anchor_attn_position_ids")
+    return pos, ws
+
+
+def anchor_attn_tile_plan(cu_doc_lens, B: int, S: int, BM: int, BN: int, causal: bool = True,
+                          device="cuda"):
+    """Tile plan as a dict of device tensors (query-major and key-major CSR)."""
+    lib = load()
+    cu = _dev_cu(cu_doc_lens, device)
+    cap = lib.anchor_attn_plan_capacity(B, S, BM, BN)
+    if cap == 0:
+        raise ValueError("unsupported tile size")
+    nq, nk = -(-S // BM), -(-S // BN)
+    i32 = dict(dtype=torch.int32, device=device)
+    u8 = dict(dtype=torch.uint8, device=device)
+    out = {
+        "qptr": torch.empty(B * nq + 1, **i32), "kidx": torch.empty(cap, **i32),
+        "kkind": torch.empty(cap, **u8), "kptr": torch.empty(B * nk + 1, **i32),
+        "qidx": torch.empty(cap, **i32), "qkind": torch.empty(cap, **u8),
+        "n_live": torch.empty(1, **i32),
+    }
+    ws = _workspace(lib.anchor_attn_plan_workspace_size(B, S, BM, BN), device)
+    _check(lib.anchor_attn_tile_plan(_ptr(cu), cu.numel() - 1, B, S, BM, BN, int(bool(causal)),
+                                     _ptr(out["qptr"]), _ptr(out["kidx"]), _ptr(out["kkind"]),
+                                     _ptr(out["kptr"]), _ptr(out["qidx"]), _ptr(out["qkind"]),
+                                     _ptr(out["n_live"]), _ptr(ws), ws.numel(),
+                                     _stream(ws.device)), "anchor_attn_tile_plan")
+    out["workspace"] = ws
+    out["nq"], out["nk"] = nq, nk
+    return out
+
+
+def anchor_attn_rope(x, pos, rope_base: float):
+    """RoPE stage alone: x [B,S,H,D] bf16, pos int32 [B*S] -> rotated bf16."""
+    lib = load()
+    _need_bf16("x", x)
+    B, S, H, D = x.shape
+    pos = pos.to(device=x.device, dtype=torch.int32).contiguous()
+    y = torch.empty_like(x)
+    table = torch.empty(S * D, dtype=torch.float32, device=x.device)
+    _check(lib.anchor_attn_rope(_ptr(x), _ptr(pos), B, S, H, D, float(rope_base), _ptr(y),
+                                _ptr(table), _stream(x.device)), "anchor_attn_rope")
+    return y
+
+
+def anchor_attn_device_status(workspace: torch.Tensor) -> int:
+    lib = load()
+    out = ctypes.c_int32(0)
+    _check(lib.anchor_attn_device_status(_ptr(workspace), _stream(workspace.device),
+                                         ctypes.byref(out)), "anchor_attn_device_status")
+    return int(out.value)
+
+
+def profile_begin(max_launches: int = 65536) -> None:
+    _check(load().anchor_attn_profile_begin(max_launches), "anchor_attn_profile_begin")
+
+
+def profile_end() -> dict:
+    """{kernel name: (total ms, launches)} since profile_begin()."""
+    n = len(KERNEL_IDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    _check(load().anchor_attn_profile_end(ms, cnt, n), "anchor_attn_profile_end")
+    return {KERNEL_IDS[i]: (float(ms[i]), int(cnt[i])) for i in range(n)}
+
+
+class _AnchorAttnFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu, rope_base, causal, softmax_scale):
+        o, lse = anchor_attn_fwd(q, k, v, cu, rope_base, causal, softmax_scale)
+        ctx.save_for_backward(q, k, v, o, lse, cu)
+        ctx.cfg = (rope_base, causal, softmax_scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, cu = ctx.saved_tensors
+        rope_base, causal, scale = ctx.cfg
+        dq, dk, dv = anchor_attn_bwd(q, k, v, o, lse, do.contiguous(), cu, rope_base, causal, scale)
+        return dq, dk, dv, None, None, None, None
+
+
+def anchor_attention(q, k, v, cu_doc_lens, rope_base: float, causal: bool = True,
+                     softmax_scale: float | None = None):
+    """AnchorAttention with autograd: q [B,S,Hq,D], k/v [B,S,Hkv,D] bf16 on the GPU."""
+    cu = _dev_cu(cu_doc_lens, q.device)
+    return _AnchorAttnFn.apply(q, k, v, cu, float(rope_base), bool(causal), softmax_scale)

@@ -1,0 +1,401 @@
+// C ABI of the AnchorAttention library: argument validation, workspace
+// carving and the stream-ordered launch sequence of each entry point.
+// The public contract is documented in include/anchor_attn.h.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/anchor_attn.h"
+#include "aa_internal.h"
+
+namespace aa {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct PlanLayout {
+  int BM, BN, nq, nk;
+  size_t cap;
+  size_t kinds, cntq, cntk, qptr, kidx, kkind, kptr, qidx, qkind, n_live, end;
+};
+
+PlanLayout plan_layout(int B, int S, int BM, int BN, size_t base) {
+  PlanLayout p;
+  p.BM = BM;
+  p.BN = BN;
+  p.nq = (S + BM - 1) / BM;
+  p.nk = (S + BN - 1) / BN;
+  p.cap = (size_t)B * p.nq * p.nk;
+  size_t o = up(base);
+  p.kinds = o;  o = up(o + p.cap);
+  p.cntq = o;   o = up(o + (size_t)B * p.nq * 4);
+  p.cntk = o;   o = up(o + (size_t)B * p.nk * 4);
+  p.qptr = o;   o = up(o + ((size_t)B * p.nq + 1) * 4);
+  p.kidx = o;   o = up(o + p.cap * 4);
+  p.kkind = o;  o = up(o + p.cap);
+  p.kptr = o;   o = up(o + ((size_t)B * p.nk + 1) * 4);
+  p.qidx = o;   o = up(o + p.cap * 4);
+  p.qkind = o;  o = up(o + p.cap);
+  p.n_live = o; o = up(o + 4);
+  p.end = o;
+  return p;
+}
+
+PlanBufs plan_bufs(const PlanLayout& l, char* ws) {
+  PlanBufs b;
+  b.BM = l.BM; b.BN = l.BN; b.nq = l.nq; b.nk = l.nk; b.cap = l.cap;
+  b.kinds = (uint8_t*)(ws + l.kinds);
+  b.cntq = (int32_t*)(ws + l.cntq);
+  b.cntk = (int32_t*)(ws + l.cntk);
+  b.qptr = (int32_t*)(ws + l.qptr);
+  b.kidx = (int32_t*)(ws + l.kidx);
+  b.kkind = (uint8_t*)(ws + l.kkind);
+  b.kptr = (int32_t*)(ws + l.kptr);
+  b.qidx = (int32_t*)(ws + l.qidx);
+  b.qkind = (uint8_t*)(ws + l.qkind);
+  b.n_live = (int32_t*)(ws + l.n_live);
+  return b;
+}
+
+// Workspace of the attention entry points.
+struct Layout {
+  size_t status, pos, lo, hi, table, qrot, krot;
+  PlanLayout pq;        // query-major plan of the forward and dq kernels
+  PlanLayout pk;        // key-major plan of the dkdv kernel (backward only)
+  size_t dvec, ds0, pdk, pdv;
+  int nblk;
+  size_t total;
+};
+
+Layout layout(int B, int S, int Hq, int Hkv, int D, bool bwd) {
+  Layout L;
+  const size_t T = (size_t)B * S;
+  size_t o = 0;
+  L.status = o; o = up(o + 4);
+  L.pos = o;    o = up(o + T * 4);
+  L.lo = o;     o = up(o + T * 4);
+  L.hi = o;     o = up(o + T * 4);
+  L.table = o;  o = up(o + (size_t)S * D * 4);
+  L.qrot = o;   o = up(o + T * Hq * D * 2);
+  L.krot = o;   o = up(o + T * Hkv * D * 2);
+  L.pq = plan_layout(B, S, kFwdBM, kFwdBN, o);
+  o = L.pq.end;
+  L.nblk = (S + kPreRows - 1) / kPreRows;
+  if (bwd) {
+    L.pk = plan_layout(B, S, kDkvBM, kDkvBN, o);
+    o = L.pk.end;
+    L.dvec = o; o = up(o + (size_t)B * Hq * S * 4);
+    L.ds0 = o;  o = up(o + (size_t)B * Hq * S * 4);
+    L.pdk = o;  o = up(o + (size_t)B * Hq * L.nblk * D * 4);
+    L.pdv = o;  o = up(o + (size_t)B * Hq * L.nblk * D * 4);
+  } else {
+    L.pk = L.pq;
+    L.dvec = L.ds0 = L.pdk = L.pdv = 0;
+  }
+  L.total = o;
+  return L;
+}
+
+bool shape_ok(int B, int S, int Hq, int Hkv, int D) {
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq > 65535) return false;
+  if (Hq % Hkv != 0) return false;
+  if ((long long)B * S > 0x7fffffffLL) return false;
+  (void)D;
+  return true;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+__global__ void k_zero_status(int32_t* status) {
+  if (threadIdx.x == 0) status[0] = kStatusOk;
+}
+
+RopeTheta make_theta(int D, double base) {
+  RopeTheta th;
+  for (int p = 0; p < kMaxHalfD; ++p) th.t[p] = p < D / 2 ? pow(base, -2.0 * p / D) : 0.0;
+  return th;
+}
+
+#define AA_HIP(expr)                                  \
+  do {                                                \
+    if ((expr) != hipSuccess) return AA_EHIP;         \
+  } while (0)
+
+// Opt-in per-kernel timing: events recorded around every launch.
+struct Profiler {
+  bool on = false;
+  int cap = 0, used = 0;
+  hipEvent_t* ev = nullptr;   // 2 * cap events
+  int* id = nullptr;          // kernel id of each recorded launch
+};
+Profiler g_prof;
+
+// Brackets one launcher call with profiling events when profiling is on.
+#define AA_LAUNCH(kid, stream, expr)                                              \
+  do {                                                                            \
+    const bool _rec = g_prof.on && g_prof.used < g_prof.cap;                      \
+    if (_rec) AA_HIP(hipEventRecord(g_prof.ev[2 * g_prof.used], (stream)));       \
+    AA_HIP(expr);                                                                 \
+    if (_rec) {                                                                   \
+      AA_HIP(hipEventRecord(g_prof.ev[2 * g_prof.used + 1], (stream)));           \
+      g_prof.id[g_prof.used++] = (kid);                                           \
+    }                                                                             \
+  } while (0)
+
+hipError_t launch_zero_status(int32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(k_zero_status, dim3(1), dim3(64), 0, st, status);
+  return hipGetLastError();
+}
+
+// Positions, plan(s), RoPE table, rotated q and k: the prologue shared by
+// the forward and the backward.
+aa_status prologue(const Layout& L, char* ws, const void* q, const void* k,
+                   const int32_t* cu, int n_seg, double rope_base, int causal, int B, int S,
+                   int Hq, int Hkv, int D, bool bwd, hipStream_t st) {
+  int32_t* status = (int32_t*)(ws + L.status);
+  TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
+  AA_LAUNCH(AA_K_STATUS, st, launch_zero_status(status, st));
+  AA_LAUNCH(AA_K_POSITIONS, st, launch_positions(cu, n_seg, B, S, causal, 0, tt, status, st));
+  AA_LAUNCH(AA_K_PLAN, st, launch_plan(tt.lo, tt.hi, B, S, plan_bufs(L.pq, ws), false, st));
+  if (bwd) AA_LAUNCH(AA_K_PLAN, st, launch_plan(tt.lo, tt.hi, B, S, plan_bufs(L.pk, ws), true, st));
+  float* table = (float*)(ws + L.table);
+  AA_LAUNCH(AA_K_ROPE_TABLE, st, launch_rope_table(S, D, make_theta(D, rope_base), table, st));
+  AA_LAUNCH(AA_K_ROPE, st,
+            launch_rope_apply((const bf16*)q, tt.pos, table, B, S, Hq, D, (bf16*)(ws + L.qrot), st));
+  AA_LAUNCH(AA_K_ROPE, st,
+            launch_rope_apply((const bf16*)k, tt.pos, table, B, S, Hkv, D, (bf16*)(ws + L.krot), st));
+  return AA_OK;
+}
+
+}  // namespace
+}  // namespace aa
+
+using namespace aa;
+
+extern "C" {
+
+const char* anchor_attn_strerror(aa_status s) {
+  switch (s) {
+    case AA_OK: return "ok";
+    case AA_EINVAL: return "invalid argument (null pointer, size, alignment or head grouping)";
+    case AA_EDOCS: return "cu_doc_lens violates the packed-segment layout";
+    case AA_EUNSUPPORTED: return "unsupported head dimension or tile size";
+    case AA_EWORKSPACE: return "workspace too small";
+    case AA_EHIP: return "HIP runtime error or kernel launch failure";
+  }
+  return "unknown status";
+}
+
+const char* anchor_attn_version(void) { return "anchor_attn 0.1 gfx950"; }
+
+size_t anchor_attn_workspace_size(int B, int S, int Hq, int Hkv, int D, int for_bwd) {
+  if (!shape_ok(B, S, Hq, Hkv, D) || (D != 64 && D != 128)) return 0;
+  return layout(B, S, Hq, Hkv, D, for_bwd != 0).total;
+}
+
+aa_status anchor_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_doc_lens,
+                          int n_seg, double rope_base, int causal, int B, int S, int Hq, int Hkv,
+                          int D, float softmax_scale, void* o, float* lse, void* workspace,
+                          size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !cu_doc_lens || !o || !lse || !workspace) return AA_EINVAL;
+  if (!shape_ok(B, S, Hq, Hkv, D) || n_seg < B) return AA_EINVAL;
+  if (D != 64 && D != 128) return AA_EUNSUPPORTED;
+  if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(cu_doc_lens, 4) || !aligned(workspace, kAlign))
+    return AA_EINVAL;
+  const Layout L = layout(B, S, Hq, Hkv, D, false);
+  if (ws_bytes < L.total) return AA_EWORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)D);
+  char* ws = (char*)workspace;
+  aa_status s = prologue(L, ws, q, k, cu_doc_lens, n_seg, rope_base, causal, B, S, Hq, Hkv, D,
+                         false, stream);
+  if (s != AA_OK) return s;
+  TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
+  AA_LAUNCH(AA_K_FWD, stream,
+            launch_fwd((const bf16*)(ws + L.qrot), (const bf16*)(ws + L.krot), (const bf16*)v, tt,
+                       plan_bufs(L.pq, ws), (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D,
+                       scale, (bf16*)o, lse, stream));
+  return AA_OK;
+}
+
+aa_status anchor_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, const int32_t* cu_doc_lens,
+                          int n_seg, double rope_base, int causal, int B, int S, int Hq, int Hkv,
+                          int D, float softmax_scale, void* dq, void* dk, void* dv,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !cu_doc_lens || !dq || !dk || !dv || !workspace)
+    return AA_EINVAL;
+  if (!shape_ok(B, S, Hq, Hkv, D) || n_seg < B) return AA_EINVAL;
+  if (D != 64 && D != 128) return AA_EUNSUPPORTED;
+  if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
+  const void* ptrs16[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : ptrs16)
+    if (!aligned(p, 16)) return AA_EINVAL;
+  if (!aligned(lse, 4) || !aligned(cu_doc_lens, 4) || !aligned(workspace, kAlign)) return AA_EINVAL;
+  const Layout L = layout(B, S, Hq, Hkv, D, true);
+  if (ws_bytes < L.total) return AA_EWORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)D);
+  char* ws = (char*)workspace;
+  aa_status s = prologue(L, ws, q, k, cu_doc_lens, n_seg, rope_base, causal, B, S, Hq, Hkv, D,
+                         true, stream);
+  if (s != AA_OK) return s;
+  BwdArgs a;
+  a.qr = (const bf16*)(ws + L.qrot);
+  a.kr = (const bf16*)(ws + L.krot);
+  a.v = (const bf16*)v;
+  a.o = (const bf16*)o;
+  a.dout = (const bf16*)dout;
+  a.lse = lse;
+  a.table = (const float*)(ws + L.table);
+  a.tt = TokenTables{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
+  a.status = (const int32_t*)(ws + L.status);
+  a.dvec = (float*)(ws + L.dvec);
+  a.ds0 = (float*)(ws + L.ds0);
+  a.part_dk = (float*)(ws + L.pdk);
+  a.part_dv = (float*)(ws + L.pdv);
+  a.nblk = L.nblk;
+  a.dq = (bf16*)dq;
+  a.dk = (bf16*)dk;
+  a.dv = (bf16*)dv;
+  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
+  a.scale = scale;
+  AA_LAUNCH(AA_K_BWD_PRE, stream, launch_bwd_pre(a, stream));
+  AA_LAUNCH(AA_K_BWD_DKDV, stream, launch_bwd_dkdv(a, plan_bufs(L.pk, ws), stream));
+  AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
+  AA_LAUNCH(AA_K_BWD_ANCHOR, stream, launch_bwd_anchor(a, stream));
+  return AA_OK;
+}
+
+aa_status anchor_attn_position_ids(const int32_t* cu_doc_lens, int n_seg, int B, int S, int mode,
+                                   int32_t* pos, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
+  if (!cu_doc_lens || !pos || !workspace) return AA_EINVAL;
+  if (B < 1 || S < 1 || (long long)B * S > 0x7fffffffLL || n_seg < B) return AA_EINVAL;
+  if (mode != 0 && mode != 1) return AA_EINVAL;
+  if (!aligned(workspace, kAlign) || !aligned(pos, 4) || !aligned(cu_doc_lens, 4)) return AA_EINVAL;
+  const size_t T = (size_t)B * S;
+  const size_t need = up(4) + 2 * up(T * 4);
+  if (ws_bytes < need) return AA_EWORKSPACE;
+  char* ws = (char*)workspace;
+  int32_t* status = (int32_t*)ws;
+  TokenTables tt{pos, (int32_t*)(ws + up(4)), (int32_t*)(ws + up(4) + up(T * 4))};
+  hipLaunchKernelGGL(k_zero_status, dim3(1), dim3(64), 0, stream, status);
+  AA_HIP(hipGetLastError());
+  AA_HIP(launch_positions(cu_doc_lens, n_seg, B, S, 1, mode, tt, status, stream));
+  return AA_OK;
+}
+
+static bool tile_ok(int t) { return t >= 16 && t <= 256 && (t & (t - 1)) == 0; }
+
+size_t anchor_attn_plan_capacity(int B, int S, int BM, int BN) {
+  if (B < 1 || S < 1 || !tile_ok(BM) || !tile_ok(BN)) return 0;
+  return (size_t)B * ((S + BM - 1) / BM) * ((S + BN - 1) / BN);
+}
+
+size_t anchor_attn_plan_workspace_size(int B, int S, int BM, int BN) {
+  if (B < 1 || S < 1 || !tile_ok(BM) || !tile_ok(BN) || (long long)B * S > 0x7fffffffLL) return 0;
+  const size_t T = (size_t)B * S;
+  const size_t base = up(4) + 3 * up(T * 4);
+  return plan_layout(B, S, BM, BN, base).end;
+}
+
+aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, int S, int BM, int BN,
+                                int causal, int32_t* qptr, int32_t* kidx, uint8_t* kkind,
+                                int32_t* kptr, int32_t* qidx, uint8_t* qkind, int32_t* n_live,
+                                void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!cu_doc_lens || !qptr || !kidx || !kkind || !kptr || !qidx || !qkind || !n_live || !workspace)
+    return AA_EINVAL;
+  if (B < 1 || S < 1 || (long long)B * S > 0x7fffffffLL || n_seg < B) return AA_EINVAL;
+  if (!tile_ok(BM) || !tile_ok(BN)) return AA_EUNSUPPORTED;
+  if (!aligned(workspace, kAlign)) return AA_EINVAL;
+  const size_t need = anchor_attn_plan_workspace_size(B, S, BM, BN);
+  if (ws_bytes < need) return AA_EWORKSPACE;
+  char* ws = (char*)workspace;
+  const size_t T = (size_t)B * S;
+  int32_t* status = (int32_t*)ws;
+  TokenTables tt{(int32_t*)(ws + up(4)), (int32_t*)(ws + up(4) + up(T * 4)),
+                 (int32_t*)(ws + up(4) + 2 * up(T * 4))};
+  const PlanLayout pl = plan_layout(B, S, BM, BN, up(4) + 3 * up(T * 4));
+  PlanBufs pb = plan_bufs(pl, ws);
+  // the caller's output arrays replace the workspace copies
+  pb.qptr = qptr; pb.kidx = kidx; pb.kkind = kkind;
+  pb.kptr = kptr; pb.qidx = qidx; pb.qkind = qkind; pb.n_live = n_live;
+  hipLaunchKernelGGL(k_zero_status, dim3(1), dim3(64), 0, stream, status);
+  AA_HIP(hipGetLastError());
+  AA_HIP(launch_positions(cu_doc_lens, n_seg, B, S, causal, 0, tt, status, stream));
+  AA_HIP(launch_plan(tt.lo, tt.hi, B, S, pb, true, stream));
+  return AA_OK;
+}
+
+aa_status anchor_attn_rope(const void* x, const int32_t* pos, int B, int S, int H, int D,
+                           double rope_base, void* x_rot, float* table, hipStream_t stream) {
+  if (!x || !pos || !x_rot || !table) return AA_EINVAL;
+  if (B < 1 || S < 1 || H < 1) return AA_EINVAL;
+  if (D != 64 && D != 128) return AA_EUNSUPPORTED;
+  if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
+  if (!aligned(x, 16) || !aligned(x_rot, 16) || !aligned(table, 16) || !aligned(pos, 4))
+    return AA_EINVAL;
+  AA_HIP(launch_rope_table(S, D, make_theta(D, rope_base), table, stream));
+  AA_HIP(launch_rope_apply((const bf16*)x, pos, table, B, S, H, D, (bf16*)x_rot, stream));
+  return AA_OK;
+}
+
+aa_status anchor_attn_profile_begin(int max_launches) {
+  if (max_launches < 1 || max_launches > (1 << 20)) return AA_EINVAL;
+  if (g_prof.ev) return AA_EINVAL;   // already profiling
+  g_prof.ev = new hipEvent_t[2 * (size_t)max_launches];
+  g_prof.id = new int[max_launches];
+  for (int i = 0; i < 2 * max_launches; ++i) {
+    if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_prof.ev[j]);
+      delete[] g_prof.ev;
+      delete[] g_prof.id;
+      g_prof = Profiler();
+      return AA_EHIP;
+    }
+  }
+  g_prof.cap = max_launches;
+  g_prof.used = 0;
+  g_prof.on = true;
+  return AA_OK;
+}
+
+aa_status anchor_attn_profile_end(double* ms, int32_t* count, int n) {
+  if (!g_prof.ev) return AA_EINVAL;
+  aa_status rc = AA_OK;
+  for (int i = 0; i < n; ++i) {
+    if (ms) ms[i] = 0.0;
+    if (count) count[i] = 0;
+  }
+  for (int r = 0; r < g_prof.used; ++r) {
+    float t = 0.f;
+    if (hipEventSynchronize(g_prof.ev[2 * r + 1]) != hipSuccess ||
+        hipEventElapsedTime(&t, g_prof.ev[2 * r], g_prof.ev[2 * r + 1]) != hipSuccess) {
+      rc = AA_EHIP;
+      continue;
+    }
+    const int k = g_prof.id[r];
+    if (k < n) {
+      if (ms) ms[k] += t;
+      if (count) count[k] += 1;
+    }
+  }
+  for (int i = 0; i < 2 * g_prof.cap; ++i) (void)hipEventDestroy(g_prof.ev[i]);
+  delete[] g_prof.ev;
+  delete[] g_prof.id;
+  g_prof = Profiler();
+  return rc;
+}
+
+aa_status anchor_attn_device_status(const void* workspace, hipStream_t stream, int32_t* out) {
+  if (!workspace || !out) return AA_EINVAL;
+  int32_t v = 0;
+  AA_HIP(hipMemcpyAsync(&v, workspace, 4, hipMemcpyDeviceToHost, stream));
+  AA_HIP(hipStreamSynchronize(stream));
+  *out = v;
+  return AA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,253 @@
+// Forward attention kernel: flash-style online softmax over the live key tiles
+// of the tile plan, bf16 MFMA (v_mfma_f32_32x32x16_bf16) with float32
+// accumulation.
+//
+// What it computes (paper-graph architecture page of arXiv 2411.13476,
+// section 3.4, "Standard attention" and "AnchorAttention: The Shared Anchor
+// Design", "Mask construction"): for every query i of a packed row,
+//   O_i = sum_j softmax_j(scale * q'_i . k'_j) v_j
+// over the keys j the mask allows: the row's anchor (column 0) and the keys
+// of i's own document that are not after i.  q', k' are the RoPE-rotated,
+// bf16-rounded inputs.
+//
+// Work decomposition.  A workgroup of four 64-lane waves owns one
+// (row b, query head, query tile of 128 rows); each wave owns 32 queries.
+// The kernel computes the transposed score block S^T = K Q^T so that each
+// lane's 32x32 accumulator column is one query: the softmax row statistics
+// are then per lane, and the two lanes holding the same query (lane l and
+// l + 32) combine with one v_permlane32_swap.
+//   * Q^T (B operand) stays in registers for the whole key loop.
+//   * K tiles (A operand, [key][d]) and V tiles (stored transposed, [d][key],
+//     A operand of O^T = V^T P^T) are staged through LDS; the next tile's
+//     global loads are in flight while the current tile is computed.
+//   * P^T goes from the score accumulators straight into the B operand of
+//     the second product: the key order inside a 16-key step is the
+//     accumulator's own row order (keys 0-3 and 8-11 in lanes 0-31, keys 4-7
+//     and 12-15 in lanes 32-63), and the V^T operand is read in that order.
+//   * The anchor column is folded in before the loop as the softmax's
+//     starting point (m = s_i0, l = 1, acc = v_0); inside the loop column 0
+//     is outside every query's document interval, so it is never counted
+//     twice.  Key tiles that see only the anchor are skipped.
+#include "aa_internal.h"
+
+namespace aa {
+
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_fwd(
+    const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
+    const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
+    const int32_t* __restrict__ qptr, const int32_t* __restrict__ kidx,
+    const uint8_t* __restrict__ kkind, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
+    int nq, float scale_log2, bf16* __restrict__ o, float* __restrict__ lse) {
+  constexpr int BM = kFwdBM, BN = kFwdBN;
+  constexpr int KST = D + 8;     // K tile row stride in bf16 (16 bytes of padding)
+  constexpr int VST = BN + 4;    // V^T tile row stride in bf16
+  constexpr int NKK = D / 16;    // 16-wide reduction steps over d
+  constexpr int NDB = D / 32;    // 32-row blocks of d in O^T
+  constexpr int NKB = BN / 32;   // 32-key blocks of a key tile
+  constexpr int KCH = BN * D / 8 / 256;          // 16-byte K chunks per thread
+  constexpr int VGROUPS = (BN / 4) * (D / 8);    // 4 keys x 8 features per group
+  __shared__ __align__(16) bf16 Ks[BN * KST];
+  __shared__ __align__(16) bf16 Vt[D * VST];
+
+  const int tile = blockIdx.x;   // b * nq + qt
+  const int hq = blockIdx.y;
+  const int b = tile / nq, qt = tile % nq;
+  const int hkv = hq / (Hq / Hkv);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, col = lane & 31;
+  const int qrow = qt * BM + wave * 32 + col;
+  const bool qvalid = qrow < S;
+  const size_t tok = (size_t)b * S + (qvalid ? qrow : S - 1);
+  int qlo = lo[tok], qhi = hi[tok];
+  if (!qvalid) { qlo = 1; qhi = 0; }
+  const bool bad = status[0] != kStatusOk;
+
+  // Q^T operand: lane holds query `col`, features 16*kk + 8*h + i.
+  bf16x8 qf[NKK];
+  {
+    const bf16* qp = qr + (tok * Hq + hq) * D + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk);
+  }
+
+  // Anchor column: s_i0 = q'_i . k'_0 (k'_0 = k_0, its position is 0).
+  const size_t tok0 = (size_t)b * S;
+  float m, l;
+  f32x16 acc[NDB];
+  {
+    const bf16* k0 = kr + (tok0 * Hkv + hkv) * D + 8 * h;
+    float s0 = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const bf16x8 kv = *(const bf16x8*)(k0 + 16 * kk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s0 += (float)qf[kk][i] * (float)kv[i];
+    }
+    s0 += partner(s0);
+    m = s0 * scale_log2;
+    l = h == 0 ? 1.f : 0.f;          // each lane keeps half of the row sum
+    const bf16* v0 = v + (tok0 * Hkv + hkv) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        acc[db][j] = (float)v0[32 * db + 8 * (j >> 2) + 4 * h + (j & 3)];
+  }
+
+  // Staging registers for the next key tile.
+  bf16x8 kreg[KCH];
+  bf16x8 vreg[4];
+  const size_t kv_row_stride = (size_t)Hkv * D;
+  const bf16* kbase = kr + tok0 * kv_row_stride + hkv * D;
+  const bf16* vbase = v + tok0 * kv_row_stride + hkv * D;
+  const int vg_key = (tid / (D / 8)) * 4, vg_d = (tid % (D / 8)) * 8;
+
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / (D / 8), ch = c % (D / 8);
+      const int key = min(kt * BN + r, S - 1);
+      kreg[u] = *(const bf16x8*)(kbase + key * kv_row_stride + ch * 8);
+    }
+    if (tid < VGROUPS) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = min(kt * BN + vg_key + r, S - 1);
+        vreg[r] = *(const bf16x8*)(vbase + key * kv_row_stride + vg_d);
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / (D / 8), ch = c % (D / 8);
+      *(bf16x8*)(Ks + r * KST + ch * 8) = kreg[u];
+    }
+    if (tid < VGROUPS) {
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        bf16x4 w;
+        w[0] = vreg[0][dd]; w[1] = vreg[1][dd]; w[2] = vreg[2][dd]; w[3] = vreg[3][dd];
+        *(bf16x4*)(Vt + (vg_d + dd) * VST + vg_key) = w;
+      }
+    }
+  };
+
+  int e = qptr[tile];
+  const int e_end = qptr[tile + 1];
+  if (e < e_end && kkind[e] == kTileAnchor) ++e;   // only key tile 0 can be anchor-only
+  if (e < e_end) gload(kidx[e]);
+
+  while (e < e_end) {
+    const int kt = kidx[e];
+    const bool need_mask = kkind[e] != kTileFull || kt == 0;
+    __syncthreads();                 // every wave is done with the previous tile
+    lstore();
+    __syncthreads();
+    if (e + 1 < e_end) gload(kidx[e + 1]);
+
+    // S^T = K Q^T for this wave's 32 queries and the BN keys of the tile.
+    f32x16 st[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st[kb][j] = 0.f;
+      const bf16* ka = Ks + (kb * 32 + col) * KST + 8 * h;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) st[kb] = mfma32(*(const bf16x8*)(ka + 16 * kk), qf[kk], st[kb]);
+    }
+
+    // Scale to log2 units, mask, tile max.
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float t = st[kb][j] * scale_log2;
+        if (need_mask) {
+          const int key = kt * BN + kb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+          t = (key >= qlo && key <= qhi) ? t : -INFINITY;
+        }
+        st[kb][j] = t;
+        mt = fmaxf(mt, t);
+      }
+    mt = fmaxf(mt, partner(mt));
+    const float m_new = fmaxf(m, mt);     // m is finite: it started at the anchor logit
+    const float factor = exp2f(m - m_new);
+    m = m_new;
+
+    // P^T = exp2(t - m) as bf16 B operands, one per 16-key step.
+    bf16x8 pb[BN / 16];
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = exp2f(st[kb][j] - m_new);
+        ls += p;
+        pb[2 * kb + (j >> 3)][j & 7] = (bf16)p;
+      }
+    l = l * factor + ls;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[db][j] *= factor;
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const bf16* va = Vt + (32 * db + col) * VST + 4 * h;
+#pragma unroll
+      for (int c = 0; c < BN / 16; ++c) {
+        const bf16x4 lo4 = *(const bf16x4*)(va + 16 * c);
+        const bf16x4 hi4 = *(const bf16x4*)(va + 16 * c + 8);
+        bf16x8 a;
+        a[0] = lo4[0]; a[1] = lo4[1]; a[2] = lo4[2]; a[3] = lo4[3];
+        a[4] = hi4[0]; a[5] = hi4[1]; a[6] = hi4[2]; a[7] = hi4[3];
+        acc[db] = mfma32(a, pb[c], acc[db]);
+      }
+    }
+    ++e;
+  }
+
+  // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.
+  const float lt = l + partner(l);
+  const float inv = 1.f / lt;
+  if (qvalid) {
+    bf16* op = o + (tok * Hq + hq) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = (bf16)(bad ? NAN : acc[db][4 * g + r] * inv);
+        *(bf16x4*)(op + 32 * db + 8 * g + 4 * h) = w;
+      }
+    if (h == 0) {
+      const float val = (m + __log2f(lt)) * 0.69314718055994530942f;
+      lse[((size_t)b * Hq + hq) * S + qrow] = bad ? NAN : val;
+    }
+  }
+}
+
+hipError_t launch_fwd(const bf16* qr, const bf16* kr, const bf16* v, TokenTables tt,
+                      const PlanBufs& pb, const int32_t* status, int B, int S, int Hq, int Hkv,
+                      int D, float scale, bf16* o, float* lse, hipStream_t st) {
+  const float scale_log2 = scale * 1.44269504088896340736f;
+  const dim3 grid(B * pb.nq, Hq);
+  if (D == 128) {
+    hipLaunchKernelGGL(k_fwd<128>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
+                       pb.kidx, pb.kkind, status, S, Hq, Hkv, pb.nq, scale_log2, o, lse);
+  } else {
+    hipLaunchKernelGGL(k_fwd<64>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
+                       pb.kidx, pb.kkind, status, S, Hq, Hkv, pb.nq, scale_log2, o, lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace aa

@@ -1,0 +1,219 @@
+// Position IDs and the block-sparse tile plan.
+//
+// Position IDs follow the paper-graph architecture page of arXiv 2411.13476,
+// section 3.4, "Intra-document attention with position ID reset (Figure 2,
+// middle)": IDs restart at every document and a document's first token gets
+// ID 1; the shared anchor (section 3.4, "AnchorAttention: The Shared Anchor
+// Design") keeps ID 0.  The mask is the page's "Mask construction": every
+// query sees its row's anchor, causal keys of its own document, nothing else.
+//
+// Because documents are contiguous segments, what query t sees besides the
+// anchor is one closed interval of keys [lo[t], hi[t]] (row-local); the tile
+// plan and the attention kernels use only these intervals.
+#include "aa_internal.h"
+
+namespace aa {
+
+// One thread per token: segment lookup by binary search over cu_doc_lens,
+// position ID, visible-key interval, and validation of the segment layout.
+// Every derived index is clamped into the row so that later kernels stay in
+// bounds even when cu_doc_lens is invalid (the status word reports it).
+__global__ void k_positions(const int32_t* __restrict__ cu, int n_seg, int B, int S, int causal,
+                            int mode, int32_t* __restrict__ pos, int32_t* __restrict__ lo,
+                            int32_t* __restrict__ hi, int32_t* __restrict__ status) {
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)B * S;
+  if (t < n_seg) {
+    if (cu[t] >= cu[t + 1]) status[0] = kStatusBadDocs;
+  }
+  if (t == 0) {
+    if (cu[0] != 0 || (long long)cu[n_seg] != total) status[0] = kStatusBadDocs;
+  }
+  if (t >= total) return;
+  int a = 0, bnd = n_seg - 1;             // largest k with cu[k] <= t
+  while (a < bnd) {
+    const int mid = (a + bnd + 1) >> 1;
+    if ((long long)cu[mid] <= t) a = mid; else bnd = mid - 1;
+  }
+  const long long s = cu[a], e = cu[a + 1];
+  const long long rs = (t / S) * (long long)S;
+  bool bad = !(s <= t && t < e && s >= rs && e <= rs + S);
+  if (t == rs && e != rs + 1) bad = true;          // the anchor is a segment of its own
+  if (t == rs + 1 && s != t) bad = true;           // so the next segment starts right after it
+  if (bad) status[0] = kStatusBadDocs;
+  const int local = (int)(t - rs);
+  int p, l, h;
+  if (t == rs) {
+    p = 0; l = 1; h = 0;                           // anchor: sees only itself (column 0)
+  } else {
+    long long sl = s - rs, el = e - rs;            // row-local segment [sl, el)
+    sl = sl < 1 ? 1 : (sl > local ? local : sl);
+    el = el > S ? S : (el <= local ? local + 1 : el);
+    p = mode == 0 ? (int)(local - sl + 1) : local;
+    l = (int)sl;
+    h = causal ? local : (int)(el - 1);
+  }
+  pos[t] = p;
+  lo[t] = l;
+  hi[t] = h;
+}
+
+// One workgroup per (row b, query tile qt): classify every key tile.
+// A tile is live when some query row of it sees some key of it (the anchor
+// column 0 is seen by every query); FULL when all BM x BN elements exist and
+// are seen; ANCHOR when it is key tile 0 and only column 0 is seen; PARTIAL
+// otherwise.  Also counts the live tiles of the query tile.
+__global__ void k_tile_kinds(const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
+                             int S, int BM, int BN, int nq, int nk, uint8_t* __restrict__ kinds,
+                             int32_t* __restrict__ cntq) {
+  __shared__ int slo[256], shi[256];
+  __shared__ int wcount[8];
+  const int tile = blockIdx.x;            // b * nq + qt
+  const int b = tile / nq, qt = tile % nq;
+  const int r0 = qt * BM;
+  const int nrows = min(BM, S - r0);
+  for (int r = threadIdx.x; r < BM; r += blockDim.x) {
+    if (r < nrows) {
+      const size_t t = (size_t)b * S + r0 + r;
+      slo[r] = lo[t];
+      shi[r] = hi[t];
+    }
+  }
+  __syncthreads();
+  int cnt = 0;
+  for (int kt = threadIdx.x; kt < nk; kt += blockDim.x) {
+    const int c0 = kt * BN;
+    const int c1 = min(S, c0 + BN) - 1;
+    const bool cols_exist = (c0 + BN) <= S;
+    bool any_live = false, any_doc = false, all_full = nrows == BM && cols_exist;
+    for (int r = 0; r < nrows; ++r) {
+      const int a = max(slo[r], c0), z = min(shi[r], c1);
+      const int ndoc = z >= a ? z - a + 1 : 0;
+      const int n = ndoc + (kt == 0 ? 1 : 0);
+      any_live |= n > 0;
+      any_doc |= ndoc > 0;
+      all_full &= n == BN;
+    }
+    uint8_t kind = 0;
+    if (any_live) kind = all_full ? kTileFull : ((kt == 0 && !any_doc) ? kTileAnchor : kTilePartial);
+    kinds[(size_t)tile * nk + kt] = kind;
+    cnt += kind != 0;
+  }
+  // block reduction of the live count
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  if ((threadIdx.x & 63) == 0) wcount[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += wcount[w];
+    cntq[tile] = tot;
+  }
+}
+
+// One thread per (row b, key tile kt): live tiles in the key-major direction.
+__global__ void k_count_keymajor(const uint8_t* __restrict__ kinds, int B, int nq, int nk,
+                                 int32_t* __restrict__ cntk) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * nk) return;
+  const int b = i / nk, kt = i % nk;
+  int c = 0;
+  for (int qt = 0; qt < nq; ++qt) c += kinds[((size_t)b * nq + qt) * nk + kt] != 0;
+  cntk[i] = c;
+}
+
+// Single-workgroup exclusive scan: ptr[i] = sum(cnt[0..i)), ptr[n] = total.
+__global__ void k_scan(const int32_t* __restrict__ cnt, int n, int32_t* __restrict__ ptr,
+                       int32_t* __restrict__ total_out) {
+  __shared__ int buf[1024];
+  __shared__ int carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += 1024) {
+    const int i = base + threadIdx.x;
+    const int x = i < n ? cnt[i] : 0;
+    buf[threadIdx.x] = x;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int y = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+      __syncthreads();
+      buf[threadIdx.x] += y;
+      __syncthreads();
+    }
+    if (i < n) ptr[i] = carry + buf[threadIdx.x] - x;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry += buf[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    ptr[n] = carry;
+    if (total_out) total_out[0] = carry;
+  }
+}
+
+// Query-major fill: one thread per (b, qt) walks its key tiles ascending.
+__global__ void k_fill_querymajor(const uint8_t* __restrict__ kinds, int B, int nq, int nk,
+                                  const int32_t* __restrict__ qptr, int32_t* __restrict__ kidx,
+                                  uint8_t* __restrict__ kkind) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * nq) return;
+  int w = qptr[i];
+  const uint8_t* row = kinds + (size_t)i * nk;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint8_t k = row[kt];
+    if (k) {
+      kidx[w] = kt;
+      kkind[w] = k;
+      ++w;
+    }
+  }
+}
+
+// Key-major fill: one thread per (b, kt) walks its query tiles ascending.
+__global__ void k_fill_keymajor(const uint8_t* __restrict__ kinds, int B, int nq, int nk,
+                                const int32_t* __restrict__ kptr, int32_t* __restrict__ qidx,
+                                uint8_t* __restrict__ qkind) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * nk) return;
+  const int b = i / nk, kt = i % nk;
+  int w = kptr[i];
+  for (int qt = 0; qt < nq; ++qt) {
+    const uint8_t k = kinds[((size_t)b * nq + qt) * nk + kt];
+    if (k) {
+      qidx[w] = qt;
+      qkind[w] = k;
+      ++w;
+    }
+  }
+}
+
+hipError_t launch_positions(const int32_t* cu, int n_seg, int B, int S, int causal, int mode,
+                            TokenTables tt, int32_t* status, hipStream_t st) {
+  const long long total = (long long)B * S;
+  const long long n = total > n_seg ? total : n_seg;
+  const int threads = 256;
+  const unsigned blocks = (unsigned)((n + threads - 1) / threads);
+  hipLaunchKernelGGL(k_positions, dim3(blocks), dim3(threads), 0, st, cu, n_seg, B, S, causal,
+                     mode, tt.pos, tt.lo, tt.hi, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const int32_t* lo, const int32_t* hi, int B, int S, PlanBufs pb,
+                       bool key_major, hipStream_t st) {
+  const int nq = pb.nq, nk = pb.nk;
+  hipLaunchKernelGGL(k_tile_kinds, dim3(B * nq), dim3(256), 0, st, lo, hi, S, pb.BM, pb.BN, nq,
+                     nk, pb.kinds, pb.cntq);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pb.cntq, B * nq, pb.qptr, pb.n_live);
+  hipLaunchKernelGGL(k_fill_querymajor, dim3((B * nq + 127) / 128), dim3(128), 0, st, pb.kinds,
+                     B, nq, nk, pb.qptr, pb.kidx, pb.kkind);
+  if (key_major) {
+    hipLaunchKernelGGL(k_count_keymajor, dim3((B * nk + 127) / 128), dim3(128), 0, st, pb.kinds,
+                       B, nq, nk, pb.cntk);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pb.cntk, B * nk, pb.kptr,
+                       (int32_t*)nullptr);
+    hipLaunchKernelGGL(k_fill_keymajor, dim3((B * nk + 127) / 128), dim3(128), 0, st, pb.kinds,
+                       B, nq, nk, pb.kptr, pb.qidx, pb.qkind);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace aa

@@ -1,0 +1,77 @@
+// RoPE stage: Eq. 6 of "When Precision Meets Position" (arXiv 2411.13476), as
+// given on the paper-graph architecture page, section 3.4: block p of the
+// block-diagonal rotation R_{i,theta} turns the adjacent pair (2p, 2p+1) by
+// i * theta_p, theta_p = base^(-2p/d).  Section 3.4, "Implementation detail:
+// where precision matters": the rotation runs in float32 outside the
+// attention kernel and the rotated vectors are rounded to bfloat16.
+//
+// Precision of this implementation: the angle pos * theta_p is formed and
+// range-reduced in float64 (a float32 product would already be off by up to
+// ~4e-3 rad at position 65535), cos and sin are rounded to float32, the pair
+// is rotated with float32 fused multiply-adds and the result is rounded to
+// bfloat16 to nearest even.
+//
+// The cos/sin table is indexed by position ID (not by token): positions are
+// row-local and below S, and every head and token with that ID shares it.
+#include "aa_internal.h"
+
+namespace aa {
+
+// table[(pos * (D/2) + p) * 2 + {0,1}] = {cos, sin}(pos * theta_p)
+__global__ void k_rope_table(int S, int half, RopeTheta th, float* __restrict__ table) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)S * half) return;
+  const int p = (int)(i % half);
+  const long long pos = i / half;
+  const double ang = (double)pos * th.t[p];
+  double s, c;
+  sincos(ang, &s, &c);
+  table[2 * i] = (float)c;
+  table[2 * i + 1] = (float)s;
+}
+
+// One thread per 8 consecutive features (4 pairs) of one (token, head).
+__global__ void k_rope_apply(const bf16* __restrict__ x, const int32_t* __restrict__ pos,
+                             const float* __restrict__ table, long long n_chunks, int S, int H,
+                             int D, bf16* __restrict__ y) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_chunks) return;
+  const int chunks_per_tok = H * D / 8;
+  const long long tok = i / chunks_per_tok;
+  const int within = (int)(i % chunks_per_tok);
+  const int d0 = (within % (D / 8)) * 8;
+  const int p = min(max(pos[tok], 0), S - 1);     // table rows exist for 0 <= pos < S
+  const bf16x8 xv = *(const bf16x8*)(x + i * 8);
+  const f32x4* tb = (const f32x4*)(table + ((size_t)p * (D / 2) + d0 / 2) * 2);
+  const f32x4 cs01 = tb[0];   // cos0 sin0 cos1 sin1
+  const f32x4 cs23 = tb[1];
+  bf16x8 out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float c = q < 2 ? cs01[2 * (q & 1)] : cs23[2 * (q & 1)];
+    const float s = q < 2 ? cs01[2 * (q & 1) + 1] : cs23[2 * (q & 1) + 1];
+    const float x0 = (float)xv[2 * q], x1 = (float)xv[2 * q + 1];
+    out[2 * q] = (bf16)__builtin_fmaf(x0, c, -x1 * s);
+    out[2 * q + 1] = (bf16)__builtin_fmaf(x0, s, x1 * c);
+  }
+  *(bf16x8*)(y + i * 8) = out;
+}
+
+hipError_t launch_rope_table(int S, int D, const RopeTheta& th, float* table, hipStream_t st) {
+  const long long n = (long long)S * (D / 2);
+  const int threads = 256;
+  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0,
+                     st, S, D / 2, th, table);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_apply(const bf16* x, const int32_t* pos, const float* table, int B, int S,
+                             int H, int D, bf16* x_rot, hipStream_t st) {
+  const long long n = (long long)B * S * H * D / 8;
+  const int threads = 256;
+  hipLaunchKernelGGL(k_rope_apply, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0,
+                     st, x, pos, table, n, S, H, D, x_rot);
+  return hipGetLastError();
+}
+
+}  // namespace aa

@@ -226,8 +226,11 @@ def forward(q, k, v, cu, rope_base: float, causal: bool = True, scale: float | N
     lse = np.zeros((len(heads), len(rows)))
     for hi, h in enumerate(heads):
         g = h * Hkv // Hq
+        kr_of = {}
         for b, rb in _blocks_of(rows, S, block):
-            kr = rope(k[b, :, g, :], pos[b * S:(b + 1) * S], rope_base)
+            if b not in kr_of:      # rotated keys of this row, once per (head, row)
+                kr_of = {b: rope(k[b, :, g, :], pos[b * S:(b + 1) * S], rope_base)}
+            kr = kr_of[b]
             vv = v[b, :, g, :]
             _, _, _, _, ob, lb = _row_block_forward(q[b, :, h, :], kr, vv, cu, B, S, rb, b, pos,
                                                      rope_base, scale, causal)
@@ -277,8 +280,11 @@ def backward(q, k, v, do, cu, rope_base: float, causal: bool = True, scale: floa
 
     for hi, h in enumerate(heads):
         g = h * Hkv // Hq
+        kr_of = {}
         for b, rb in _blocks_of(need_rows, S, block):
-            kr = rope(k[b, :, g, :], pos[b * S:(b + 1) * S], rope_base)
+            if b not in kr_of:
+                kr_of = {b: rope(k[b, :, g, :], pos[b * S:(b + 1) * S], rope_base)}
+            kr = kr_of[b]
             vv = v[b, :, g, :]
             qr, cols, m_allowed, p, o, _ = _row_block_forward(q[b, :, h, :], kr, vv, cu, B, S, rb, b,
                                                                pos, rope_base, scale, causal)
@@ -311,6 +317,45 @@ def rotated_bf16_reference(x, pos, base: float) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # Block-sparse tile plan, by brute force over the explicit mask
 # ----------------------------------------------------------------------------
+def _classify(m: np.ndarray, e: np.ndarray, kt: int) -> int:
+    """Kind of one tile from its allowed / exists element masks [BM, BN]."""
+    if not m.any():
+        return KIND_NONE
+    if e.all() and m.all():
+        return KIND_FULL
+    if kt == 0 and not m[:, 1:].any():
+        return KIND_ANCHOR
+    return KIND_PARTIAL
+
+
+def tile_kinds_row(cu, B: int, S: int, BM: int, BN: int, b: int, qt: int,
+                   causal: bool = True) -> np.ndarray:
+    """Kinds of every key tile for query tile qt of row b, from the dense mask."""
+    nk = -(-S // BN)
+    rows = np.arange(b * S + qt * BM, b * S + min(S, (qt + 1) * BM))
+    cols = np.arange(b * S, (b + 1) * S)
+    m = np.zeros((BM, nk * BN), dtype=bool)
+    e = np.zeros((BM, nk * BN), dtype=bool)
+    m[:len(rows), :S] = allowed(cu, B, S, rows, cols, causal)
+    e[:len(rows), :S] = True
+    return np.array([_classify(m[:, kt * BN:(kt + 1) * BN], e[:, kt * BN:(kt + 1) * BN], kt)
+                     for kt in range(nk)], dtype=np.uint8)
+
+
+def tile_kinds_col(cu, B: int, S: int, BM: int, BN: int, b: int, kt: int,
+                   causal: bool = True) -> np.ndarray:
+    """Kinds of every query tile for key tile kt of row b, from the dense mask."""
+    nq = -(-S // BM)
+    cols = np.arange(b * S + kt * BN, b * S + min(S, (kt + 1) * BN))
+    rows = np.arange(b * S, (b + 1) * S)
+    m = np.zeros((nq * BM, BN), dtype=bool)
+    e = np.zeros((nq * BM, BN), dtype=bool)
+    m[:S, :len(cols)] = allowed(cu, B, S, rows, cols, causal)
+    e[:S, :len(cols)] = True
+    return np.array([_classify(m[qt * BM:(qt + 1) * BM], e[qt * BM:(qt + 1) * BM], kt)
+                     for qt in range(nq)], dtype=np.uint8)
+
+
 def tile_plan(cu, B: int, S: int, BM: int, BN: int, causal: bool = True):
     """Live (query-tile, key-tile) pairs and their kinds, from the dense mask.
 
@@ -325,25 +370,8 @@ def tile_plan(cu, B: int, S: int, BM: int, BN: int, causal: bool = True):
     nk = -(-S // BN)
     kinds = np.zeros((B, nq, nk), dtype=np.uint8)
     for b in range(B):
-        cols = np.arange(b * S, (b + 1) * S)
         for qt in range(nq):
-            rows = np.arange(b * S + qt * BM, b * S + min(S, (qt + 1) * BM))
-            m = np.zeros((BM, nk * BN), dtype=bool)
-            exists = np.zeros((BM, nk * BN), dtype=bool)
-            m[:len(rows), :S] = allowed(cu, B, S, rows, cols, causal)
-            exists[:len(rows), :S] = True
-            m3 = m.reshape(BM, nk, BN)
-            e3 = exists.reshape(BM, nk, BN)
-            for kt in range(nk):
-                t = m3[:, kt, :]
-                if not t.any():
-                    continue
-                if e3[:, kt, :].all() and t.all():
-                    kinds[b, qt, kt] = KIND_FULL
-                elif kt == 0 and not t[:, 1:].any():
-                    kinds[b, qt, kt] = KIND_ANCHOR
-                else:
-                    kinds[b, qt, kt] = KIND_PARTIAL
+            kinds[b, qt] = tile_kinds_row(cu, B, S, BM, BN, b, qt, causal)
     qptr = [0]
     kidx, kkind = [], []
     for b in range(B):

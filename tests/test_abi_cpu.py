@@ -1,0 +1,79 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, and rejects bad arguments before launching anything (these calls
+return before any HIP runtime call, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "anchor_attn.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(anchor_attn_\w+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from long_context_attention_doc_amd import api
+    return api.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("anchor_attn_fwd", "anchor_attn_bwd", "anchor_attn_position_ids",
+              "anchor_attn_tile_plan", "anchor_attn_rope", "anchor_attn_workspace_size"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from long_context_attention_doc_amd import api
+    names = _declared()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(api.EXPORTS) == names
+
+
+def test_version_and_strerror(lib):
+    assert b"gfx950" in lib.anchor_attn_version()
+    for code in range(6):
+        assert lib.anchor_attn_strerror(code)
+
+
+def test_workspace_sizes(lib):
+    f = lib.anchor_attn_workspace_size
+    assert f(1, 65536, 32, 32, 128, 0) > 0
+    assert f(1, 65536, 32, 32, 128, 1) > f(1, 65536, 32, 32, 128, 0)
+    assert f(1, 256, 32, 8, 96, 0) == 0        # unsupported D
+    assert f(1, 256, 30, 8, 128, 0) == 0       # Hq % Hkv != 0
+    assert lib.anchor_attn_plan_capacity(1, 300, 64, 128) == 5 * 3
+    assert lib.anchor_attn_plan_capacity(1, 300, 48, 128) == 0
+
+
+def test_argument_errors_before_launch(lib):
+    from long_context_attention_doc_amd import api
+    P = ctypes.c_void_p
+    fake = P(0x1000)          # never dereferenced: every call below fails validation first
+    def fwd(q=fake, Hq=4, Hkv=2, D=128, ws=fake, wsn=1 << 40, base=1e4, n_seg=4):
+        return lib.anchor_attn_fwd(q, fake, fake, fake, n_seg, base, 1, 1, 256, Hq, Hkv, D, 0.0,
+                                   fake, fake, ws, wsn, None)
+    assert fwd(q=None) == api.AA_EINVAL
+    assert fwd(Hq=3) == api.AA_EINVAL
+    assert fwd(D=96) == api.AA_EUNSUPPORTED
+    assert fwd(wsn=16) == api.AA_EWORKSPACE
+    assert fwd(base=-1.0) == api.AA_EINVAL
+    assert fwd(ws=P(0x1010)) == api.AA_EINVAL          # workspace not 256-byte aligned
+    assert fwd(q=P(0x1002)) == api.AA_EINVAL           # tensor not 16-byte aligned
+    assert fwd(n_seg=0) == api.AA_EINVAL
+    rc = lib.anchor_attn_bwd(fake, fake, fake, fake, fake, None, fake, 4, 1e4, 1, 1, 256, 4, 2, 128,
+                             0.0, fake, fake, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    rc = lib.anchor_attn_tile_plan(fake, 4, 1, 256, 48, 64, 1, fake, fake, fake, fake, fake, fake,
+                                   fake, fake, 1 << 40, None)
+    assert rc == api.AA_EUNSUPPORTED
+    rc = lib.anchor_attn_rope(fake, fake, 1, 256, 2, 80, 1e4, fake, fake, None)
+    assert rc == api.AA_EUNSUPPORTED

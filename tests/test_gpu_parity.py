@@ -1,0 +1,155 @@
+"""Forward and backward through the C ABI against the float64 oracle.
+
+Bars: max|O - O_ref| <= 4e-3 max|O_ref|; dq, dk, dv within 1e-2 relative
+Frobenius error; LSE within 5e-2 absolute (bf16 rounding of the rotated q, k
+moves a logit by ~4e-3 per standard deviation, see the design notes).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from _helpers import f64, o_err, rel_frob, say
+
+pytestmark = pytest.mark.gpu
+
+O_TOL, G_TOL, LSE_TOL = 4e-3, 1e-2, 5e-2
+
+
+def _small_cases():
+    rng = np.random.default_rng(2024)
+    return [
+        # name, B, S, Hq, Hkv, D, rows, base, causal
+        ("tiny", 1, 256, 2, 2, 64, [[80, 100, 75]], 1e4, True),
+        ("ragged_gqa_d128", 2, 1000, 4, 2, 128, [W.random_partition(rng, 1000, 30) for _ in range(2)], 5e6, True),
+        ("one_doc_d64", 1, 777, 2, 2, 64, [[776]], 1e4, True),
+        ("len1_docs", 1, 513, 2, 1, 128, [[1] * 512], 5e6, True),
+        ("mixed_b2", 2, 640, 2, 2, 128, [[1, 300, 1, 337], [639]], 5e5, True),
+        ("noncausal", 1, 600, 2, 2, 128, [[100, 1, 250, 248]], 1e4, False),
+        ("s2", 2, 2, 2, 2, 64, [[1], [1]], 1e4, True),
+        ("gqa8", 1, 300, 8, 1, 64, [[150, 149]], 1e4, True),
+    ]
+
+
+def _inputs(B, S, Hq, Hkv, D, seed):
+    q, k, v, do = W.make_tensors(B, S, Hq, Hkv, D, seed)
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("case", _small_cases(), ids=lambda c: c[0])
+def test_fwd_bwd_small_full_compare(gpu_lib, case):
+    name, B, S, Hq, Hkv, D, rows, base, causal = case
+    say(f"[parity] {name} B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} causal={causal}")
+    cu = W.cu_doc_lens_from_lengths(rows, S)
+    q, k, v, do = _inputs(B, S, Hq, Hkv, D, 1234)
+    o, lse = gpu_lib.anchor_attn_fwd(q.cuda(), k.cuda(), v.cuda(), cu, base, causal)
+    o_ref, lse_ref, _, _ = oracle.forward(q, k, v, cu, base, causal)
+    o_g = f64(o).reshape(B * S, Hq, D)
+    assert o_err(o_g, o_ref) <= O_TOL, o_err(o_g, o_ref)
+    lse_g = f64(lse).transpose(1, 0, 2).reshape(Hq, B * S)
+    assert np.abs(lse_g - lse_ref).max() <= LSE_TOL
+    dq, dk, dv = gpu_lib.anchor_attn_bwd(q.cuda(), k.cuda(), v.cuda(), o, lse, do.cuda(), cu, base, causal)
+    dq_r, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, base, causal)
+    e = (rel_frob(f64(dq).reshape(B * S, Hq, D), dq_r), rel_frob(f64(dk).reshape(B * S, Hkv, D), dk_r),
+         rel_frob(f64(dv).reshape(B * S, Hkv, D), dv_r))
+    say(f"[parity] {name} O {o_err(o_g, o_ref):.2e} dq {e[0]:.2e} dk {e[1]:.2e} dv {e[2]:.2e}")
+    assert max(e) <= G_TOL, e
+
+
+def test_determinism(gpu_lib):
+    B, S, Hq, Hkv, D = 2, 1000, 4, 2, 128
+    rng = np.random.default_rng(3)
+    cu = W.cu_doc_lens_from_lengths([W.random_partition(rng, S, 20) for _ in range(B)], S)
+    q, k, v, do = (t.cuda() for t in _inputs(B, S, Hq, Hkv, D, 99))
+    o1, l1 = gpu_lib.anchor_attn_fwd(q, k, v, cu, 5e6)
+    o2, l2 = gpu_lib.anchor_attn_fwd(q, k, v, cu, 5e6)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    g1 = gpu_lib.anchor_attn_bwd(q, k, v, o1, l1, do, cu, 5e6)
+    g2 = gpu_lib.anchor_attn_bwd(q, k, v, o1, l1, do, cu, 5e6)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_autograd_function(gpu_lib):
+    B, S, Hq, Hkv, D = 1, 400, 2, 2, 64
+    cu = W.cu_doc_lens_from_lengths([[199, 200]], S)
+    q, k, v, do = _inputs(B, S, Hq, Hkv, D, 7)
+    qc, kc, vc = (t.cuda().requires_grad_(True) for t in (q, k, v))
+    o = gpu_lib.anchor_attention(qc, kc, vc, cu, 1e4)
+    o.backward(do.cuda())
+    dq_r, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, 1e4)
+    assert rel_frob(f64(qc.grad).reshape(B * S, Hq, D), dq_r) <= G_TOL
+    assert rel_frob(f64(kc.grad).reshape(B * S, Hkv, D), dk_r) <= G_TOL
+    assert rel_frob(f64(vc.grad).reshape(B * S, Hkv, D), dv_r) <= G_TOL
+
+
+def _sample_rows(w, rng, n):
+    """Query rows to check: anchors, document starts and ends, random rows."""
+    S = w.S
+    rows = set()
+    for b in range(w.B):
+        rows.add(b * S)
+        rows.update(int(b * S + x) for x in rng.integers(0, S, n))
+        cu = w.cu_doc_lens
+        for c in cu[1:]:
+            if b * S < c < (b + 1) * S:
+                rows.add(int(c)); rows.add(int(c) - 1)
+    return np.array(sorted(rows))[: 3 * n]
+
+
+def _sample_keys(w, rng, n, max_doc=2500):
+    """Keys in documents short enough for the oracle to sum over, plus anchors."""
+    cu = w.cu_doc_lens
+    keys = set()
+    for s, e in zip(cu[:-1], cu[1:]):
+        if e - s <= max_doc and e - s > 1:
+            keys.update(int(x) for x in rng.integers(s, e, 3))
+            keys.add(int(s)); keys.add(int(e) - 1)
+    keys = sorted(keys)
+    pick = rng.choice(len(keys), size=min(n, len(keys)), replace=False)
+    return np.array(sorted(keys[i] for i in pick))
+
+
+@pytest.mark.parametrize("wname", ["8k", "64k", "128k_gqa", "short_docs"])
+def test_full_size_sampled(gpu_lib, wname):
+    """The benchmark's shapes and launch configuration; sampled outputs."""
+    w = W.get(wname)
+    B, S, Hq, Hkv, D = w.B, w.S, w.Hq, w.Hkv, w.D
+    say(f"[full] {wname} generating inputs")
+    q, k, v, do = W.make_tensors(B, S, Hq, Hkv, D, w.tensor_seed)
+    cu = w.cu_doc_lens
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    say(f"[full] {wname} fwd+bwd on GPU")
+    o, lse = gpu_lib.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base)
+    dq, dk, dv = gpu_lib.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o.float()).any()
+    rng = np.random.default_rng(11)
+    heads = [0, Hq - 1] if Hq == Hkv else list(range(Hq // Hkv))     # GQA: all of kv group 0
+    rows = _sample_rows(w, rng, 48)
+    say(f"[full] {wname} oracle forward on {len(rows)} rows x {len(heads)} heads")
+    o_ref, lse_ref, _, _ = oracle.forward(q, k, v, cu, w.rope_base, heads=heads, rows=rows)
+    o_g = f64(o).reshape(B * S, Hq, D)[rows][:, heads]
+    lse_g = f64(lse).transpose(1, 0, 2).reshape(Hq, B * S)[heads][:, rows]
+    say(f"[full] {wname} O err {o_err(o_g, o_ref):.2e} lse err {np.abs(lse_g - lse_ref).max():.2e}")
+    assert o_err(o_g, o_ref) <= O_TOL
+    assert np.abs(lse_g - lse_ref).max() <= LSE_TOL
+    keys = _sample_keys(w, rng, 24)
+    say(f"[full] {wname} oracle backward on {len(rows)} rows, {len(keys)} keys")
+    dq_r, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, w.rope_base, heads=heads,
+                                             q_rows=rows, k_cols=keys)
+    dq_g = f64(dq).reshape(B * S, Hq, D)[rows][:, heads]
+    g = heads[0] * Hkv // Hq
+    dk_g = f64(dk).reshape(B * S, Hkv, D)[keys][:, [g]]
+    dv_g = f64(dv).reshape(B * S, Hkv, D)[keys][:, [g]]
+    if Hq == Hkv:
+        # key gradients from a subset of heads only cover those heads: compare per head
+        e_dk = max(rel_frob(f64(dk).reshape(B * S, Hkv, D)[keys][:, [h]], dk_r[:, [h]]) for h in heads)
+        e_dv = max(rel_frob(f64(dv).reshape(B * S, Hkv, D)[keys][:, [h]], dv_r[:, [h]]) for h in heads)
+    else:
+        e_dk = rel_frob(dk_g, dk_r[:, [g]])
+        e_dv = rel_frob(dv_g, dv_r[:, [g]])
+    e_dq = rel_frob(dq_g, dq_r)
+    say(f"[full] {wname} dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
+    assert max(e_dq, e_dk, e_dv) <= G_TOL

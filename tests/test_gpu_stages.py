@@ -1,0 +1,146 @@
+"""GPU stages against the oracle: position IDs and tile plans bit-exact, the
+RoPE stage within one bf16 ulp of round-to-nearest-even of the float64 rotation."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from _helpers import bf16_rne, bf16_ulp, f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _partitions():
+    rng = np.random.default_rng(77)
+    cases = [
+        ("tiny", 1, 256, [[80, 100, 75]]),
+        ("one_doc_ragged", 1, 1000, [[999]]),
+        ("len1_docs", 1, 300, [[1] * 299]),
+        ("b2_random", 2, 777, [W.random_partition(rng, 777, 40) for _ in range(2)]),
+        ("b2_mixed", 2, 513, [[1, 200, 1, 310], [512]]),
+        ("s2", 3, 2, [[1], [1], [1]]),
+        ("s1", 2, 1, [[], []]),
+    ]
+    w8 = W.get("8k")
+    cases.append(("8k", 1, w8.S, [list(r) for r in w8.doc_rows]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _partitions(), ids=lambda c: c[0])
+def test_position_ids_bit_exact(gpu_lib, case):
+    name, B, S, rows = case
+    say(f"[positions] {name} B={B} S={S}")
+    cu = W.cu_doc_lens_from_lengths(rows, S)
+    for mode, label in ((0, "reset"), (1, "continuous")):
+        pos, ws = gpu_lib.anchor_attn_position_ids(cu, B, S, mode)
+        ref = oracle.position_ids(cu, B, S, label)
+        assert np.array_equal(pos.cpu().numpy().astype(np.int64), ref)
+        assert gpu_lib.anchor_attn_device_status(ws) == 0
+
+
+def _cmp_plan(gp, ref, B):
+    qptr = gp["qptr"].cpu().numpy()
+    n = int(gp["n_live"].cpu().item())
+    assert n == len(ref["kidx"]) == qptr[-1]
+    assert np.array_equal(qptr, ref["qptr"])
+    assert np.array_equal(gp["kidx"][:n].cpu().numpy(), ref["kidx"])
+    assert np.array_equal(gp["kkind"][:n].cpu().numpy(), ref["kkind"])
+    assert np.array_equal(gp["kptr"].cpu().numpy(), ref["kptr"])
+    assert np.array_equal(gp["qidx"][:n].cpu().numpy(), ref["qidx"])
+    assert np.array_equal(gp["qkind"][:n].cpu().numpy(), ref["qkind"])
+
+
+@pytest.mark.parametrize("tile", [(64, 64), (128, 64), (64, 128), (128, 128), (32, 16)])
+@pytest.mark.parametrize("case", _partitions()[:-1], ids=lambda c: c[0])
+def test_tile_plan_bit_exact_small(gpu_lib, case, tile):
+    name, B, S, rows = case
+    BM, BN = tile
+    say(f"[plan] {name} B={B} S={S} tile={BM}x{BN}")
+    cu = W.cu_doc_lens_from_lengths(rows, S)
+    for causal in (True, False):
+        gp = gpu_lib.anchor_attn_tile_plan(cu, B, S, BM, BN, causal)
+        ref = oracle.tile_plan(cu, B, S, BM, BN, causal)
+        _cmp_plan(gp, ref, B)
+
+
+def test_tile_plan_bit_exact_8k_all_tiles(gpu_lib):
+    w = W.get("8k")
+    for BM, BN in ((128, 64), (64, 128), (128, 128)):
+        say(f"[plan] 8k tile={BM}x{BN}")
+        gp = gpu_lib.anchor_attn_tile_plan(w.cu_doc_lens, w.B, w.S, BM, BN)
+        ref = oracle.tile_plan(w.cu_doc_lens, w.B, w.S, BM, BN)
+        _cmp_plan(gp, ref, w.B)
+
+
+def _rows_of(gp, bq, key="q"):
+    if key == "q":
+        a, b = gp["qptr"][bq:bq + 2].tolist()
+        return gp["kidx"][a:b].cpu().numpy(), gp["kkind"][a:b].cpu().numpy()
+    a, b = gp["kptr"][bq:bq + 2].tolist()
+    return gp["qidx"][a:b].cpu().numpy(), gp["qkind"][a:b].cpu().numpy()
+
+
+@pytest.mark.parametrize("wname", ["64k", "128k_gqa", "short_docs"])
+def test_tile_plan_bit_exact_full_size_sampled(gpu_lib, wname):
+    """Full-size plans in the kernels' tile shapes; sampled query tiles (query
+    major) and key tiles (key major) are checked against the brute force."""
+    w = W.get(wname)
+    cu = w.cu_doc_lens
+    rng = np.random.default_rng(5)
+    for BM, BN in ((128, 64), (64, 128)):
+        say(f"[plan] {wname} tile={BM}x{BN}")
+        gp = gpu_lib.anchor_attn_tile_plan(cu, w.B, w.S, BM, BN)
+        nq, nk = gp["nq"], gp["nk"]
+        # live-tile total from the closed form is not available; check sampled rows/cols
+        for b in range(w.B):
+            for qt in sorted(set([0, 1, nq - 1] + list(rng.integers(0, nq, 6)))):
+                ref = oracle.tile_kinds_row(cu, w.B, w.S, BM, BN, b, int(qt))
+                idx, kind = _rows_of(gp, b * nq + int(qt), "q")
+                assert np.array_equal(idx, np.nonzero(ref)[0])
+                assert np.array_equal(kind, ref[ref != 0])
+            for kt in sorted(set([0, 1, nk - 1] + list(rng.integers(0, nk, 4)))):
+                ref = oracle.tile_kinds_col(cu, w.B, w.S, BM, BN, b, int(kt))
+                idx, kind = _rows_of(gp, b * nk + int(kt), "k")
+                assert np.array_equal(idx, np.nonzero(ref)[0])
+                assert np.array_equal(kind, ref[ref != 0])
+
+
+@pytest.mark.parametrize("wname", ["tiny", "8k", "64k", "128k_gqa"])
+def test_rope_stage_within_one_ulp(gpu_lib, wname):
+    w = W.get(wname)
+    S = w.S
+    say(f"[rope] {wname}")
+    g = torch.Generator("cpu").manual_seed(55)
+    ntok = min(S, 4096)
+    x = torch.randn((1, S, 4, w.D), generator=g).to(torch.bfloat16)
+    pos = oracle.position_ids(w.cu_doc_lens[: 2 + len(w.doc_rows[0])], 1, S)
+    y = gpu_lib.anchor_attn_rope(x.cuda(), torch.from_numpy(pos.astype(np.int32)), w.rope_base).cpu()
+    toks = np.unique(np.concatenate([np.arange(min(S, 64)), np.random.default_rng(1).integers(0, S, ntok)]))
+    ref = oracle.rope(f64(x[0, toks]), pos[toks], w.rope_base)          # float64 [n, 4, D]
+    want = bf16_rne(ref)
+    got = f64(y[0, toks])
+    diff = np.abs(got - want)
+    ulp = bf16_ulp(want)
+    # The rotation runs in float32: besides the final bf16 rounding (one ulp
+    # at a near tie), x0*c - x1*s carries float32 rounding of the products,
+    # which near cancellation is large next to the result itself.
+    xin = f64(x[0, toks])
+    pair_mag = np.repeat(np.abs(xin[..., 0::2]) + np.abs(xin[..., 1::2]), 2, axis=-1)
+    bound = ulp + 2.0 ** -22 * pair_mag
+    assert np.all(diff <= bound), float((diff / bound).max())
+    rate = float((diff > 0).mean())
+    say(f"[rope] {wname} mismatch rate {rate:.2e}")
+    assert rate <= 1e-3
+    # the anchor (position 0) is unchanged: R_0 = I
+    assert torch.equal(y[0, 0], x[0, 0])
+
+
+def test_device_status_flags_bad_documents(gpu_lib):
+    S = 64
+    bad = np.array([0, 10, 64], dtype=np.int32)            # no one-token anchor segment
+    pos, ws = gpu_lib.anchor_attn_position_ids(bad, 1, S)
+    assert gpu_lib.anchor_attn_device_status(ws) == gpu_lib.AA_EDOCS
+    q = torch.randn((1, S, 2, 64)).to(torch.bfloat16).cuda()
+    o, lse = gpu_lib.anchor_attn_fwd(q, q, q, bad, 1e4)
+    assert torch.isnan(o.float()).all() and torch.isnan(lse).all()
