@@ -110,6 +110,92 @@ __device__ __forceinline__ float partner(float x) {
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// ---------------------------------------------------------------- LDS tiles
+// A [rows][D] bf16 tile in LDS, row-major with the 16-byte chunks of each row
+// permuted by an XOR swizzle, so that both access patterns of the kernels are
+// free of bank conflicts:
+//   * row reads: 16 consecutive rows, the same 16-byte chunk (MFMA operand
+//     whose reduction runs along the features);
+//   * transposed reads (ds_read_b64_tr_b16): 4 consecutive rows x 4
+//     consecutive chunks per 32 lanes (MFMA operand whose reduction runs
+//     along the rows).
+// For D = 128 a row is exactly one 256-byte bank row; the permutation swaps
+// the two 2-bit fields of (row mod 16).  For D = 64 two rows share a bank row.
+template <int D>
+struct SwzTile {
+  static constexpr int kChunks = D / 8;
+  __device__ static __forceinline__ int swz(int row) {
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((row >> 1) & 7);
+  }
+  // element offset of (row, 8-element chunk c)
+  __device__ static __forceinline__ int chunk_off(int row, int c) {
+    return row * D + ((c ^ swz(row)) & (kChunks - 1)) * 8;
+  }
+  // element offset of (row, feature f) for f a multiple of 4
+  __device__ static __forceinline__ int off(int row, int f) {
+    return chunk_off(row, f >> 3) + (f & 7);
+  }
+};
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// One 8-byte transposed LDS read: within each group of 16 lanes, lane t
+// receives element t%4 of the 8-byte pieces addressed by lanes t/4 + 4*i,
+// i = 0..3.
+__device__ __forceinline__ i16x4 ds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// MFMA operand whose reduction index runs over tile rows r0 .. r0+15 and
+// whose row/column index is the feature f0 + (lane % 32), read from a
+// row-major swizzled tile.  Element i of lane l holds
+//   T[r0 + 8*(i/4) + 4*(l/32) + i%4][f0 + l%32],
+// the row order of a 32x32 accumulator column, so that this operand pairs
+// with B/A operands built directly from accumulator registers.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int r0, int f0) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, t = lane & 15;
+  const int row = r0 + 4 * (g >> 1) + (t >> 2);
+  const int f = f0 + 16 * (g & 1) + 4 * (t & 3);
+  // whole-vector casts: the two 4-element results become the two halves of
+  // the operand without element-wise repacking
+  const bf16x4 a = __builtin_bit_cast(bf16x4, ds_read_tr(tile + SwzTile<D>::off(row, f)));
+  const bf16x4 b = __builtin_bit_cast(bf16x4, ds_read_tr(tile + SwzTile<D>::off(row + 8, f)));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copy (global_load_lds_dwordx4) of a [ROWS][D] tile
+// into the swizzled layout: lane L of a wave's instruction writes the 16
+// bytes at LDS chunk base + L, so each lane fetches the logical chunk that
+// the swizzle places there.  Global rows row0 .. row0+ROWS-1 are clamped to
+// row_max.  Every thread of the NTHREADS-thread workgroup calls it; the data
+// is visible after wait_direct_loads() and a workgroup barrier.
+template <int D, int ROWS, int NTHREADS>
+__device__ __forceinline__ void tile_load_direct(bf16* lds_tile, const bf16* gbase,
+                                                 size_t row_stride, int row0, int row_max) {
+  constexpr int NCH = D / 8;
+  constexpr int ITERS = ROWS * NCH / NTHREADS;
+  static_assert(ROWS * NCH % NTHREADS == 0, "tile must split evenly over the waves");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < ITERS; ++u) {
+    const int base = (wave * ITERS + u) * 64;     // first physical chunk of this instruction
+    const int pc_idx = base + lane;
+    const int row = pc_idx / NCH, pc = pc_idx % NCH;
+    const int c = (pc ^ SwzTile<D>::swz(row)) & (NCH - 1);
+    const bf16* src = gbase + (size_t)min(row0 + row, row_max) * row_stride + c * 8;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds_tile + base * 8), 16, 0, 0);
+  }
+}
+
+// Wait until this wave's direct-to-LDS loads (and other vector memory loads)
+// have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Tile shapes of the attention kernels.
 constexpr int kFwdBM = 128, kFwdBN = 64;     // forward and dQ: query tile x key tile
 constexpr int kDkvBM = 64, kDkvBN = 128;     // dK/dV: query tile x key tile

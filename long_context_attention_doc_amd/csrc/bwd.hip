@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
       dp0 += __shfl_xor(dp0, off2);
     }
     const float L = lse[((size_t)b * Hq + hq) * S + (valid ? row : S - 1)];
-    float p0 = valid ? exp2f((s0 * scale - L) * kLog2e) : 0.f;
+    float p0 = valid ? __builtin_amdgcn_exp2f((s0 * scale - L) * kLog2e) : 0.f;
     const float dsv = p0 * (dp0 - d_o);
     if (valid && (tid % LPR) == 0) {
       dvec[((size_t)b * Hq + hq) * S + row] = d_o;
@@ -107,13 +107,23 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
 }
 
 // ---------------------------------------------------------------------------
-// dkdv: one workgroup (4 waves) per (row b, kv head, key tile of 128 keys);
-// each wave owns 32 keys.  In this kernel the MFMA accumulators are laid out
-// with keys as columns, so that P, dS (query x key) feed the B operand of
-// dV^T = dO^T P and dK^T = Q^T dS directly.
+// dkdv: one workgroup of eight waves per (row b, kv head, key tile of 128
+// keys).  Wave w owns the 32 keys kg = w % 4 of the tile and the half
+// p = w / 4: it computes S = Q K^T and dP = dO V^T for queries
+// [32p, 32p+32) of each 64-query tile, and accumulates dV^T and dK^T for
+// features [64p, 64p+64) over all 64 queries.  The two waves of a key group
+// swap their halves of P and dS through LDS, so each wave holds only half of
+// the key gradients (2 x 64 accumulator registers instead of 2 x 128) and the
+// kernel runs two waves per SIMD.
+//   * K^T and V^T (B operands, keys as columns) stay in registers.
+//   * Q and dO tiles go straight into double-buffered swizzled LDS
+//     (global_load_lds); row reads feed S and dP, transposing reads feed Q^T
+//     and dO^T.
+//   * P and dS feed the B operand of dV^T = dO^T P and dK^T = Q^T dS straight
+//     from the accumulator layout.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
+__global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dvec,
     const float* __restrict__ table, const int32_t* __restrict__ pos,
@@ -121,27 +131,23 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
     const int32_t* __restrict__ kptr, const int32_t* __restrict__ qidx,
     const uint8_t* __restrict__ qkind, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
     int nk, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
-  constexpr int BM = kDkvBM, BN = kDkvBN;
-  constexpr int RST = D + 8;     // row-major tile stride (bf16)
-  constexpr int TST = BM + 4;    // transposed tile stride (bf16)
+  constexpr int BM = kDkvBM, BN = kDkvBN;    // 64 queries x 128 keys
   constexpr int NKK = D / 16;
-  constexpr int NDB = D / 32;
-  constexpr int NQB = BM / 32;   // 32-query blocks of a query tile
-  constexpr int NQC = BM / 16;   // 16-query reduction steps
-  constexpr int GROUPS = (BM / 4) * (D / 8);
-  __shared__ __align__(16) bf16 Qs[BM * RST];
-  __shared__ __align__(16) bf16 Qt[D * TST];
-  __shared__ __align__(16) bf16 Gs[BM * RST];    // dO
-  __shared__ __align__(16) bf16 Gt[D * TST];
-  __shared__ float s_lse[BM], s_dv[BM];
-  __shared__ int s_lo[BM], s_hi[BM];
+  constexpr int NDH = D / 64;                // 32-feature blocks per half
+  using T = SwzTile<D>;
+  __shared__ __align__(16) bf16 Qs[2][BM * D];
+  __shared__ __align__(16) bf16 Gs[2][BM * D];
+  __shared__ __align__(16) bf16x8 Xs[4][2][4][64];   // [key group][P, dS][16-query step][lane]
+  __shared__ __align__(16) float s_lse[2][BM], s_dv[2][BM];
+  __shared__ __align__(16) int s_lo[2][BM], s_hi[2][BM];
 
   const int b = blockIdx.x / nk, kt = blockIdx.x % nk;
   const int hkv = blockIdx.y;
   const int group = Hq / Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
-  const int key = kt * BN + wave * 32 + col;       // row-local key of this lane's column
+  const int kg = wave & 3, p = wave >> 2;
+  const int key = kt * BN + kg * 32 + col;       // row-local key of this lane's column
   const bool kvalid = key < S;
   const size_t tok0 = (size_t)b * S;
   const size_t ktok = tok0 + (kvalid ? key : S - 1);
@@ -159,30 +165,22 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
       vf[kk] = *(const bf16x8*)(vp + 16 * kk);
     }
   }
-  f32x16 dka[NDB], dva[NDB];
+  f32x16 dka[NDH], dva[NDH];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDH; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) { dka[db][j] = 0.f; dva[db][j] = 0.f; }
 
-  // Staging: each thread owns 4 consecutive query rows x 8 features of Q
-  // and of dO; it writes them row-major and transposed.
-  const int g_row = (tid / (D / 8)) * 4, g_f = (tid % (D / 8)) * 8;
-  bf16x8 qreg[4], greg[4];
+  // Q and dO tiles go straight into double-buffered LDS; the per-query
+  // statistics (LSE, Dv, visible-key interval) are staged by threads 0-63.
   float r_lse = 0.f, r_dv = 0.f;
   int r_lo = 1, r_hi = 0;
   const size_t q_row_stride = (size_t)Hq * D;
-
-  auto gload = [&](int hq, int qt) {
-    if (tid < GROUPS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int q = min(qt * BM + g_row + r, S - 1);
-        const size_t off = (tok0 + q) * q_row_stride + (size_t)hq * D + g_f;
-        qreg[r] = *(const bf16x8*)(qr + off);
-        greg[r] = *(const bf16x8*)(dout + off);
-      }
-    }
+  auto issue = [&](int buf, int hq, int qt) {
+    tile_load_direct<D, BM, 512>(Qs[buf], qr + tok0 * q_row_stride + (size_t)hq * D, q_row_stride,
+                                 qt * BM, S - 1);
+    tile_load_direct<D, BM, 512>(Gs[buf], dout + tok0 * q_row_stride + (size_t)hq * D,
+                                 q_row_stride, qt * BM, S - 1);
     if (tid < BM) {
       const int q = qt * BM + tid;
       const int qc = min(q, S - 1);
@@ -192,123 +190,132 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
       r_hi = q < S ? hi[tok0 + qc] : 0;
     }
   };
-  auto lstore = [&]() {
-    if (tid < GROUPS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *(bf16x8*)(Qs + (g_row + r) * RST + g_f) = qreg[r];
-        *(bf16x8*)(Gs + (g_row + r) * RST + g_f) = greg[r];
-      }
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        bf16x4 a, c;
-        a[0] = qreg[0][dd]; a[1] = qreg[1][dd]; a[2] = qreg[2][dd]; a[3] = qreg[3][dd];
-        c[0] = greg[0][dd]; c[1] = greg[1][dd]; c[2] = greg[2][dd]; c[3] = greg[3][dd];
-        *(bf16x4*)(Qt + (g_f + dd) * TST + g_row) = a;
-        *(bf16x4*)(Gt + (g_f + dd) * TST + g_row) = c;
-      }
-    }
+  auto stats_store = [&](int buf) {
     if (tid < BM) {
-      s_lse[tid] = r_lse;
-      s_dv[tid] = r_dv;
-      s_lo[tid] = r_lo;
-      s_hi[tid] = r_hi;
+      s_lse[buf][tid] = r_lse;
+      s_dv[buf][tid] = r_dv;
+      s_lo[buf][tid] = r_lo;
+      s_hi[buf][tid] = r_hi;
     }
   };
 
-  const int e_begin = kptr[blockIdx.x], e_end = kptr[blockIdx.x + 1];
   // Work list: every q head of the group x every live, not anchor-only query tile.
-  int e = e_begin, hi_q = hkv * group;
+  const int e_begin = kptr[blockIdx.x], e_end = kptr[blockIdx.x + 1];
+  const int h_end = (hkv + 1) * group;
+  auto first = [&](int& ee, int& hh) {
+    ee = e_begin;
+    hh = hkv * group;
+    if (e_begin >= e_end) { hh = h_end; return; }
+    while (ee < e_end && qkind[ee] == kTileAnchor) ++ee;
+    if (ee >= e_end) hh = h_end;             // nothing live besides the anchor
+  };
   auto advance = [&](int& ee, int& hh) {
     do {
       ++ee;
       if (ee >= e_end) { ee = e_begin; ++hh; }
-    } while (hh < (hkv + 1) * group && qkind[ee] == kTileAnchor);
+    } while (hh < h_end && qkind[ee] == kTileAnchor);
   };
-  // first item
-  if (e_begin < e_end) {
-    while (e < e_end && qkind[e] == kTileAnchor) ++e;
-    if (e >= e_end) hi_q = (hkv + 1) * group;   // nothing live besides the anchor
-  } else {
-    hi_q = (hkv + 1) * group;
-  }
-  if (hi_q < (hkv + 1) * group) gload(hi_q, qidx[e]);
 
-  while (hi_q < (hkv + 1) * group) {
+  int e, hq;
+  first(e, hq);
+  if (hq < h_end) issue(0, hq, qidx[e]);
+  int cur = 0;
+  while (hq < h_end) {
     const int qt = qidx[e];
     const bool need_mask = qkind[e] != kTileFull || kt == 0;
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    int e_next = e, h_next = hi_q;
-    advance(e_next, h_next);
-    if (h_next < (hkv + 1) * group) gload(h_next, qidx[e_next]);
+    wait_direct_loads();
+    stats_store(cur);
+    __syncthreads();      // tile in buffer `cur` visible; buffer cur^1 and Xs free
+    int e1 = e, h1 = hq;
+    advance(e1, h1);
+    if (h1 < h_end) issue(cur ^ 1, h1, qidx[e1]);
+    const bf16* Qc = Qs[cur];
+    const bf16* Gc = Gs[cur];
 
-    // S = Q K^T and dP = dO V^T: columns = this wave's keys, rows = queries.
-    f32x16 sp[NQB], dp[NQB];
+    // S = Q K^T, dP = dO V^T for queries [32p, 32p+32): columns = keys.
+    f32x16 sp, dp;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
+    for (int j = 0; j < 16; ++j) { sp[j] = 0.f; dp[j] = 0.f; }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) { sp[qb][j] = 0.f; dp[qb][j] = 0.f; }
-      const bf16* qa = Qs + (qb * 32 + col) * RST + 8 * h;
-      const bf16* ga = Gs + (qb * 32 + col) * RST + 8 * h;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        sp[qb] = mfma32(*(const bf16x8*)(qa + 16 * kk), kf[kk], sp[qb]);
-        dp[qb] = mfma32(*(const bf16x8*)(ga + 16 * kk), vf[kk], dp[qb]);
-      }
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int off = T::chunk_off(32 * p + col, 2 * kk + h);
+      sp = mfma32(*(const bf16x8*)(Qc + off), kf[kk], sp);
+      dp = mfma32(*(const bf16x8*)(Gc + off), vf[kk], dp);
     }
     // P = exp2(s * scale_log2 - lse_log2), dS = P (dP - Dv).
-    bf16x8 pbv[NQC], dsb[NQC];
+    bf16x8 pown[2], down[2];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
+    for (int g = 0; g < 4; ++g) {
+      const int q0 = 32 * p + 8 * g + 4 * h;   // tile-local queries q0 .. q0+3
+      const f32x4 l4 = *(const f32x4*)(&s_lse[cur][q0]);
+      const f32x4 d4 = *(const f32x4*)(&s_dv[cur][q0]);
+      float pv[4];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int qi = qb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);   // tile-local query
-        float p = exp2f(sp[qb][j] * scale_log2 - s_lse[qi]);
-        if (need_mask) p = (key >= s_lo[qi] && key <= s_hi[qi]) ? p : 0.f;
-        const float ds = p * (dp[qb][j] - s_dv[qi]);
-        pbv[2 * qb + (j >> 3)][j & 7] = (bf16)p;
-        dsb[2 * qb + (j >> 3)][j & 7] = (bf16)ds;
+      for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[4 * g + r], scale_log2, -l4[r]));
+      if (need_mask) {
+        const int4 lo4 = *(const int4*)(&s_lo[cur][q0]);
+        const int4 hi4 = *(const int4*)(&s_hi[cur][q0]);
+        pv[0] = (key >= lo4.x && key <= hi4.x) ? pv[0] : 0.f;
+        pv[1] = (key >= lo4.y && key <= hi4.y) ? pv[1] : 0.f;
+        pv[2] = (key >= lo4.z && key <= hi4.z) ? pv[2] : 0.f;
+        pv[3] = (key >= lo4.w && key <= hi4.w) ? pv[3] : 0.f;
       }
-    // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over queries, accumulator
-    // order of 16-query steps: rows 0-3, 8-11 in lanes 0-31; 4-7, 12-15 above)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const bf16* gta = Gt + (32 * db + col) * TST + 4 * h;
-      const bf16* qta = Qt + (32 * db + col) * TST + 4 * h;
-#pragma unroll
-      for (int c = 0; c < NQC; ++c) {
-        const bf16x4 g0 = *(const bf16x4*)(gta + 16 * c), g1 = *(const bf16x4*)(gta + 16 * c + 8);
-        const bf16x4 q0 = *(const bf16x4*)(qta + 16 * c), q1 = *(const bf16x4*)(qta + 16 * c + 8);
-        bf16x8 ga, qa;
-        ga[0] = g0[0]; ga[1] = g0[1]; ga[2] = g0[2]; ga[3] = g0[3];
-        ga[4] = g1[0]; ga[5] = g1[1]; ga[6] = g1[2]; ga[7] = g1[3];
-        qa[0] = q0[0]; qa[1] = q0[1]; qa[2] = q0[2]; qa[3] = q0[3];
-        qa[4] = q1[0]; qa[5] = q1[1]; qa[6] = q1[2]; qa[7] = q1[3];
-        dva[db] = mfma32(ga, pbv[c], dva[db]);
-        dka[db] = mfma32(qa, dsb[c], dka[db]);
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * g + r;
+        pown[j >> 3][j & 7] = (bf16)pv[r];
+        down[j >> 3][j & 7] = (bf16)(pv[r] * (dp[j] - d4[r]));
       }
     }
-    e = e_next;
-    hi_q = h_next;
+    // swap halves with the partner wave of this key group
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      Xs[kg][0][2 * p + c][lane] = pown[c];
+      Xs[kg][1][2 * p + c][lane] = down[c];
+    }
+    __syncthreads();
+    bf16x8 pf[4], df[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if ((c >> 1) == p) {
+        pf[c] = pown[c & 1];
+        df[c] = down[c & 1];
+      } else {
+        pf[c] = Xs[kg][0][c][lane];
+        df[c] = Xs[kg][1][c][lane];
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS for features [64p, 64p+64).
+#pragma unroll
+    for (int db = 0; db < NDH; ++db) {
+      const int f0 = 32 * (NDH * p + db);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        dva[db] = mfma32(tr_operand<D>(Gc, 16 * c, f0), pf[c], dva[db]);
+        dka[db] = mfma32(tr_operand<D>(Qc, 16 * c, f0), df[c], dka[db]);
+      }
+    }
+    e = e1; hq = h1;
+    cur ^= 1;
   }
 
-  // Epilogue: dK = R(pos)^T (scale * dK'), dV as accumulated.
+  // Epilogue: dK = R(pos)^T (scale * dK'), dV as accumulated; this wave
+  // writes its 32 keys x features [64p, 64p+64).
   if (kvalid) {
-    const int p = pos[ktok];
-    const float* tb = table + (size_t)p * D;      // (D/2) pairs of {cos, sin}
+    const int pk = pos[ktok];
+    const float* tb = table + (size_t)pk * D;      // (D/2) pairs of {cos, sin}
     bf16* dkp = dk + (ktok * Hkv + hkv) * D;
     bf16* dvp = dv + (ktok * Hkv + hkv) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDH; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * h;     // features d0 .. d0+3 = pairs d0/2, d0/2+1
+        const int d0 = 32 * (NDH * p + db) + 8 * g + 4 * h;
+        const f32x4 cs = *(const f32x4*)(tb + d0);    // cos, sin of pairs d0/2, d0/2+1
         bf16x4 wk, wv;
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
-          const float c = tb[d0 + 2 * pr], s = tb[d0 + 2 * pr + 1];
+          const float c = cs[2 * pr], s = cs[2 * pr + 1];
           const float x0 = dka[db][4 * g + 2 * pr] * scale, x1 = dka[db][4 * g + 2 * pr + 1] * scale;
           wk[2 * pr] = (bf16)(bad ? NAN : x0 * c + x1 * s);
           wk[2 * pr + 1] = (bf16)(bad ? NAN : x1 * c - x0 * s);
@@ -323,7 +330,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
 
 // ---------------------------------------------------------------------------
 // dq: one workgroup (4 waves) per (row b, query head, query tile of 128);
-// each wave owns 32 queries, as in the forward kernel.
+// each wave owns 32 queries, as in the forward kernel.  K and V tiles go
+// straight into double-buffered swizzled LDS: row reads feed S^T = K Q^T and
+// dP^T = V dO^T, transposing reads feed K^T in dQ^T = K^T dS^T.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(
@@ -336,16 +345,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const int32_t* __restrict__ status, int S, int Hq, int Hkv, int nq, float scale,
     bf16* __restrict__ dq) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
-  constexpr int RST = D + 8;
-  constexpr int TST = BN + 4;
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NKB = BN / 32;
-  constexpr int NKC = BN / 16;
-  constexpr int GROUPS = (BN / 4) * (D / 8);
-  __shared__ __align__(16) bf16 Ks[BN * RST];
-  __shared__ __align__(16) bf16 Vs[BN * RST];
-  __shared__ __align__(16) bf16 Kt[D * TST];
+  using T = SwzTile<D>;
+  __shared__ __align__(16) bf16 Ks[2][BN * D];
+  __shared__ __align__(16) bf16 Vs[2][BN * D];
 
   const int tile = blockIdx.x;
   const int hq = blockIdx.y;
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   const bool bad = status[0] != kStatusOk;
   const float scale_log2 = scale * kLog2e;
   const size_t rowstat = ((size_t)b * Hq + hq) * S + (qvalid ? qrow : S - 1);
-  const float lse2 = lse[rowstat] * kLog2e;
+  const float nlse2 = -lse[rowstat] * kLog2e;
   const float dvi = dvec[rowstat];
 
   bf16x8 qf[NKK], gf[NKK];
@@ -383,95 +388,68 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   const size_t kv_row_stride = (size_t)Hkv * D;
   const bf16* kbase = kr + tok0 * kv_row_stride + hkv * D;
   const bf16* vbase = v + tok0 * kv_row_stride + hkv * D;
-  const int g_key = (tid / (D / 8)) * 4, g_f = (tid % (D / 8)) * 8;
-  bf16x8 kreg[4], vreg[4];
-
-  auto gload = [&](int kt) {
-    if (tid < GROUPS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = min(kt * BN + g_key + r, S - 1);
-        kreg[r] = *(const bf16x8*)(kbase + key * kv_row_stride + g_f);
-        vreg[r] = *(const bf16x8*)(vbase + key * kv_row_stride + g_f);
-      }
-    }
-  };
-  auto lstore = [&]() {
-    if (tid < GROUPS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *(bf16x8*)(Ks + (g_key + r) * RST + g_f) = kreg[r];
-        *(bf16x8*)(Vs + (g_key + r) * RST + g_f) = vreg[r];
-      }
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        bf16x4 w;
-        w[0] = kreg[0][dd]; w[1] = kreg[1][dd]; w[2] = kreg[2][dd]; w[3] = kreg[3][dd];
-        *(bf16x4*)(Kt + (g_f + dd) * TST + g_key) = w;
-      }
-    }
+  auto issue = [&](int buf, int kt) {
+    tile_load_direct<D, BN, 256>(Ks[buf], kbase, kv_row_stride, kt * BN, S - 1);
+    tile_load_direct<D, BN, 256>(Vs[buf], vbase, kv_row_stride, kt * BN, S - 1);
   };
 
   int e = qptr[tile];
   const int e_end = qptr[tile + 1];
   if (e < e_end && kkind[e] == kTileAnchor) ++e;
-  if (e < e_end) gload(kidx[e]);
+  if (e < e_end) issue(0, kidx[e]);
+  int cur = 0;
   while (e < e_end) {
     const int kt = kidx[e];
     const bool need_mask = kkind[e] != kTileFull || kt == 0;
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (e + 1 < e_end) gload(kidx[e + 1]);
+    wait_direct_loads();
+    __syncthreads();                 // tile e in buffer cur; buffer cur^1 free
+    if (e + 1 < e_end) issue(cur ^ 1, kidx[e + 1]);
+    const bf16* Kc = Ks[cur];
+    const bf16* Vc = Vs[cur];
 
-    // S^T = K Q^T, dP^T = V dO^T: rows = keys, columns = this wave's queries.
-    f32x16 st[NKB], dpt[NKB];
+    // One 32-key block at a time: S^T = K Q^T, dP^T = V dO^T (rows = keys,
+    // columns = this wave's queries), dS^T, then dQ^T += K^T dS^T.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      f32x16 st, dpt;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) { st[kb][j] = 0.f; dpt[kb][j] = 0.f; }
-      const bf16* ka = Ks + (kb * 32 + col) * RST + 8 * h;
-      const bf16* va = Vs + (kb * 32 + col) * RST + 8 * h;
+      for (int j = 0; j < 16; ++j) { st[j] = 0.f; dpt[j] = 0.f; }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        st[kb] = mfma32(*(const bf16x8*)(ka + 16 * kk), qf[kk], st[kb]);
-        dpt[kb] = mfma32(*(const bf16x8*)(va + 16 * kk), gf[kk], dpt[kb]);
+        const int off = T::chunk_off(kb * 32 + col, 2 * kk + h);
+        st = mfma32(*(const bf16x8*)(Kc + off), qf[kk], st);
+        dpt = mfma32(*(const bf16x8*)(Vc + off), gf[kk], dpt);
       }
-    }
-    bf16x8 dsb[NKC];
+      // P^T = exp2(s * scale_log2 - lse_log2) in place of the scores
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int j = 0; j < 16; ++j) st[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[j], scale_log2, nlse2));
+      if (need_mask) {
+        const int a = qlo - kt * BN - 4 * h - kb * 32, z = qhi - kt * BN - 4 * h - kb * 32;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float p = exp2f(st[kb][j] * scale_log2 - lse2);
-        if (need_mask) {
-          const int key = kt * BN + kb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-          p = (key >= qlo && key <= qhi) ? p : 0.f;
+        for (int j = 0; j < 16; ++j) {
+          const int off = 8 * (j >> 2) + (j & 3);
+          st[j] = (off >= a && off <= z) ? st[j] : 0.f;
         }
-        dsb[2 * kb + (j >> 3)][j & 7] = (bf16)(p * (dpt[kb][j] - dvi));
       }
-    // dQ^T += K^T dS^T
+      bf16x8 dsb[2];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const bf16* ta = Kt + (32 * db + col) * TST + 4 * h;
+      for (int j = 0; j < 16; ++j) dsb[j >> 3][j & 7] = (bf16)(st[j] * (dpt[j] - dvi));
 #pragma unroll
-      for (int c = 0; c < NKC; ++c) {
-        const bf16x4 a0 = *(const bf16x4*)(ta + 16 * c), a1 = *(const bf16x4*)(ta + 16 * c + 8);
-        bf16x8 a;
-        a[0] = a0[0]; a[1] = a0[1]; a[2] = a0[2]; a[3] = a0[3];
-        a[4] = a1[0]; a[5] = a1[1]; a[6] = a1[2]; a[7] = a1[3];
-        acc[db] = mfma32(a, dsb[c], acc[db]);
-      }
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          acc[db] = mfma32(tr_operand<D>(Kc, 32 * kb + 16 * c, 32 * db), dsb[c], acc[db]);
     }
     ++e;
+    cur ^= 1;
   }
 
   // Epilogue: dq' = scale (acc + dS_i0 k'_0); dq = R(pos_i)^T dq'.
   if (qvalid) {
     const float a0 = ds0[rowstat];
     const bf16* k0 = kr + (tok0 * Hkv + hkv) * D;
-    const int p = pos[tok];
-    const float* tb = table + (size_t)p * D;
+    const int pq = pos[tok];
+    const float* tb = table + (size_t)pq * D;
     bf16* dqp = dq + (tok * Hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -479,10 +457,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * db + 8 * g + 4 * h;
         const bf16x4 kz = *(const bf16x4*)(k0 + d0);
+        const f32x4 cs = *(const f32x4*)(tb + d0);
         bf16x4 w;
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
-          const float c = tb[d0 + 2 * pr], s = tb[d0 + 2 * pr + 1];
+          const float c = cs[2 * pr], s = cs[2 * pr + 1];
           const float x0 = scale * (acc[db][4 * g + 2 * pr] + a0 * (float)kz[2 * pr]);
           const float x1 = scale * (acc[db][4 * g + 2 * pr + 1] + a0 * (float)kz[2 * pr + 1]);
           w[2 * pr] = (bf16)(bad ? NAN : x0 * c + x1 * s);
@@ -534,11 +513,11 @@ hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st) {
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, hipStream_t st) {
   const dim3 grid(a.B * pk.nk, a.Hkv);
   if (a.D == 128)
-    hipLaunchKernelGGL(k_bwd_dkdv<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
+    hipLaunchKernelGGL(k_bwd_dkdv<128>, grid, dim3(512), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pk.kptr, pk.qidx, pk.qkind,
                        a.status, a.S, a.Hq, a.Hkv, pk.nk, a.scale, a.dk, a.dv);
   else
-    hipLaunchKernelGGL(k_bwd_dkdv<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
+    hipLaunchKernelGGL(k_bwd_dkdv<64>, grid, dim3(512), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pk.kptr, pk.qidx, pk.qkind,
                        a.status, a.S, a.Hq, a.Hkv, pk.nk, a.scale, a.dk, a.dv);
   return hipGetLastError();

@@ -17,21 +17,25 @@
 // are then per lane, and the two lanes holding the same query (lane l and
 // l + 32) combine with one v_permlane32_swap.
 //   * Q^T (B operand) stays in registers for the whole key loop.
-//   * K tiles (A operand, [key][d]) and V tiles (stored transposed, [d][key],
-//     A operand of O^T = V^T P^T) are staged through LDS; the next tile's
-//     global loads are in flight while the current tile is computed.
+//   * K and V tiles go straight from global memory into double-buffered LDS
+//     (global_load_lds) in a row-major layout with an XOR swizzle; K is read
+//     row-wise (A operand of S^T), V with transposing LDS reads (A operand
+//     V^T of O^T = V^T P^T).  The next tile's loads are in flight while the
+//     current tile is computed.
 //   * P^T goes from the score accumulators straight into the B operand of
-//     the second product: the key order inside a 16-key step is the
-//     accumulator's own row order (keys 0-3 and 8-11 in lanes 0-31, keys 4-7
-//     and 12-15 in lanes 32-63), and the V^T operand is read in that order.
+//     the second product; the transposed V^T reads deliver keys in the
+//     accumulator's row order.
 //   * The anchor column is folded in before the loop as the softmax's
 //     starting point (m = s_i0, l = 1, acc = v_0); inside the loop column 0
 //     is outside every query's document interval, so it is never counted
 //     twice.  Key tiles that see only the anchor are skipped.
+//   * The running maximum m is exact (the largest weight of every row is
+//     exactly 1 before bf16 rounding), but the O rescale is skipped, wave by
+//     wave, on tiles where no query's maximum grew; on long documents that
+//     is most tiles.
 #include "aa_internal.h"
 
 namespace aa {
-
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_fwd(
@@ -41,15 +45,12 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     const uint8_t* __restrict__ kkind, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
     int nq, float scale_log2, bf16* __restrict__ o, float* __restrict__ lse) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
-  constexpr int KST = D + 8;     // K tile row stride in bf16 (16 bytes of padding)
-  constexpr int VST = BN + 4;    // V^T tile row stride in bf16
   constexpr int NKK = D / 16;    // 16-wide reduction steps over d
   constexpr int NDB = D / 32;    // 32-row blocks of d in O^T
   constexpr int NKB = BN / 32;   // 32-key blocks of a key tile
-  constexpr int KCH = BN * D / 8 / 256;          // 16-byte K chunks per thread
-  constexpr int VGROUPS = (BN / 4) * (D / 8);    // 4 keys x 8 features per group
-  __shared__ __align__(16) bf16 Ks[BN * KST];
-  __shared__ __align__(16) bf16 Vt[D * VST];
+  using T = SwzTile<D>;
+  __shared__ __align__(16) bf16 Ks[2][BN * D];
+  __shared__ __align__(16) bf16 Vs[2][BN * D];
 
   const int tile = blockIdx.x;   // b * nq + qt
   const int hq = blockIdx.y;
@@ -92,63 +93,36 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        acc[db][j] = (float)v0[32 * db + 8 * (j >> 2) + 4 * h + (j & 3)];
+      for (int g = 0; g < 4; ++g) {
+        const bf16x4 w = *(const bf16x4*)(v0 + 32 * db + 8 * g + 4 * h);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[db][4 * g + r] = (float)w[r];
+      }
   }
 
-  // Staging registers for the next key tile.
-  bf16x8 kreg[KCH];
-  bf16x8 vreg[4];
+  // K and V tiles are loaded straight into LDS, double-buffered.
   const size_t kv_row_stride = (size_t)Hkv * D;
   const bf16* kbase = kr + tok0 * kv_row_stride + hkv * D;
   const bf16* vbase = v + tok0 * kv_row_stride + hkv * D;
-  const int vg_key = (tid / (D / 8)) * 4, vg_d = (tid % (D / 8)) * 8;
-
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / (D / 8), ch = c % (D / 8);
-      const int key = min(kt * BN + r, S - 1);
-      kreg[u] = *(const bf16x8*)(kbase + key * kv_row_stride + ch * 8);
-    }
-    if (tid < VGROUPS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = min(kt * BN + vg_key + r, S - 1);
-        vreg[r] = *(const bf16x8*)(vbase + key * kv_row_stride + vg_d);
-      }
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c / (D / 8), ch = c % (D / 8);
-      *(bf16x8*)(Ks + r * KST + ch * 8) = kreg[u];
-    }
-    if (tid < VGROUPS) {
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        bf16x4 w;
-        w[0] = vreg[0][dd]; w[1] = vreg[1][dd]; w[2] = vreg[2][dd]; w[3] = vreg[3][dd];
-        *(bf16x4*)(Vt + (vg_d + dd) * VST + vg_key) = w;
-      }
-    }
+  auto issue = [&](int buf, int kt) {
+    tile_load_direct<D, BN, 256>(Ks[buf], kbase, kv_row_stride, kt * BN, S - 1);
+    tile_load_direct<D, BN, 256>(Vs[buf], vbase, kv_row_stride, kt * BN, S - 1);
   };
 
   int e = qptr[tile];
   const int e_end = qptr[tile + 1];
   if (e < e_end && kkind[e] == kTileAnchor) ++e;   // only key tile 0 can be anchor-only
-  if (e < e_end) gload(kidx[e]);
+  if (e < e_end) issue(0, kidx[e]);
+  int cur = 0;
 
   while (e < e_end) {
     const int kt = kidx[e];
     const bool need_mask = kkind[e] != kTileFull || kt == 0;
-    __syncthreads();                 // every wave is done with the previous tile
-    lstore();
-    __syncthreads();
-    if (e + 1 < e_end) gload(kidx[e + 1]);
+    wait_direct_loads();
+    __syncthreads();                 // tile e in buffer cur; buffer cur^1 free
+    if (e + 1 < e_end) issue(cur ^ 1, kidx[e + 1]);
+    const bf16* Kc = Ks[cur];
+    const bf16* Vc = Vs[cur];
 
     // S^T = K Q^T for this wave's 32 queries and the BN keys of the tile.
     f32x16 st[NKB];
@@ -156,62 +130,61 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) st[kb][j] = 0.f;
-      const bf16* ka = Ks + (kb * 32 + col) * KST + 8 * h;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) st[kb] = mfma32(*(const bf16x8*)(ka + 16 * kk), qf[kk], st[kb]);
+      for (int kk = 0; kk < NKK; ++kk)
+        st[kb] = mfma32(*(const bf16x8*)(Kc + T::chunk_off(kb * 32 + col, 2 * kk + h)), qf[kk],
+                        st[kb]);
     }
-
-    // Scale to log2 units, mask, tile max.
+    if (need_mask) {
+      // keys outside [qlo, qhi] (row-local) are masked
+      const int a = qlo - kt * BN - 4 * h, z = qhi - kt * BN - 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
+          st[kb][j] = (off >= a && off <= z) ? st[kb][j] : -INFINITY;
+        }
+    }
+    // Tile maximum (raw scores; the scale is positive).
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float t = st[kb][j] * scale_log2;
-        if (need_mask) {
-          const int key = kt * BN + kb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-          t = (key >= qlo && key <= qhi) ? t : -INFINITY;
-        }
-        st[kb][j] = t;
-        mt = fmaxf(mt, t);
-      }
-    mt = fmaxf(mt, partner(mt));
-    const float m_new = fmaxf(m, mt);     // m is finite: it started at the anchor logit
-    const float factor = exp2f(m - m_new);
-    m = m_new;
+      for (int j = 0; j < 16; j += 2) mt = fmaxf(mt, fmaxf(st[kb][j], st[kb][j + 1]));
+    mt = fmaxf(mt, partner(mt)) * scale_log2;
+    const bool raise = mt > m;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float m_new = raise ? mt : m;
+      const float factor = __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l *= factor;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[db][j] *= factor;
+    }
 
-    // P^T = exp2(t - m) as bf16 B operands, one per 16-key step.
+    // P^T = exp2(s * scale_log2 - m) as bf16 B operands, one per 16-key step.
     bf16x8 pb[BN / 16];
-    float ls = 0.f;
+    const float nm = -m;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = exp2f(st[kb][j] - m_new);
-        ls += p;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j], scale_log2, nm));
+        l += p;
         pb[2 * kb + (j >> 3)][j & 7] = (bf16)p;
       }
-    l = l * factor + ls;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[db][j] *= factor;
 
     // O^T += V^T P^T.
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const bf16* va = Vt + (32 * db + col) * VST + 4 * h;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int c = 0; c < BN / 16; ++c) {
-        const bf16x4 lo4 = *(const bf16x4*)(va + 16 * c);
-        const bf16x4 hi4 = *(const bf16x4*)(va + 16 * c + 8);
-        bf16x8 a;
-        a[0] = lo4[0]; a[1] = lo4[1]; a[2] = lo4[2]; a[3] = lo4[3];
-        a[4] = hi4[0]; a[5] = hi4[1]; a[6] = hi4[2]; a[7] = hi4[3];
-        acc[db] = mfma32(a, pb[c], acc[db]);
-      }
-    }
+      for (int c = 0; c < BN / 16; ++c)
+        acc[db] = mfma32(tr_operand<D>(Vc, 16 * c, 32 * db), pb[c], acc[db]);
     ++e;
+    cur ^= 1;
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.

@@ -46,6 +46,7 @@ def test_fwd_bwd_small_full_compare(gpu_lib, case):
     o, lse = gpu_lib.anchor_attn_fwd(q.cuda(), k.cuda(), v.cuda(), cu, base, causal)
     o_ref, lse_ref, _, _ = oracle.forward(q, k, v, cu, base, causal)
     o_g = f64(o).reshape(B * S, Hq, D)
+    say(f"[parity] {name} O err {o_err(o_g, o_ref):.2e}")
     assert o_err(o_g, o_ref) <= O_TOL, o_err(o_g, o_ref)
     lse_g = f64(lse).transpose(1, 0, 2).reshape(Hq, B * S)
     assert np.abs(lse_g - lse_ref).max() <= LSE_TOL
