@@ -196,6 +196,21 @@ __device__ __forceinline__ void tile_load_direct(bf16* lds_tile, const bf16* gba
 // have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// ---------------------------------------------------------------- XCD-aware order
+// The MI355X dispatcher deals consecutive workgroup ids round-robin to its
+// 8 XCDs, each with a private L2.  Work items that share K/V or Q/dO tiles
+// are neighbours in the natural order (tiles of one head and document), so a
+// launch of padded_grid(total) workgroups maps id L to work item
+// (L % 8) * per + L / 8: every XCD walks one contiguous slice of the items.
+// Returns -1 for the padding workgroups (at most 7).
+constexpr int kXcds = 8;
+__host__ __device__ inline int xcd_per(int total) { return (total + kXcds - 1) / kXcds; }
+__host__ __device__ inline int padded_grid(int total) { return xcd_per(total) * kXcds; }
+__device__ __forceinline__ int xcd_work_item(int linear, int total) {
+  const int w = (linear % kXcds) * xcd_per(total) + linear / kXcds;
+  return w < total ? w : -1;
+}
+
 // Tile shapes of the attention kernels.
 constexpr int kFwdBM = 128, kFwdBN = 64;     // forward and dQ: query tile x key tile
 constexpr int kDkvBM = 64, kDkvBN = 128;     // dK/dV: query tile x key tile

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
     const int32_t* __restrict__ kptr, const int32_t* __restrict__ qidx,
     const uint8_t* __restrict__ qkind, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
-    int nk, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
+    int nk, int n_items, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
   constexpr int BM = kDkvBM, BN = kDkvBN;    // 64 queries x 128 keys
   constexpr int NKK = D / 16;
   constexpr int NDH = D / 64;                // 32-feature blocks per half
@@ -141,8 +141,11 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
   __shared__ __align__(16) float s_lse[2][BM], s_dv[2][BM];
   __shared__ __align__(16) int s_lo[2][BM], s_hi[2][BM];
 
-  const int b = blockIdx.x / nk, kt = blockIdx.x % nk;
-  const int hkv = blockIdx.y;
+  const int item = xcd_work_item(blockIdx.x, n_items);   // (hkv, b, kt), kt fastest
+  if (item < 0) return;
+  const int ktile = item % (n_items / Hkv);                // b * nk + kt
+  const int hkv = item / (n_items / Hkv);
+  const int b = ktile / nk, kt = ktile % nk;
   const int group = Hq / Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
   };
 
   // Work list: every q head of the group x every live, not anchor-only query tile.
-  const int e_begin = kptr[blockIdx.x], e_end = kptr[blockIdx.x + 1];
+  const int e_begin = kptr[ktile], e_end = kptr[ktile + 1];
   const int h_end = (hkv + 1) * group;
   auto first = [&](int& ee, int& hh) {
     ee = e_begin;
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const int32_t* __restrict__ pos, const int32_t* __restrict__ lo,
     const int32_t* __restrict__ hi, const int32_t* __restrict__ qptr,
     const int32_t* __restrict__ kidx, const uint8_t* __restrict__ kkind,
-    const int32_t* __restrict__ status, int S, int Hq, int Hkv, int nq, float scale,
+    const int32_t* __restrict__ status, int S, int Hq, int Hkv, int nq, int n_items, float scale,
     bf16* __restrict__ dq) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int NKK = D / 16;
@@ -352,8 +355,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   __shared__ __align__(16) bf16 Ks[2][BN * D];
   __shared__ __align__(16) bf16 Vs[2][BN * D];
 
-  const int tile = blockIdx.x;
-  const int hq = blockIdx.y;
+  const int item = xcd_work_item(blockIdx.x, n_items);   // (hq, b, qt), qt fastest
+  if (item < 0) return;
+  const int tile = item % (n_items / Hq);
+  const int hq = item / (n_items / Hq);
   const int b = tile / nq, qt = tile % nq;
   const int hkv = hq / (Hq / Hkv);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -473,22 +478,36 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
 }
 
 // ---------------------------------------------------------------------------
-// anchor: one workgroup per (row b, kv head); thread d sums the partials of
-// the group's query heads and row blocks into dk_0[d], dv_0[d].  The anchor's
-// position is 0, so R(0)^T = I.
+// anchor: one workgroup of 1024 threads per (row b, kv head).  Thread
+// (part, d) sums every parts-th row-block partial of the group's query heads
+// for feature d; the parts are then added in LDS.  The anchor's position is
+// 0, so R(0)^T = I.
 // ---------------------------------------------------------------------------
-__global__ void k_bwd_anchor(const float* __restrict__ part_dk, const float* __restrict__ part_dv,
-                             const int32_t* __restrict__ status, int S, int Hq, int Hkv, int D,
-                             int nblk, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
-  const int b = blockIdx.x, hkv = blockIdx.y;
+__global__ __launch_bounds__(1024) void k_bwd_anchor(
+    const float* __restrict__ part_dk, const float* __restrict__ part_dv,
+    const int32_t* __restrict__ status, int S, int Hq, int Hkv, int D, int nblk, float scale,
+    bf16* __restrict__ dk, bf16* __restrict__ dv) {
+  __shared__ float red[2][1024];
+  const int b = blockIdx.x / Hkv, hkv = blockIdx.x % Hkv;
   const int group = Hq / Hkv;
+  const int parts = 1024 / D;
+  const int d = threadIdx.x % D, part = threadIdx.x / D;
   const bool bad = status[0] != kStatusOk;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float sk = 0.f, sv = 0.f;
-    for (int hq = hkv * group; hq < (hkv + 1) * group; ++hq) {
-      const float* pk = part_dk + ((size_t)b * Hq + hq) * nblk * D + d;
-      const float* pv = part_dv + ((size_t)b * Hq + hq) * nblk * D + d;
-      for (int n = 0; n < nblk; ++n) { sk += pk[(size_t)n * D]; sv += pv[(size_t)n * D]; }
+  float sk = 0.f, sv = 0.f;
+  for (int hq = hkv * group; hq < (hkv + 1) * group; ++hq) {
+    const size_t base = ((size_t)b * Hq + hq) * nblk * D + d;
+    for (int n = part; n < nblk; n += parts) {
+      sk += part_dk[base + (size_t)n * D];
+      sv += part_dv[base + (size_t)n * D];
+    }
+  }
+  red[0][threadIdx.x] = sk;
+  red[1][threadIdx.x] = sv;
+  __syncthreads();
+  if (part == 0) {
+    for (int q = 1; q < parts; ++q) {
+      sk += red[0][q * D + d];
+      sv += red[1][q * D + d];
     }
     const size_t off = ((size_t)b * S * Hkv + hkv) * D + d;
     dk[off] = (bf16)(bad ? NAN : sk * scale);
@@ -511,33 +530,35 @@ hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, hipStream_t st) {
-  const dim3 grid(a.B * pk.nk, a.Hkv);
+  const int n_items = a.B * pk.nk * a.Hkv;
+  const dim3 grid(padded_grid(n_items));
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_dkdv<128>, grid, dim3(512), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pk.kptr, pk.qidx, pk.qkind,
-                       a.status, a.S, a.Hq, a.Hkv, pk.nk, a.scale, a.dk, a.dv);
+                       a.status, a.S, a.Hq, a.Hkv, pk.nk, n_items, a.scale, a.dk, a.dv);
   else
     hipLaunchKernelGGL(k_bwd_dkdv<64>, grid, dim3(512), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pk.kptr, pk.qidx, pk.qkind,
-                       a.status, a.S, a.Hq, a.Hkv, pk.nk, a.scale, a.dk, a.dv);
+                       a.status, a.S, a.Hq, a.Hkv, pk.nk, n_items, a.scale, a.dk, a.dv);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, const PlanBufs& pq, hipStream_t st) {
-  const dim3 grid(a.B * pq.nq, a.Hq);
+  const int n_items = a.B * pq.nq * a.Hq;
+  const dim3 grid(padded_grid(n_items));
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kidx,
-                       pq.kkind, a.status, a.S, a.Hq, a.Hkv, pq.nq, a.scale, a.dq);
+                       pq.kkind, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.dq);
   else
     hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kidx,
-                       pq.kkind, a.status, a.S, a.Hq, a.Hkv, pq.nq, a.scale, a.dq);
+                       pq.kkind, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.dq);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_anchor(const BwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_bwd_anchor, dim3(a.B, a.Hkv), dim3(128), 0, st, a.part_dk, a.part_dv,
+  hipLaunchKernelGGL(k_bwd_anchor, dim3(a.B * a.Hkv), dim3(1024), 0, st, a.part_dk, a.part_dv,
                      a.status, a.S, a.Hq, a.Hkv, a.D, a.nblk, a.scale, a.dk, a.dv);
   return hipGetLastError();
 }

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
     const int32_t* __restrict__ qptr, const int32_t* __restrict__ kidx,
     const uint8_t* __restrict__ kkind, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
-    int nq, float scale_log2, bf16* __restrict__ o, float* __restrict__ lse) {
+    int nq, int n_items, float scale_log2, bf16* __restrict__ o, float* __restrict__ lse) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int NKK = D / 16;    // 16-wide reduction steps over d
   constexpr int NDB = D / 32;    // 32-row blocks of d in O^T
@@ -52,8 +52,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   __shared__ __align__(16) bf16 Ks[2][BN * D];
   __shared__ __align__(16) bf16 Vs[2][BN * D];
 
-  const int tile = blockIdx.x;   // b * nq + qt
-  const int hq = blockIdx.y;
+  const int item = xcd_work_item(blockIdx.x, n_items);   // (hq, b, qt), qt fastest
+  if (item < 0) return;
+  const int tile = item % (n_items / Hq);   // b * nq + qt
+  const int hq = item / (n_items / Hq);
   const int b = tile / nq, qt = tile % nq;
   const int hkv = hq / (Hq / Hkv);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -212,13 +214,14 @@ hipError_t launch_fwd(const bf16* qr, const bf16* kr, const bf16* v, TokenTables
                       const PlanBufs& pb, const int32_t* status, int B, int S, int Hq, int Hkv,
                       int D, float scale, bf16* o, float* lse, hipStream_t st) {
   const float scale_log2 = scale * 1.44269504088896340736f;
-  const dim3 grid(B * pb.nq, Hq);
+  const int n_items = B * pb.nq * Hq;
+  const dim3 grid(padded_grid(n_items));
   if (D == 128) {
     hipLaunchKernelGGL(k_fwd<128>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
-                       pb.kidx, pb.kkind, status, S, Hq, Hkv, pb.nq, scale_log2, o, lse);
+                       pb.kidx, pb.kkind, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, o, lse);
   } else {
     hipLaunchKernelGGL(k_fwd<64>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
-                       pb.kidx, pb.kkind, status, S, Hq, Hkv, pb.nq, scale_log2, o, lse);
+                       pb.kidx, pb.kkind, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, o, lse);
   }
   return hipGetLastError();
 }
