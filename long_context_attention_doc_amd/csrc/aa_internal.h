@@ -43,14 +43,17 @@ struct PlanBufs {
   int BM, BN, nq, nk;
   size_t cap;          // B * nq * nk
   uint8_t* kinds;      // dense [B][nq][nk]
+  uint8_t* kinds_t;    // dense [B][nk][nq] (key-major copy)
   int32_t* cntq;       // [B*nq]
   int32_t* cntk;       // [B*nk]
   int32_t* qptr;       // [B*nq + 1]
   int32_t* kidx;       // [cap]
   uint8_t* kkind;      // [cap]
+  int32_t* kpack;      // [cap] kidx | kkind << 24 (read with scalar loads), may be null
   int32_t* kptr;       // [B*nk + 1]
   int32_t* qidx;       // [cap]
   uint8_t* qkind;      // [cap]
+  int32_t* qpack;      // [cap] qidx | qkind << 24, may be null
   int32_t* n_live;     // [1]
 };
 
@@ -78,6 +81,7 @@ struct BwdArgs {
   const int32_t* status;
   float* dvec;         // [B,Hq,S]   rowsum(dO * O)
   float* ds0;          // [B,Hq,S]   dS of the anchor column
+  float* qstats;       // [B,Hq,nblk][4][kPreRows] per 64-query tile: LSE*log2(e), Dv, lo, hi
   float* part_dk;      // [B,Hq,nblk,D] per-row-block sums for the anchor key
   float* part_dv;      // [B,Hq,nblk,D]
   int nblk;
@@ -196,6 +200,14 @@ __device__ __forceinline__ void tile_load_direct(bf16* lds_tile, const bf16* gba
 // have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N of this wave's vector memory loads are outstanding
+// (s_waitcnt vmcnt(N), N < 16): the loads issued before the last N are done.
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // ---------------------------------------------------------------- XCD-aware order
 // The MI355X dispatcher deals consecutive workgroup ids round-robin to its
 // 8 XCDs, each with a private L2.  Work items that share K/V or Q/dO tiles
@@ -210,6 +222,11 @@ __device__ __forceinline__ int xcd_work_item(int linear, int total) {
   const int w = (linear % kXcds) * xcd_per(total) + linear / kXcds;
   return w < total ? w : -1;
 }
+
+// Packed plan entries: tile index in the low 24 bits, kind in the high 8.
+__host__ __device__ inline int pack_tile(int idx, int kind) { return idx | (kind << 24); }
+__device__ __forceinline__ int packed_idx(int v) { return v & 0xffffff; }
+__device__ __forceinline__ int packed_kind(int v) { return (unsigned)v >> 24; }
 
 // Tile shapes of the attention kernels.
 constexpr int kFwdBM = 128, kFwdBN = 64;     // forward and dQ: query tile x key tile

@@ -4,7 +4,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "../../include/anchor_attn.h"
+#include "anchor_attn.h"
 #include "aa_internal.h"
 
 namespace aa {
@@ -17,7 +17,7 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct PlanLayout {
   int BM, BN, nq, nk;
   size_t cap;
-  size_t kinds, cntq, cntk, qptr, kidx, kkind, kptr, qidx, qkind, n_live, end;
+  size_t kinds, kinds_t, cntq, cntk, qptr, kidx, kkind, kpack, kptr, qidx, qkind, qpack, n_live, end;
 };
 
 PlanLayout plan_layout(int B, int S, int BM, int BN, size_t base) {
@@ -29,14 +29,17 @@ PlanLayout plan_layout(int B, int S, int BM, int BN, size_t base) {
   p.cap = (size_t)B * p.nq * p.nk;
   size_t o = up(base);
   p.kinds = o;  o = up(o + p.cap);
+  p.kinds_t = o; o = up(o + p.cap);
   p.cntq = o;   o = up(o + (size_t)B * p.nq * 4);
   p.cntk = o;   o = up(o + (size_t)B * p.nk * 4);
   p.qptr = o;   o = up(o + ((size_t)B * p.nq + 1) * 4);
   p.kidx = o;   o = up(o + p.cap * 4);
   p.kkind = o;  o = up(o + p.cap);
+  p.kpack = o;  o = up(o + p.cap * 4);
   p.kptr = o;   o = up(o + ((size_t)B * p.nk + 1) * 4);
   p.qidx = o;   o = up(o + p.cap * 4);
   p.qkind = o;  o = up(o + p.cap);
+  p.qpack = o;  o = up(o + p.cap * 4);
   p.n_live = o; o = up(o + 4);
   p.end = o;
   return p;
@@ -46,14 +49,17 @@ PlanBufs plan_bufs(const PlanLayout& l, char* ws) {
   PlanBufs b;
   b.BM = l.BM; b.BN = l.BN; b.nq = l.nq; b.nk = l.nk; b.cap = l.cap;
   b.kinds = (uint8_t*)(ws + l.kinds);
+  b.kinds_t = (uint8_t*)(ws + l.kinds_t);
   b.cntq = (int32_t*)(ws + l.cntq);
   b.cntk = (int32_t*)(ws + l.cntk);
   b.qptr = (int32_t*)(ws + l.qptr);
   b.kidx = (int32_t*)(ws + l.kidx);
   b.kkind = (uint8_t*)(ws + l.kkind);
+  b.kpack = (int32_t*)(ws + l.kpack);
   b.kptr = (int32_t*)(ws + l.kptr);
   b.qidx = (int32_t*)(ws + l.qidx);
   b.qkind = (uint8_t*)(ws + l.qkind);
+  b.qpack = (int32_t*)(ws + l.qpack);
   b.n_live = (int32_t*)(ws + l.n_live);
   return b;
 }
@@ -63,7 +69,7 @@ struct Layout {
   size_t status, pos, lo, hi, table, qrot, krot;
   PlanLayout pq;        // query-major plan of the forward and dq kernels
   PlanLayout pk;        // key-major plan of the dkdv kernel (backward only)
-  size_t dvec, ds0, pdk, pdv;
+  size_t dvec, ds0, pdk, pdv, qstats;
   int nblk;
   size_t total;
 };
@@ -89,9 +95,10 @@ Layout layout(int B, int S, int Hq, int Hkv, int D, bool bwd) {
     L.ds0 = o;  o = up(o + (size_t)B * Hq * S * 4);
     L.pdk = o;  o = up(o + (size_t)B * Hq * L.nblk * D * 4);
     L.pdv = o;  o = up(o + (size_t)B * Hq * L.nblk * D * 4);
+    L.qstats = o; o = up(o + (size_t)B * Hq * L.nblk * 4 * kPreRows * 4);
   } else {
     L.pk = L.pq;
-    L.dvec = L.ds0 = L.pdk = L.pdv = 0;
+    L.dvec = L.ds0 = L.pdk = L.pdv = L.qstats = 0;
   }
   L.total = o;
   return L;
@@ -255,6 +262,7 @@ aa_status anchor_attn_bwd(const void* q, const void* k, const void* v, const voi
   a.ds0 = (float*)(ws + L.ds0);
   a.part_dk = (float*)(ws + L.pdk);
   a.part_dv = (float*)(ws + L.pdv);
+  a.qstats = (float*)(ws + L.qstats);
   a.nblk = L.nblk;
   a.dq = (bf16*)dq;
   a.dk = (bf16*)dk;
@@ -322,6 +330,7 @@ aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, in
   // the caller's output arrays replace the workspace copies
   pb.qptr = qptr; pb.kidx = kidx; pb.kkind = kkind;
   pb.kptr = kptr; pb.qidx = qidx; pb.qkind = qkind; pb.n_live = n_live;
+  pb.kpack = nullptr; pb.qpack = nullptr;
   hipLaunchKernelGGL(k_zero_status, dim3(1), dim3(64), 0, stream, status);
   AA_HIP(hipGetLastError());
   AA_HIP(launch_positions(cu_doc_lens, n_seg, B, S, causal, 0, tt, status, stream));

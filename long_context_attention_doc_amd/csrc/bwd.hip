@@ -36,8 +36,9 @@ template <int D>
 __global__ __launch_bounds__(256) void k_bwd_pre(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
     const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
-    int S, int Hq, int Hkv, int nblk, float scale, float* __restrict__ dvec,
-    float* __restrict__ ds0, float* __restrict__ part_dk, float* __restrict__ part_dv) {
+    const int32_t* __restrict__ lo, const int32_t* __restrict__ hi, int S, int Hq, int Hkv,
+    int nblk, float scale, float* __restrict__ dvec, float* __restrict__ ds0,
+    float* __restrict__ part_dk, float* __restrict__ part_dv, float* __restrict__ qstats) {
   constexpr int LPR = D / 8;                // lanes per row
   constexpr int RPP = 256 / LPR;            // rows per pass of the workgroup
   __shared__ float red_k[RPP][D + 4];
@@ -85,6 +86,15 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
       dvec[((size_t)b * Hq + hq) * S + row] = d_o;
       ds0[((size_t)b * Hq + hq) * S + row] = dsv;
     }
+    if ((tid % LPR) == 0) {
+      // tile-aligned record for the dK/dV kernel; rows past S see nothing
+      float* rec = qstats + (((size_t)b * Hq + hq) * nblk + blk) * 4 * kPreRows;
+      const int rr = r0 + slot;
+      rec[rr] = valid ? L * kLog2e : 0.f;
+      rec[kPreRows + rr] = valid ? d_o : 0.f;
+      rec[2 * kPreRows + rr] = __int_as_float(valid ? lo[tok] : 1);
+      rec[3 * kPreRows + rr] = __int_as_float(valid ? hi[tok] : 0);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       pk[i] += dsv * (float)qv[i];
@@ -108,16 +118,17 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
 
 // ---------------------------------------------------------------------------
 // dkdv: one workgroup of eight waves per (row b, kv head, key tile of 128
-// keys).  Wave w owns the 32 keys kg = w % 4 of the tile and the half
-// p = w / 4: it computes S = Q K^T and dP = dO V^T for queries
-// [32p, 32p+32) of each 64-query tile, and accumulates dV^T and dK^T for
-// features [64p, 64p+64) over all 64 queries.  The two waves of a key group
-// swap their halves of P and dS through LDS, so each wave holds only half of
-// the key gradients (2 x 64 accumulator registers instead of 2 x 128) and the
-// kernel runs two waves per SIMD.
-//   * K^T and V^T (B operands, keys as columns) stay in registers.
-//   * Q and dO tiles go straight into double-buffered swizzled LDS
-//     (global_load_lds); row reads feed S and dP, transposing reads feed Q^T
+// keys).  Wave w owns the 32 keys kg = w % 4 of the tile and the query half
+// p = w / 4: for queries [32p, 32p+32) of each 64-query tile it computes
+// S = Q K^T and dP = dO V^T, and accumulates its share of dV^T = dO^T P and
+// dK^T = Q^T dS over all D features.  The two waves of a key group never
+// talk inside the loop (no exchange, one barrier per tile); their partial
+// key gradients are added through LDS once, at the end.
+//   * V^T (B operand of dP, keys as columns) stays in registers; the
+//     workgroup's 128 K rows sit in swizzled LDS for the whole loop (B operand
+//     of S), which keeps the kernel within 256 registers per lane.
+//   * Q and dO tiles go straight into swizzled LDS (global_load_lds), up to
+//     two tiles ahead; row reads feed S and dP, transposing reads feed Q^T
 //     and dO^T.
 //   * P and dS feed the B operand of dV^T = dO^T P and dK^T = Q^T dS straight
 //     from the accumulator layout.
@@ -125,21 +136,21 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
 template <int D>
 __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
-    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dvec,
+    const bf16* __restrict__ dout, const float* __restrict__ qstats,
     const float* __restrict__ table, const int32_t* __restrict__ pos,
-    const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
-    const int32_t* __restrict__ kptr, const int32_t* __restrict__ qidx,
-    const uint8_t* __restrict__ qkind, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
-    int nk, int n_items, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
+    const int32_t* __restrict__ kptr, const int32_t* __restrict__ qpack,
+    const int32_t* __restrict__ status, int S, int Hq, int Hkv,
+    int nk, int nblk, int n_items, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
   constexpr int BM = kDkvBM, BN = kDkvBN;    // 64 queries x 128 keys
   constexpr int NKK = D / 16;
-  constexpr int NDH = D / 64;                // 32-feature blocks per half
+  constexpr int NDB = D / 32;                // 32-feature blocks
+  constexpr int NBUF = 3;                    // tiles in flight: current + 2 prefetched
+  constexpr int LD_ITERS = BM * (D / 8) / 512;   // direct-load instructions per wave and tensor
   using T = SwzTile<D>;
-  __shared__ __align__(16) bf16 Qs[2][BM * D];
-  __shared__ __align__(16) bf16 Gs[2][BM * D];
-  __shared__ __align__(16) bf16x8 Xs[4][2][4][64];   // [key group][P, dS][16-query step][lane]
-  __shared__ __align__(16) float s_lse[2][BM], s_dv[2][BM];
-  __shared__ __align__(16) int s_lo[2][BM], s_hi[2][BM];
+  __shared__ __align__(16) bf16 Qs[NBUF][BM * D];
+  __shared__ __align__(16) bf16 Gs[NBUF][BM * D];
+  __shared__ __align__(16) float s_st[NBUF][4][BM];  // LSE*log2(e), Dv, lo, hi (int bits)
+  __shared__ __align__(16) bf16 Ks[BN * D];          // this workgroup's keys (rotated)
 
   const int item = xcd_work_item(blockIdx.x, n_items);   // (hkv, b, kt), kt fastest
   if (item < 0) return;
@@ -157,48 +168,44 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
   const bool bad = status[0] != kStatusOk;
   const float scale_log2 = scale * kLog2e;
 
-  // K^T and V^T operands: lane holds key `col`, features 16*kk + 8*h + i.
-  bf16x8 kf[NKK], vf[NKK];
+  // V^T operand: lane holds key `col`, features 16*kk + 8*h + i; K rows in LDS.
+  bf16x8 vf[NKK];
   {
-    const bf16* kp = kr + (ktok * Hkv + hkv) * D + 8 * h;
     const bf16* vp = v + (ktok * Hkv + hkv) * D + 8 * h;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      kf[kk] = *(const bf16x8*)(kp + 16 * kk);
-      vf[kk] = *(const bf16x8*)(vp + 16 * kk);
-    }
+    for (int kk = 0; kk < NKK; ++kk) vf[kk] = *(const bf16x8*)(vp + 16 * kk);
+    const size_t kv_row_stride = (size_t)Hkv * D;
+    tile_load_direct<D, BN, 512>(Ks, kr + tok0 * kv_row_stride + hkv * D, kv_row_stride, kt * BN,
+                                 S - 1);
   }
-  f32x16 dka[NDH], dva[NDH];
+  f32x16 dka[NDB], dva[NDB];
 #pragma unroll
-  for (int db = 0; db < NDH; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) { dka[db][j] = 0.f; dva[db][j] = 0.f; }
 
-  // Q and dO tiles go straight into double-buffered LDS; the per-query
-  // statistics (LSE, Dv, visible-key interval) are staged by threads 0-63.
-  float r_lse = 0.f, r_dv = 0.f;
-  int r_lo = 1, r_hi = 0;
+  // Q and dO tiles go straight into LDS; wave 0 also fetches the tile's
+  // per-query record (LSE, Dv, visible-key interval).
   const size_t q_row_stride = (size_t)Hq * D;
   auto issue = [&](int buf, int hq, int qt) {
     tile_load_direct<D, BM, 512>(Qs[buf], qr + tok0 * q_row_stride + (size_t)hq * D, q_row_stride,
                                  qt * BM, S - 1);
     tile_load_direct<D, BM, 512>(Gs[buf], dout + tok0 * q_row_stride + (size_t)hq * D,
                                  q_row_stride, qt * BM, S - 1);
-    if (tid < BM) {
-      const int q = qt * BM + tid;
-      const int qc = min(q, S - 1);
-      r_lse = lse[((size_t)b * Hq + hq) * S + qc] * kLog2e;
-      r_dv = dvec[((size_t)b * Hq + hq) * S + qc];
-      r_lo = q < S ? lo[tok0 + qc] : 1;
-      r_hi = q < S ? hi[tok0 + qc] : 0;
+    if (wave == 0) {
+      const float* rec = qstats + (((size_t)b * Hq + hq) * nblk + qt) * 4 * BM;
+      __builtin_amdgcn_global_load_lds((const void*)(rec + 4 * lane), (lds_void*)(&s_st[buf][0][0]),
+                                       16, 0, 0);
     }
   };
-  auto stats_store = [&](int buf) {
-    if (tid < BM) {
-      s_lse[buf][tid] = r_lse;
-      s_dv[buf][tid] = r_dv;
-      s_lo[buf][tid] = r_lo;
-      s_hi[buf][tid] = r_hi;
+  // wait for the current tile while the next one may stay in flight
+  auto wait_current = [&](bool next_in_flight) {
+    if (!next_in_flight) {
+      wait_direct_loads();
+    } else if (wave == 0) {
+      wait_loads_but<2 * LD_ITERS + 1>();
+    } else {
+      wait_loads_but<2 * LD_ITERS>();
     }
   };
 
@@ -209,29 +216,33 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
     ee = e_begin;
     hh = hkv * group;
     if (e_begin >= e_end) { hh = h_end; return; }
-    while (ee < e_end && qkind[ee] == kTileAnchor) ++ee;
+    while (ee < e_end && packed_kind(qpack[ee]) == kTileAnchor) ++ee;
     if (ee >= e_end) hh = h_end;             // nothing live besides the anchor
   };
   auto advance = [&](int& ee, int& hh) {
     do {
       ++ee;
       if (ee >= e_end) { ee = e_begin; ++hh; }
-    } while (hh < h_end && qkind[ee] == kTileAnchor);
+    } while (hh < h_end && packed_kind(qpack[ee]) == kTileAnchor);
   };
 
   int e, hq;
   first(e, hq);
-  if (hq < h_end) issue(0, hq, qidx[e]);
+  int e1 = e, h1 = hq;
+  if (hq < h_end) {
+    issue(0, hq, packed_idx(qpack[e]));
+    advance(e1, h1);
+    if (h1 < h_end) issue(1, h1, packed_idx(qpack[e1]));
+  }
   int cur = 0;
   while (hq < h_end) {
-    const int qt = qidx[e];
-    const bool need_mask = qkind[e] != kTileFull || kt == 0;
-    wait_direct_loads();
-    stats_store(cur);
-    __syncthreads();      // tile in buffer `cur` visible; buffer cur^1 and Xs free
-    int e1 = e, h1 = hq;
-    advance(e1, h1);
-    if (h1 < h_end) issue(cur ^ 1, h1, qidx[e1]);
+    const bool need_mask = packed_kind(qpack[e]) != kTileFull || kt == 0;
+    int e2 = e1, h2 = h1;
+    if (h1 < h_end) advance(e2, h2);
+    const int qt2 = h2 < h_end ? packed_idx(qpack[e2]) : 0;
+    wait_current(h1 < h_end);
+    __syncthreads();      // tile in buffer `cur` visible; buffer cur+2 free
+    if (h2 < h_end) issue(cur >= 1 ? cur - 1 : cur + 2, h2, qt2);
     const bf16* Qc = Qs[cur];
     const bf16* Gc = Gs[cur];
 
@@ -242,22 +253,23 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int off = T::chunk_off(32 * p + col, 2 * kk + h);
-      sp = mfma32(*(const bf16x8*)(Qc + off), kf[kk], sp);
+      const bf16x8 kb = *(const bf16x8*)(Ks + T::chunk_off(32 * kg + col, 2 * kk + h));
+      sp = mfma32(*(const bf16x8*)(Qc + off), kb, sp);
       dp = mfma32(*(const bf16x8*)(Gc + off), vf[kk], dp);
     }
     // P = exp2(s * scale_log2 - lse_log2), dS = P (dP - Dv).
-    bf16x8 pown[2], down[2];
+    bf16x8 pb[2], db_[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int q0 = 32 * p + 8 * g + 4 * h;   // tile-local queries q0 .. q0+3
-      const f32x4 l4 = *(const f32x4*)(&s_lse[cur][q0]);
-      const f32x4 d4 = *(const f32x4*)(&s_dv[cur][q0]);
+      const f32x4 l4 = *(const f32x4*)(&s_st[cur][0][q0]);
+      const f32x4 d4 = *(const f32x4*)(&s_st[cur][1][q0]);
       float pv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[4 * g + r], scale_log2, -l4[r]));
       if (need_mask) {
-        const int4 lo4 = *(const int4*)(&s_lo[cur][q0]);
-        const int4 hi4 = *(const int4*)(&s_hi[cur][q0]);
+        const int4 lo4 = *(const int4*)(&s_st[cur][2][q0]);
+        const int4 hi4 = *(const int4*)(&s_st[cur][3][q0]);
         pv[0] = (key >= lo4.x && key <= hi4.x) ? pv[0] : 0.f;
         pv[1] = (key >= lo4.y && key <= hi4.y) ? pv[1] : 0.f;
         pv[2] = (key >= lo4.z && key <= hi4.z) ? pv[2] : 0.f;
@@ -266,64 +278,77 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * g + r;
-        pown[j >> 3][j & 7] = (bf16)pv[r];
-        down[j >> 3][j & 7] = (bf16)(pv[r] * (dp[j] - d4[r]));
+        pb[j >> 3][j & 7] = (bf16)pv[r];
+        db_[j >> 3][j & 7] = (bf16)(pv[r] * (dp[j] - d4[r]));
       }
     }
-    // swap halves with the partner wave of this key group
+    // dV^T += dO^T P, dK^T += Q^T dS over this wave's 32 queries.
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      Xs[kg][0][2 * p + c][lane] = pown[c];
-      Xs[kg][1][2 * p + c][lane] = down[c];
-    }
-    __syncthreads();
-    bf16x8 pf[4], df[4];
+    for (int dblk = 0; dblk < NDB; ++dblk)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if ((c >> 1) == p) {
-        pf[c] = pown[c & 1];
-        df[c] = down[c & 1];
-      } else {
-        pf[c] = Xs[kg][0][c][lane];
-        df[c] = Xs[kg][1][c][lane];
+      for (int c = 0; c < 2; ++c) {
+        dva[dblk] = mfma32(tr_operand<D>(Gc, 32 * p + 16 * c, 32 * dblk), pb[c], dva[dblk]);
+        dka[dblk] = mfma32(tr_operand<D>(Qc, 32 * p + 16 * c, 32 * dblk), db_[c], dka[dblk]);
       }
-    }
-    // dV^T += dO^T P, dK^T += Q^T dS for features [64p, 64p+64).
-#pragma unroll
-    for (int db = 0; db < NDH; ++db) {
-      const int f0 = 32 * (NDH * p + db);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        dva[db] = mfma32(tr_operand<D>(Gc, 16 * c, f0), pf[c], dva[db]);
-        dka[db] = mfma32(tr_operand<D>(Qc, 16 * c, f0), df[c], dka[db]);
-      }
-    }
     e = e1; hq = h1;
-    cur ^= 1;
+    e1 = e2; h1 = h2;
+    cur = cur == NBUF - 1 ? 0 : cur + 1;
   }
 
-  // Epilogue: dK = R(pos)^T (scale * dK'), dV as accumulated; this wave
-  // writes its 32 keys x features [64p, 64p+64).
-  if (kvalid) {
+  // Add the two query halves: waves p = 1 hand their partial sums to p = 0
+  // through LDS (the tile buffers are free now), dK first, then dV.
+  float* red = reinterpret_cast<float*>(&Qs[0][0]);    // [4 key groups][NDB][16][64] floats
+  const int red_off = ((kg * NDB) * 16) * 64 + lane;
+  __syncthreads();
+  if (p == 1) {
+#pragma unroll
+    for (int dblk = 0; dblk < NDB; ++dblk)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) red[red_off + (dblk * 16 + j) * 64] = dka[dblk][j];
+  }
+  __syncthreads();
+  if (p == 0) {
+#pragma unroll
+    for (int dblk = 0; dblk < NDB; ++dblk)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dka[dblk][j] += red[red_off + (dblk * 16 + j) * 64];
+  }
+  __syncthreads();
+  if (p == 1) {
+#pragma unroll
+    for (int dblk = 0; dblk < NDB; ++dblk)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) red[red_off + (dblk * 16 + j) * 64] = dva[dblk][j];
+  }
+  __syncthreads();
+  if (p == 0) {
+#pragma unroll
+    for (int dblk = 0; dblk < NDB; ++dblk)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dva[dblk][j] += red[red_off + (dblk * 16 + j) * 64];
+  }
+
+  // Epilogue (waves p = 0): dK = R(pos)^T (scale * dK'), dV as accumulated.
+  if (p == 0 && kvalid) {
     const int pk = pos[ktok];
     const float* tb = table + (size_t)pk * D;      // (D/2) pairs of {cos, sin}
     bf16* dkp = dk + (ktok * Hkv + hkv) * D;
     bf16* dvp = dv + (ktok * Hkv + hkv) * D;
 #pragma unroll
-    for (int db = 0; db < NDH; ++db)
+    for (int dblk = 0; dblk < NDB; ++dblk)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * (NDH * p + db) + 8 * g + 4 * h;
+        const int d0 = 32 * dblk + 8 * g + 4 * h;
         const f32x4 cs = *(const f32x4*)(tb + d0);    // cos, sin of pairs d0/2, d0/2+1
         bf16x4 wk, wv;
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
           const float c = cs[2 * pr], s = cs[2 * pr + 1];
-          const float x0 = dka[db][4 * g + 2 * pr] * scale, x1 = dka[db][4 * g + 2 * pr + 1] * scale;
+          const float x0 = dka[dblk][4 * g + 2 * pr] * scale, x1 = dka[dblk][4 * g + 2 * pr + 1] * scale;
           wk[2 * pr] = (bf16)(bad ? NAN : x0 * c + x1 * s);
           wk[2 * pr + 1] = (bf16)(bad ? NAN : x1 * c - x0 * s);
-          wv[2 * pr] = (bf16)(bad ? NAN : dva[db][4 * g + 2 * pr]);
-          wv[2 * pr + 1] = (bf16)(bad ? NAN : dva[db][4 * g + 2 * pr + 1]);
+          wv[2 * pr] = (bf16)(bad ? NAN : dva[dblk][4 * g + 2 * pr]);
+          wv[2 * pr + 1] = (bf16)(bad ? NAN : dva[dblk][4 * g + 2 * pr + 1]);
         }
         *(bf16x4*)(dkp + d0) = wk;
         *(bf16x4*)(dvp + d0) = wv;
@@ -344,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const float* __restrict__ ds0, const float* __restrict__ table,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ lo,
     const int32_t* __restrict__ hi, const int32_t* __restrict__ qptr,
-    const int32_t* __restrict__ kidx, const uint8_t* __restrict__ kkind,
+    const int32_t* __restrict__ kpack,
     const int32_t* __restrict__ status, int S, int Hq, int Hkv, int nq, int n_items, float scale,
     bf16* __restrict__ dq) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
@@ -400,15 +425,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
 
   int e = qptr[tile];
   const int e_end = qptr[tile + 1];
-  if (e < e_end && kkind[e] == kTileAnchor) ++e;
-  if (e < e_end) issue(0, kidx[e]);
+  if (e < e_end && packed_kind(kpack[e]) == kTileAnchor) ++e;
+  int ent = e < e_end ? kpack[e] : 0;
+  if (e < e_end) issue(0, packed_idx(ent));
   int cur = 0;
   while (e < e_end) {
-    const int kt = kidx[e];
-    const bool need_mask = kkind[e] != kTileFull || kt == 0;
+    const int kt = packed_idx(ent);
+    const bool need_mask = packed_kind(ent) != kTileFull || kt == 0;
+    const int ent_next = e + 1 < e_end ? kpack[e + 1] : 0;
     wait_direct_loads();
     __syncthreads();                 // tile e in buffer cur; buffer cur^1 free
-    if (e + 1 < e_end) issue(cur ^ 1, kidx[e + 1]);
+    if (e + 1 < e_end) issue(cur ^ 1, packed_idx(ent_next));
     const bf16* Kc = Ks[cur];
     const bf16* Vc = Vs[cur];
 
@@ -446,6 +473,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
           acc[db] = mfma32(tr_operand<D>(Kc, 32 * kb + 16 * c, 32 * db), dsb[c], acc[db]);
     }
     ++e;
+    ent = ent_next;
     cur ^= 1;
   }
 
@@ -520,12 +548,12 @@ hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st) {
   const dim3 grid(a.B * a.nblk, a.Hq);
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_pre<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.dout,
-                       a.lse, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.dvec, a.ds0, a.part_dk,
-                       a.part_dv);
+                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.dvec, a.ds0,
+                       a.part_dk, a.part_dv, a.qstats);
   else
     hipLaunchKernelGGL(k_bwd_pre<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.dout,
-                       a.lse, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.dvec, a.ds0, a.part_dk,
-                       a.part_dv);
+                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.dvec, a.ds0,
+                       a.part_dk, a.part_dv, a.qstats);
   return hipGetLastError();
 }
 
@@ -533,13 +561,13 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, hipStream_t st)
   const int n_items = a.B * pk.nk * a.Hkv;
   const dim3 grid(padded_grid(n_items));
   if (a.D == 128)
-    hipLaunchKernelGGL(k_bwd_dkdv<128>, grid, dim3(512), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
-                       a.dvec, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pk.kptr, pk.qidx, pk.qkind,
-                       a.status, a.S, a.Hq, a.Hkv, pk.nk, n_items, a.scale, a.dk, a.dv);
+    hipLaunchKernelGGL(k_bwd_dkdv<128>, grid, dim3(512), 0, st, a.qr, a.kr, a.v, a.dout,
+                       a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, a.status, a.S,
+                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.dk, a.dv);
   else
-    hipLaunchKernelGGL(k_bwd_dkdv<64>, grid, dim3(512), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
-                       a.dvec, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pk.kptr, pk.qidx, pk.qkind,
-                       a.status, a.S, a.Hq, a.Hkv, pk.nk, n_items, a.scale, a.dk, a.dv);
+    hipLaunchKernelGGL(k_bwd_dkdv<64>, grid, dim3(512), 0, st, a.qr, a.kr, a.v, a.dout,
+                       a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, a.status, a.S,
+                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.dk, a.dv);
   return hipGetLastError();
 }
 
@@ -548,12 +576,12 @@ hipError_t launch_bwd_dq(const BwdArgs& a, const PlanBufs& pq, hipStream_t st) {
   const dim3 grid(padded_grid(n_items));
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
-                       a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kidx,
-                       pq.kkind, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.dq);
+                       a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
+                       a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.dq);
   else
     hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
-                       a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kidx,
-                       pq.kkind, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.dq);
+                       a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
+                       a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.dq);
   return hipGetLastError();
 }
 

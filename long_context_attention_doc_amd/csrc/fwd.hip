@@ -41,8 +41,8 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void k_fwd(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
-    const int32_t* __restrict__ qptr, const int32_t* __restrict__ kidx,
-    const uint8_t* __restrict__ kkind, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
+    const int32_t* __restrict__ qptr, const int32_t* __restrict__ kpack,
+    const int32_t* __restrict__ status, int S, int Hq, int Hkv,
     int nq, int n_items, float scale_log2, bf16* __restrict__ o, float* __restrict__ lse) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int NKK = D / 16;    // 16-wide reduction steps over d
@@ -113,16 +113,18 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
 
   int e = qptr[tile];
   const int e_end = qptr[tile + 1];
-  if (e < e_end && kkind[e] == kTileAnchor) ++e;   // only key tile 0 can be anchor-only
-  if (e < e_end) issue(0, kidx[e]);
+  if (e < e_end && packed_kind(kpack[e]) == kTileAnchor) ++e;   // only key tile 0 can be anchor-only
+  int ent = e < e_end ? kpack[e] : 0;
+  if (e < e_end) issue(0, packed_idx(ent));
   int cur = 0;
 
   while (e < e_end) {
-    const int kt = kidx[e];
-    const bool need_mask = kkind[e] != kTileFull || kt == 0;
+    const int kt = packed_idx(ent);
+    const bool need_mask = packed_kind(ent) != kTileFull || kt == 0;
+    const int ent_next = e + 1 < e_end ? kpack[e + 1] : 0;
     wait_direct_loads();
     __syncthreads();                 // tile e in buffer cur; buffer cur^1 free
-    if (e + 1 < e_end) issue(cur ^ 1, kidx[e + 1]);
+    if (e + 1 < e_end) issue(cur ^ 1, packed_idx(ent_next));
     const bf16* Kc = Ks[cur];
     const bf16* Vc = Vs[cur];
 
@@ -186,6 +188,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
       for (int c = 0; c < BN / 16; ++c)
         acc[db] = mfma32(tr_operand<D>(Vc, 16 * c, 32 * db), pb[c], acc[db]);
     ++e;
+    ent = ent_next;
     cur ^= 1;
   }
 
@@ -218,10 +221,10 @@ hipError_t launch_fwd(const bf16* qr, const bf16* kr, const bf16* v, TokenTables
   const dim3 grid(padded_grid(n_items));
   if (D == 128) {
     hipLaunchKernelGGL(k_fwd<128>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
-                       pb.kidx, pb.kkind, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, o, lse);
+                       pb.kpack, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, o, lse);
   } else {
     hipLaunchKernelGGL(k_fwd<64>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
-                       pb.kidx, pb.kkind, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, o, lse);
+                       pb.kpack, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, o, lse);
   }
   return hipGetLastError();
 }

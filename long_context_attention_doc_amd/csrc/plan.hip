@@ -110,17 +110,6 @@ __global__ void k_tile_kinds(const int32_t* __restrict__ lo, const int32_t* __re
   }
 }
 
-// One thread per (row b, key tile kt): live tiles in the key-major direction.
-__global__ void k_count_keymajor(const uint8_t* __restrict__ kinds, int B, int nq, int nk,
-                                 int32_t* __restrict__ cntk) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= B * nk) return;
-  const int b = i / nk, kt = i % nk;
-  int c = 0;
-  for (int qt = 0; qt < nq; ++qt) c += kinds[((size_t)b * nq + qt) * nk + kt] != 0;
-  cntk[i] = c;
-}
-
 // Single-workgroup exclusive scan: ptr[i] = sum(cnt[0..i)), ptr[n] = total.
 __global__ void k_scan(const int32_t* __restrict__ cnt, int n, int32_t* __restrict__ ptr,
                        int32_t* __restrict__ total_out) {
@@ -150,39 +139,61 @@ __global__ void k_scan(const int32_t* __restrict__ cnt, int n, int32_t* __restri
   }
 }
 
-// Query-major fill: one thread per (b, qt) walks its key tiles ascending.
-__global__ void k_fill_querymajor(const uint8_t* __restrict__ kinds, int B, int nq, int nk,
-                                  const int32_t* __restrict__ qptr, int32_t* __restrict__ kidx,
-                                  uint8_t* __restrict__ kkind) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= B * nq) return;
-  int w = qptr[i];
-  const uint8_t* row = kinds + (size_t)i * nk;
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t k = row[kt];
-    if (k) {
-      kidx[w] = kt;
-      kkind[w] = k;
-      ++w;
-    }
+// Transposed copy of the kind matrix: kinds_t[b][kt][qt] = kinds[b][qt][kt],
+// 64 x 64 blocks through LDS.
+__global__ void k_transpose_kinds(const uint8_t* __restrict__ kinds, int nq, int nk,
+                                  uint8_t* __restrict__ kinds_t) {
+  __shared__ uint8_t blk[64][65];
+  const int b = blockIdx.z;
+  const int q0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
+  const uint8_t* src = kinds + (size_t)b * nq * nk;
+  uint8_t* dst = kinds_t + (size_t)b * nq * nk;
+  for (int i = threadIdx.y; i < 64; i += blockDim.y) {
+    const int q = q0 + i, k = k0 + threadIdx.x;
+    blk[i][threadIdx.x] = (q < nq && k < nk) ? src[(size_t)q * nk + k] : 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.y; i < 64; i += blockDim.y) {
+    const int k = k0 + i, q = q0 + threadIdx.x;
+    if (k < nk && q < nq) dst[(size_t)k * nq + q] = blk[threadIdx.x][i];
   }
 }
 
-// Key-major fill: one thread per (b, kt) walks its query tiles ascending.
-__global__ void k_fill_keymajor(const uint8_t* __restrict__ kinds, int B, int nq, int nk,
-                                const int32_t* __restrict__ kptr, int32_t* __restrict__ qidx,
-                                uint8_t* __restrict__ qkind) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= B * nk) return;
-  const int b = i / nk, kt = i % nk;
-  int w = kptr[i];
-  for (int qt = 0; qt < nq; ++qt) {
-    const uint8_t k = kinds[((size_t)b * nq + qt) * nk + kt];
+// One wave per row of a dense [rows][n] kind matrix: number of live entries.
+__global__ void k_row_count(const uint8_t* __restrict__ m, int rows, int n,
+                            int32_t* __restrict__ cnt) {
+  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const uint8_t* r = m + (size_t)row * n;
+  int c = 0;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    c += __popcll(__builtin_amdgcn_ballot_w64(i < n && r[i] != 0));
+  }
+  if (lane == 0) cnt[row] = c;
+}
+
+// One wave per row: the live entries of the row, ascending, at ptr[row].
+__global__ void k_row_compact(const uint8_t* __restrict__ m, int rows, int n,
+                              const int32_t* __restrict__ ptr, int32_t* __restrict__ idx,
+                              uint8_t* __restrict__ kind, int32_t* __restrict__ pack) {
+  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const uint8_t* r = m + (size_t)row * n;
+  int w = ptr[row];
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const uint8_t k = i < n ? r[i] : 0;
+    const unsigned long long live = __builtin_amdgcn_ballot_w64(k != 0);
     if (k) {
-      qidx[w] = qt;
-      qkind[w] = k;
-      ++w;
+      const int before = __popcll(live & ((1ull << lane) - 1ull));
+      idx[w + before] = i;
+      kind[w + before] = k;
+      if (pack) pack[w + before] = pack_tile(i, k);
     }
+    w += __popcll(live);
   }
 }
 
@@ -203,15 +214,17 @@ hipError_t launch_plan(const int32_t* lo, const int32_t* hi, int B, int S, PlanB
   hipLaunchKernelGGL(k_tile_kinds, dim3(B * nq), dim3(256), 0, st, lo, hi, S, pb.BM, pb.BN, nq,
                      nk, pb.kinds, pb.cntq);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pb.cntq, B * nq, pb.qptr, pb.n_live);
-  hipLaunchKernelGGL(k_fill_querymajor, dim3((B * nq + 127) / 128), dim3(128), 0, st, pb.kinds,
-                     B, nq, nk, pb.qptr, pb.kidx, pb.kkind);
+  hipLaunchKernelGGL(k_row_compact, dim3((B * nq + 3) / 4), dim3(256), 0, st, pb.kinds, B * nq, nk,
+                     pb.qptr, pb.kidx, pb.kkind, pb.kpack);
   if (key_major) {
-    hipLaunchKernelGGL(k_count_keymajor, dim3((B * nk + 127) / 128), dim3(128), 0, st, pb.kinds,
-                       B, nq, nk, pb.cntk);
+    hipLaunchKernelGGL(k_transpose_kinds, dim3((nk + 63) / 64, (nq + 63) / 64, B), dim3(64, 4), 0,
+                       st, pb.kinds, nq, nk, pb.kinds_t);
+    hipLaunchKernelGGL(k_row_count, dim3((B * nk + 3) / 4), dim3(256), 0, st, pb.kinds_t, B * nk,
+                       nq, pb.cntk);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pb.cntk, B * nk, pb.kptr,
                        (int32_t*)nullptr);
-    hipLaunchKernelGGL(k_fill_keymajor, dim3((B * nk + 127) / 128), dim3(128), 0, st, pb.kinds,
-                       B, nq, nk, pb.kptr, pb.qidx, pb.qkind);
+    hipLaunchKernelGGL(k_row_compact, dim3((B * nk + 3) / 4), dim3(256), 0, st, pb.kinds_t, B * nk,
+                       nq, pb.kptr, pb.qidx, pb.qkind, pb.qpack);
   }
   return hipGetLastError();
 }
