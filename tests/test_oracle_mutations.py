@@ -1,0 +1,46 @@
+"""Planted mistakes in a copy of the oracle must each fail some pin.
+
+Each case rewrites one line of a private copy of the oracle (on the CPU, in a
+temporary directory) and runs the pin tests against that copy in a
+subprocess; the pins pass only for the unmodified oracle.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = [
+    ("sin sign in the rotation", "out[..., 0::2] = x0 * c - x1 * s", "out[..., 0::2] = x0 * c + x1 * s"),
+    ("theta exponent", "return np.power(float(base), -2.0 * p / D)", "return np.power(float(base), -1.0 * p / D)"),
+    ("dropped Dv term", "ds = p * (dp - dv_i[:, None])", "ds = p * dp"),
+    ("reset starts at 0", "pos = t - cu[seg] + 1", "pos = t - cu[seg]"),
+    ("strict causality", "same_doc &= cols[None, :] <= rows[:, None]", "same_doc &= cols[None, :] < rows[:, None]"),
+    ("GQA head mapping", "g = h * Hkv // Hq", "g = h % Hkv"),
+    ("dK not un-rotated", "dk[:, gi, :] = rope(dk_rot[:, gi, :], pos[k_cols], rope_base, inverse=True)",
+     "dk[:, gi, :] = rope(dk_rot[:, gi, :], pos[k_cols], rope_base)"),
+    ("anchor column dropped", "return same_batch_row & (sees_anchor | same_doc)", "return same_batch_row & same_doc"),
+    ("anchor kind on any key tile", "    if kt == 0 and not m[:, 1:].any():", "    if not m[:, 1:].any():"),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = os.path.join(ROOT, "oracle")
+    dst = tmp_path / "oracle"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("__pycache__"))
+    f = dst / "anchor_oracle.py"
+    text = f.read_text()
+    assert text.count(old) >= 1, f"mutation site not found: {old}"
+    f.write_text(text.replace(old, new))
+    env = dict(os.environ)
+    env["PYTHONPATH"] = str(tmp_path) + os.pathsep + ROOT
+    res = subprocess.run(
+        [sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle_pins.py"), "-x", "-q",
+         "-p", "no:cacheprovider", "-m", "not gpu"],
+        cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=600)
+    assert res.returncode != 0, f"mutant '{name}' survived the pins:\n{res.stdout[-2000:]}"
