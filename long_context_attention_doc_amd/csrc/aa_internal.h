@@ -196,16 +196,66 @@ __device__ __forceinline__ void tile_load_direct(bf16* lds_tile, const bf16* gba
   }
 }
 
+// The same copy with the per-lane part of the addresses computed once:
+// DirectTile<D, ROWS, NTHREADS>::init() precomputes each lane's element
+// offsets (row * row_stride + chunk * 8) inside a tile; load() adds the
+// tile's first row (a wave-uniform base) and only re-derives clamped offsets
+// for a tile that runs past row_max.
+template <int D, int ROWS, int NTHREADS>
+struct DirectTile {
+  static constexpr int NCH = D / 8;
+  static constexpr int ITERS = ROWS * NCH / NTHREADS;
+  static_assert(ROWS * NCH % NTHREADS == 0, "tile must split evenly over the waves");
+  uint32_t off[ITERS];
+  __device__ __forceinline__ static void locate(int u, int& row, int& chunk) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int pc_idx = (wave * ITERS + u) * 64 + lane;
+    row = pc_idx / NCH;
+    chunk = ((pc_idx % NCH) ^ SwzTile<D>::swz(row)) & (NCH - 1);
+  }
+  __device__ __forceinline__ void init(size_t row_stride) {
+#pragma unroll
+    for (int u = 0; u < ITERS; ++u) {
+      int row, chunk;
+      locate(u, row, chunk);
+      off[u] = (uint32_t)(row * row_stride + chunk * 8);
+    }
+  }
+  __device__ __forceinline__ void load(bf16* lds_tile, const bf16* gbase, size_t row_stride,
+                                       int row0, int row_max) const {
+    const int wave = threadIdx.x >> 6;
+    const bf16* tbase = gbase + (size_t)row0 * row_stride;
+    if (row0 + ROWS - 1 <= row_max) {
+#pragma unroll
+      for (int u = 0; u < ITERS; ++u)
+        __builtin_amdgcn_global_load_lds((const void*)(tbase + off[u]),
+                                         (lds_void*)(lds_tile + (wave * ITERS + u) * 64 * 8), 16, 0,
+                                         0);
+    } else {
+#pragma unroll
+      for (int u = 0; u < ITERS; ++u) {
+        int row, chunk;
+        locate(u, row, chunk);
+        const int r = min(row0 + row, row_max) - row0;
+        __builtin_amdgcn_global_load_lds((const void*)(tbase + (size_t)r * row_stride + chunk * 8),
+                                         (lds_void*)(lds_tile + (wave * ITERS + u) * 64 * 8), 16, 0,
+                                         0);
+      }
+    }
+  }
+};
+
 // Wait until this wave's direct-to-LDS loads (and other vector memory loads)
 // have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Wait until at most N of this wave's vector memory loads are outstanding
-// (s_waitcnt vmcnt(N), N < 16): the loads issued before the last N are done.
+// (s_waitcnt vmcnt(N), N < 64; the count's high bits live in bits 15:14):
+// every load issued before the last N is done.
 template <int N>
 __device__ __forceinline__ void wait_loads_but() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // ---------------------------------------------------------------- XCD-aware order
@@ -228,8 +278,25 @@ __host__ __device__ inline int pack_tile(int idx, int kind) { return idx | (kind
 __device__ __forceinline__ int packed_idx(int v) { return v & 0xffffff; }
 __device__ __forceinline__ int packed_kind(int v) { return (unsigned)v >> 24; }
 
+// Wait until at most `tiles` groups of PER vector-memory instructions issued
+// after the one waited for are still outstanding (tiles <= 3).
+template <int PER>
+__device__ __forceinline__ void wait_all_but_tiles(int tiles) {
+  if (tiles <= 0) wait_direct_loads();
+  else if (tiles == 1) wait_loads_but<PER>();
+  else if (tiles == 2) wait_loads_but<(2 * PER < 63 ? 2 * PER : 63)>();
+  else wait_loads_but<(3 * PER < 63 ? 3 * PER : 63)>();
+}
+
 // Tile shapes of the attention kernels.
-constexpr int kFwdBM = 128, kFwdBN = 64;     // forward and dQ: query tile x key tile
-constexpr int kDkvBM = 64, kDkvBN = 128;     // dK/dV: query tile x key tile
+#ifndef AA_FWD_BN
+#define AA_FWD_BN 64
+#endif
+#ifndef AA_FWD_STAGES
+#define AA_FWD_STAGES 2
+#endif
+constexpr int kFwdBM = 128, kFwdBN = AA_FWD_BN;   // forward and dQ: query tile x key tile
+constexpr int kFwdStages = AA_FWD_STAGES;         // K/V tiles in LDS (prefetch depth + 1)
+constexpr int kDkvBM = 64, kDkvBN = 128;          // dK/dV: query tile x key tile
 
 }  // namespace aa

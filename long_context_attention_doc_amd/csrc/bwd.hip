@@ -22,6 +22,8 @@
 // A float32 atomic accumulation of dq across key tiles would move about
 // 34 GB at 64K tokens x 32 heads and is limited by the L2 atomic rate, so dq
 // is recomputed query-major instead (deterministic, no dq scratch).
+#include <type_traits>
+
 #include "aa_internal.h"
 
 namespace aa {
@@ -359,8 +361,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
 // ---------------------------------------------------------------------------
 // dq: one workgroup (4 waves) per (row b, query head, query tile of 128);
 // each wave owns 32 queries, as in the forward kernel.  K and V tiles go
-// straight into double-buffered swizzled LDS: row reads feed S^T = K Q^T and
-// dP^T = V dO^T, transposing reads feed K^T in dQ^T = K^T dS^T.
+// straight into a ring of swizzled LDS buffers: row reads feed S^T = K Q^T
+// and dP^T = V dO^T, transposing reads feed K^T in dQ^T = K^T dS^T.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(
@@ -377,8 +379,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   constexpr int NDB = D / 32;
   constexpr int NKB = BN / 32;
   using T = SwzTile<D>;
-  __shared__ __align__(16) bf16 Ks[2][BN * D];
-  __shared__ __align__(16) bf16 Vs[2][BN * D];
+  constexpr int NBUF = kFwdStages;
+  constexpr int LPT = 2 * (BN * (D / 8) / 256);   // direct-load instructions per wave and tile
+  __shared__ __align__(16) bf16 Ks[NBUF][BN * D];
+  __shared__ __align__(16) bf16 Vs[NBUF][BN * D];
 
   const int item = xcd_work_item(blockIdx.x, n_items);   // (hq, b, qt), qt fastest
   if (item < 0) return;
@@ -415,29 +419,35 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
 
+  static_assert(NBUF == 2, "the unrolled tile loop assumes two buffers");
   const size_t kv_row_stride = (size_t)Hkv * D;
   const bf16* kbase = kr + tok0 * kv_row_stride + hkv * D;
   const bf16* vbase = v + tok0 * kv_row_stride + hkv * D;
+  DirectTile<D, BN, 256> dl;
+  dl.init(kv_row_stride);
   auto issue = [&](int buf, int kt) {
-    tile_load_direct<D, BN, 256>(Ks[buf], kbase, kv_row_stride, kt * BN, S - 1);
-    tile_load_direct<D, BN, 256>(Vs[buf], vbase, kv_row_stride, kt * BN, S - 1);
+    dl.load(Ks[buf], kbase, kv_row_stride, kt * BN, S - 1);
+    dl.load(Vs[buf], vbase, kv_row_stride, kt * BN, S - 1);
   };
 
-  int e = qptr[tile];
+  int e_first = qptr[tile];
   const int e_end = qptr[tile + 1];
-  if (e < e_end && packed_kind(kpack[e]) == kTileAnchor) ++e;
-  int ent = e < e_end ? kpack[e] : 0;
-  if (e < e_end) issue(0, packed_idx(ent));
-  int cur = 0;
-  while (e < e_end) {
+  if (e_first < e_end && packed_kind(kpack[e_first]) == kTileAnchor) ++e_first;
+  const int n_tiles = e_end - e_first;
+  if (n_tiles > 0) issue(0, packed_idx(kpack[e_first]));
+  // tile loop unrolled by two: every LDS address of a buffer is base + constant
+  auto step = [&](auto bufc, int i) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int ent = kpack[e_first + i];
     const int kt = packed_idx(ent);
     const bool need_mask = packed_kind(ent) != kTileFull || kt == 0;
-    const int ent_next = e + 1 < e_end ? kpack[e + 1] : 0;
+    const bool more = i + 1 < n_tiles;
+    const int ent_next = more ? kpack[e_first + i + 1] : 0;
     wait_direct_loads();
-    __syncthreads();                 // tile e in buffer cur; buffer cur^1 free
-    if (e + 1 < e_end) issue(cur ^ 1, packed_idx(ent_next));
-    const bf16* Kc = Ks[cur];
-    const bf16* Vc = Vs[cur];
+    __syncthreads();                 // tile i visible; the other buffer is free
+    if (more) issue(BUF ^ 1, packed_idx(ent_next));
+    const bf16* Kc = Ks[BUF];
+    const bf16* Vc = Vs[BUF];
 
     // One 32-key block at a time: S^T = K Q^T, dP^T = V dO^T (rows = keys,
     // columns = this wave's queries), dS^T, then dQ^T += K^T dS^T.
@@ -472,9 +482,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
         for (int c = 0; c < 2; ++c)
           acc[db] = mfma32(tr_operand<D>(Kc, 32 * kb + 16 * c, 32 * db), dsb[c], acc[db]);
     }
-    ++e;
-    ent = ent_next;
-    cur ^= 1;
+  };
+  for (int i = 0; i < n_tiles; i += 2) {
+    step(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < n_tiles) step(std::integral_constant<int, 1>{}, i + 1);
   }
 
   // Epilogue: dq' = scale (acc + dS_i0 k'_0); dq = R(pos_i)^T dq'.

@@ -17,11 +17,11 @@
 // are then per lane, and the two lanes holding the same query (lane l and
 // l + 32) combine with one v_permlane32_swap.
 //   * Q^T (B operand) stays in registers for the whole key loop.
-//   * K and V tiles go straight from global memory into double-buffered LDS
-//     (global_load_lds) in a row-major layout with an XOR swizzle; K is read
-//     row-wise (A operand of S^T), V with transposing LDS reads (A operand
-//     V^T of O^T = V^T P^T).  The next tile's loads are in flight while the
-//     current tile is computed.
+//   * K and V tiles go straight from global memory into a ring of LDS
+//     buffers (global_load_lds) in a row-major layout with an XOR swizzle; K
+//     is read row-wise (A operand of S^T), V with transposing LDS reads
+//     (A operand V^T of O^T = V^T P^T).  Up to kFwdStages-1 tiles are in
+//     flight while the current tile is computed.
 //   * P^T goes from the score accumulators straight into the B operand of
 //     the second product; the transposed V^T reads deliver keys in the
 //     accumulator's row order.
@@ -33,6 +33,8 @@
 //     exactly 1 before bf16 rounding), but the O rescale is skipped, wave by
 //     wave, on tiles where no query's maximum grew; on long documents that
 //     is most tiles.
+#include <type_traits>
+
 #include "aa_internal.h"
 
 namespace aa {
@@ -49,8 +51,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   constexpr int NDB = D / 32;    // 32-row blocks of d in O^T
   constexpr int NKB = BN / 32;   // 32-key blocks of a key tile
   using T = SwzTile<D>;
-  __shared__ __align__(16) bf16 Ks[2][BN * D];
-  __shared__ __align__(16) bf16 Vs[2][BN * D];
+  constexpr int NBUF = kFwdStages;
+  constexpr int LPT = 2 * (BN * (D / 8) / 256);   // direct-load instructions per wave and tile
+  __shared__ __align__(16) bf16 Ks[NBUF][BN * D];
+  __shared__ __align__(16) bf16 Vs[NBUF][BN * D];
 
   const int item = xcd_work_item(blockIdx.x, n_items);   // (hq, b, qt), qt fastest
   if (item < 0) return;
@@ -102,31 +106,38 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
       }
   }
 
-  // K and V tiles are loaded straight into LDS, double-buffered.
+  // K and V tiles are loaded straight into LDS, two buffers; the tile loop is
+  // unrolled by two so that every LDS address of a buffer is base + constant.
+  static_assert(NBUF == 2, "the unrolled tile loop assumes two buffers");
   const size_t kv_row_stride = (size_t)Hkv * D;
   const bf16* kbase = kr + tok0 * kv_row_stride + hkv * D;
   const bf16* vbase = v + tok0 * kv_row_stride + hkv * D;
+  DirectTile<D, BN, 256> dl;
+  dl.init(kv_row_stride);
   auto issue = [&](int buf, int kt) {
-    tile_load_direct<D, BN, 256>(Ks[buf], kbase, kv_row_stride, kt * BN, S - 1);
-    tile_load_direct<D, BN, 256>(Vs[buf], vbase, kv_row_stride, kt * BN, S - 1);
+    dl.load(Ks[buf], kbase, kv_row_stride, kt * BN, S - 1);
+    dl.load(Vs[buf], vbase, kv_row_stride, kt * BN, S - 1);
   };
 
-  int e = qptr[tile];
+  // Live key tiles e_first .. e_end-1 (only key tile 0 can be anchor-only).
+  int e_first = qptr[tile];
   const int e_end = qptr[tile + 1];
-  if (e < e_end && packed_kind(kpack[e]) == kTileAnchor) ++e;   // only key tile 0 can be anchor-only
-  int ent = e < e_end ? kpack[e] : 0;
-  if (e < e_end) issue(0, packed_idx(ent));
-  int cur = 0;
+  if (e_first < e_end && packed_kind(kpack[e_first]) == kTileAnchor) ++e_first;
+  const int n_tiles = e_end - e_first;
+  if (n_tiles > 0) issue(0, packed_idx(kpack[e_first]));
 
-  while (e < e_end) {
+  auto step = [&](auto bufc, int i) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int ent = kpack[e_first + i];
     const int kt = packed_idx(ent);
     const bool need_mask = packed_kind(ent) != kTileFull || kt == 0;
-    const int ent_next = e + 1 < e_end ? kpack[e + 1] : 0;
+    const bool more = i + 1 < n_tiles;
+    const int ent_next = more ? kpack[e_first + i + 1] : 0;
     wait_direct_loads();
-    __syncthreads();                 // tile e in buffer cur; buffer cur^1 free
-    if (e + 1 < e_end) issue(cur ^ 1, packed_idx(ent_next));
-    const bf16* Kc = Ks[cur];
-    const bf16* Vc = Vs[cur];
+    __syncthreads();                 // tile i visible; the other buffer is free
+    if (more) issue(BUF ^ 1, packed_idx(ent_next));
+    const bf16* Kc = Ks[BUF];
+    const bf16* Vc = Vs[BUF];
 
     // S^T = K Q^T for this wave's 32 queries and the BN keys of the tile.
     f32x16 st[NKB];
@@ -187,9 +198,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
 #pragma unroll
       for (int c = 0; c < BN / 16; ++c)
         acc[db] = mfma32(tr_operand<D>(Vc, 16 * c, 32 * db), pb[c], acc[db]);
-    ++e;
-    ent = ent_next;
-    cur ^= 1;
+  };
+  for (int i = 0; i < n_tiles; i += 2) {
+    step(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < n_tiles) step(std::integral_constant<int, 1>{}, i + 1);
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.
