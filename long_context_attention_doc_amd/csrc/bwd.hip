@@ -126,11 +126,11 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
 // dK^T = Q^T dS over all D features.  The two waves of a key group never
 // talk inside the loop (no exchange, one barrier per tile); their partial
 // key gradients are added through LDS once, at the end.
-//   * V^T (B operand of dP, keys as columns) stays in registers; the
-//     workgroup's 128 K rows sit in swizzled LDS for the whole loop (B operand
-//     of S), which keeps the kernel within 256 registers per lane.
-//   * Q and dO tiles go straight into swizzled LDS (global_load_lds), up to
-//     two tiles ahead; row reads feed S and dP, transposing reads feed Q^T
+//   * The workgroup's 128 K and V rows sit in swizzled LDS for the whole loop
+//     (B operands of S and dP), which keeps the kernel within 256 registers
+//     per lane.
+//   * Q and dO tiles go straight into double-buffered swizzled LDS
+//     (global_load_lds), one tile ahead; row reads feed S and dP, transposing reads feed Q^T
 //     and dO^T.
 //   * P and dS feed the B operand of dV^T = dO^T P and dK^T = Q^T dS straight
 //     from the accumulator layout.
@@ -146,13 +146,13 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
   constexpr int BM = kDkvBM, BN = kDkvBN;    // 64 queries x 128 keys
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;                // 32-feature blocks
-  constexpr int NBUF = 3;                    // tiles in flight: current + 2 prefetched
-  constexpr int LD_ITERS = BM * (D / 8) / 512;   // direct-load instructions per wave and tensor
+  constexpr int NBUF = 2;                    // current tile + 1 prefetched
   using T = SwzTile<D>;
   __shared__ __align__(16) bf16 Qs[NBUF][BM * D];
   __shared__ __align__(16) bf16 Gs[NBUF][BM * D];
   __shared__ __align__(16) float s_st[NBUF][4][BM];  // LSE*log2(e), Dv, lo, hi (int bits)
   __shared__ __align__(16) bf16 Ks[BN * D];          // this workgroup's keys (rotated)
+  __shared__ __align__(16) bf16 Vs[BN * D];          // and values
 
   const int item = xcd_work_item(blockIdx.x, n_items);   // (hkv, b, kt), kt fastest
   if (item < 0) return;
@@ -170,14 +170,12 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
   const bool bad = status[0] != kStatusOk;
   const float scale_log2 = scale * kLog2e;
 
-  // V^T operand: lane holds key `col`, features 16*kk + 8*h + i; K rows in LDS.
-  bf16x8 vf[NKK];
+  // The workgroup's K and V rows live in LDS for the whole loop.
   {
-    const bf16* vp = v + (ktok * Hkv + hkv) * D + 8 * h;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) vf[kk] = *(const bf16x8*)(vp + 16 * kk);
     const size_t kv_row_stride = (size_t)Hkv * D;
     tile_load_direct<D, BN, 512>(Ks, kr + tok0 * kv_row_stride + hkv * D, kv_row_stride, kt * BN,
+                                 S - 1);
+    tile_load_direct<D, BN, 512>(Vs, v + tok0 * kv_row_stride + hkv * D, kv_row_stride, kt * BN,
                                  S - 1);
   }
   f32x16 dka[NDB], dva[NDB];
@@ -200,17 +198,6 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
                                        16, 0, 0);
     }
   };
-  // wait for the current tile while the next one may stay in flight
-  auto wait_current = [&](bool next_in_flight) {
-    if (!next_in_flight) {
-      wait_direct_loads();
-    } else if (wave == 0) {
-      wait_loads_but<2 * LD_ITERS + 1>();
-    } else {
-      wait_loads_but<2 * LD_ITERS>();
-    }
-  };
-
   // Work list: every q head of the group x every live, not anchor-only query tile.
   const int e_begin = kptr[ktile], e_end = kptr[ktile + 1];
   const int h_end = (hkv + 1) * group;
@@ -230,21 +217,16 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
 
   int e, hq;
   first(e, hq);
-  int e1 = e, h1 = hq;
-  if (hq < h_end) {
-    issue(0, hq, packed_idx(qpack[e]));
-    advance(e1, h1);
-    if (h1 < h_end) issue(1, h1, packed_idx(qpack[e1]));
-  }
+  if (hq < h_end) issue(0, hq, packed_idx(qpack[e]));
   int cur = 0;
   while (hq < h_end) {
     const bool need_mask = packed_kind(qpack[e]) != kTileFull || kt == 0;
-    int e2 = e1, h2 = h1;
-    if (h1 < h_end) advance(e2, h2);
-    const int qt2 = h2 < h_end ? packed_idx(qpack[e2]) : 0;
-    wait_current(h1 < h_end);
-    __syncthreads();      // tile in buffer `cur` visible; buffer cur+2 free
-    if (h2 < h_end) issue(cur >= 1 ? cur - 1 : cur + 2, h2, qt2);
+    int e1 = e, h1 = hq;
+    advance(e1, h1);
+    const int qt1 = h1 < h_end ? packed_idx(qpack[e1]) : 0;
+    wait_direct_loads();
+    __syncthreads();      // tile in buffer `cur` visible; the other buffer free
+    if (h1 < h_end) issue(cur ^ 1, h1, qt1);
     const bf16* Qc = Qs[cur];
     const bf16* Gc = Gs[cur];
 
@@ -255,9 +237,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int off = T::chunk_off(32 * p + col, 2 * kk + h);
-      const bf16x8 kb = *(const bf16x8*)(Ks + T::chunk_off(32 * kg + col, 2 * kk + h));
-      sp = mfma32(*(const bf16x8*)(Qc + off), kb, sp);
-      dp = mfma32(*(const bf16x8*)(Gc + off), vf[kk], dp);
+      const int koff = T::chunk_off(32 * kg + col, 2 * kk + h);
+      sp = mfma32(*(const bf16x8*)(Qc + off), *(const bf16x8*)(Ks + koff), sp);
+      dp = mfma32(*(const bf16x8*)(Gc + off), *(const bf16x8*)(Vs + koff), dp);
     }
     // P = exp2(s * scale_log2 - lse_log2), dS = P (dP - Dv).
     bf16x8 pb[2], db_[2];
@@ -293,8 +275,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
         dka[dblk] = mfma32(tr_operand<D>(Qc, 32 * p + 16 * c, 32 * dblk), db_[c], dka[dblk]);
       }
     e = e1; hq = h1;
-    e1 = e2; h1 = h2;
-    cur = cur == NBUF - 1 ? 0 : cur + 1;
+    cur ^= 1;
   }
 
   // Add the two query halves: waves p = 1 hand their partial sums to p = 0
