@@ -161,13 +161,22 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
           st[kb][j] = (off >= a && off <= z) ? st[kb][j] : -INFINITY;
         }
     }
-    // Tile maximum (raw scores; the scale is positive).
-    float mt = -INFINITY;
+    // Tile maximum (raw scores; the scale is positive).  IEEE maximum needs
+    // no input canonicalisation and fuses into three-input maxima.
+    float mk[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      mk[kb] = st[kb][0];
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) mt = fmaxf(mt, fmaxf(st[kb][j], st[kb][j + 1]));
-    mt = fmaxf(mt, partner(mt)) * scale_log2;
+      for (int j = 1; j < 15; j += 2)
+        mk[kb] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mk[kb], st[kb][j]),
+                                               st[kb][j + 1]);
+      mk[kb] = __builtin_elementwise_maximum(mk[kb], st[kb][15]);
+    }
+    float mt = mk[0];
+#pragma unroll
+    for (int kb = 1; kb < NKB; ++kb) mt = __builtin_elementwise_maximum(mt, mk[kb]);
+    mt = __builtin_elementwise_maximum(mt, partner(mt)) * scale_log2;
     const bool raise = mt > m;
     if (__builtin_amdgcn_ballot_w64(raise)) {
       const float m_new = raise ? mt : m;
@@ -181,16 +190,24 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     }
 
     // P^T = exp2(s * scale_log2 - m) as bf16 B operands, one per 16-key step.
+    // The row sum adds the same bf16 weights that multiply V (pairwise dot
+    // products with ones), so numerator and denominator see identical P.
     bf16x8 pb[BN / 16];
     const float nm = -m;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j], scale_log2, nm));
-        l += p;
-        pb[2 * kb + (j >> 3)][j & 7] = (bf16)p;
-      }
+      for (int j = 0; j < 16; ++j)
+        pb[2 * kb + (j >> 3)][j & 7] =
+            (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j], scale_log2, nm));
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+    for (int c = 0; c < BN / 16; ++c) {
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 0, 1), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 2, 3), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 4, 5), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 6, 7), ones, l, false);
+    }
 
     // O^T += V^T P^T.
 #pragma unroll
