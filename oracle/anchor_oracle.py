@@ -27,6 +27,13 @@ Position: BFloat16 Breaks Down RoPE in Long-Context Training"):
   ID 0) attends only to itself; its key is rotated by R_0 = I.
 * arch page §3.4, "Reduction in attention computations": each token attends
   only within its own document plus the anchor.
+* arch page §3.4, "Intra-document attention (Figure 2, left)" and Figure 2,
+  middle: the baselines without an anchor, where a query sees only the causal
+  keys of its own document; position IDs continue across documents (left) or
+  restart at 1 for every document (middle).  ``anchor=False`` computes them.
+* The paper's own reading of AnchorAttention (arch page, "Core design
+  (Figure 2, right)"): continuous document position IDs counting on from 1
+  after the anchor; ``mode="continuous"``.
 
 Readings where the pages are silent (listed with reasons in the design notes):
 position IDs are reset per document (first document token = 1, anchor = 0);
@@ -54,8 +61,10 @@ KIND_ANCHOR = 3    # key tile 0 where the only allowed key is the anchor column
 # ----------------------------------------------------------------------------
 # Segments and position IDs
 # ----------------------------------------------------------------------------
-def validate_cu(cu, B: int, S: int) -> np.ndarray:
-    """Check the packed-segment offsets; raise ValueError on misuse."""
+def validate_cu(cu, B: int, S: int, anchor: bool = True) -> np.ndarray:
+    """Check the packed-segment offsets; raise ValueError on misuse.  Every
+    row starts a segment (segments never cross rows); with an anchor that
+    first segment is the one-token anchor."""
     cu = np.asarray(cu, dtype=np.int64)
     if cu.ndim != 1 or len(cu) < 2:
         raise ValueError("cu_doc_lens must be a 1-D array with at least two entries")
@@ -65,27 +74,31 @@ def validate_cu(cu, B: int, S: int) -> np.ndarray:
         raise ValueError("cu_doc_lens must be strictly increasing (no empty segments)")
     cs = set(int(x) for x in cu)
     for b in range(B):
-        if b * S not in cs or b * S + 1 not in cs:
+        if b * S not in cs:
+            raise ValueError(f"a segment crosses into row {b}")
+        if anchor and b * S + 1 not in cs:
             raise ValueError(f"row {b} must start with a one-token anchor segment")
     return cu
 
 
-def segment_ids(cu, B: int, S: int) -> np.ndarray:
+def segment_ids(cu, B: int, S: int, anchor: bool = True) -> np.ndarray:
     """Index of the segment holding every token of the flattened stream."""
-    cu = validate_cu(cu, B, S)
+    cu = validate_cu(cu, B, S, anchor)
     t = np.arange(B * S, dtype=np.int64)
     return np.searchsorted(cu, t, side="right") - 1
 
 
-def position_ids(cu, B: int, S: int, mode: str = "reset") -> np.ndarray:
-    """Position ID of every token (arch page §3.4, Figure 2 middle and right).
+def position_ids(cu, B: int, S: int, mode: str = "reset", anchor: bool = True) -> np.ndarray:
+    """Position ID of every token (arch page §3.4, Figure 2).
 
     reset:      anchor -> 0; document token t in segment [s, e) -> t - s + 1.
     continuous: anchor -> 0; document tokens count on from 1 across documents,
                 i.e. t - (row start).
+    Without an anchor the row's first token is an ordinary document token:
+    reset gives it 1, continuous gives it 0 (t - row start).
     """
-    cu = validate_cu(cu, B, S)
-    seg = segment_ids(cu, B, S)
+    cu = validate_cu(cu, B, S, anchor)
+    seg = segment_ids(cu, B, S, anchor)
     t = np.arange(B * S, dtype=np.int64)
     row_start = (t // S) * S
     is_anchor = t == row_start
@@ -95,7 +108,8 @@ def position_ids(cu, B: int, S: int, mode: str = "reset") -> np.ndarray:
         pos = t - row_start
     else:
         raise ValueError(f"unknown position mode {mode!r}")
-    pos = np.where(is_anchor, 0, pos)
+    if anchor:
+        pos = np.where(is_anchor, 0, pos)
     return pos.astype(np.int64)
 
 
@@ -137,14 +151,15 @@ def rope(x: np.ndarray, pos: np.ndarray, base: float, inverse: bool = False) -> 
 # ----------------------------------------------------------------------------
 # The explicit mask
 # ----------------------------------------------------------------------------
-def allowed(cu, B: int, S: int, rows, cols, causal: bool = True) -> np.ndarray:
+def allowed(cu, B: int, S: int, rows, cols, causal: bool = True,
+            anchor: bool = True) -> np.ndarray:
     """Dense boolean mask block allowed[len(rows), len(cols)] (Mask construction).
 
     rows and cols are flattened token indices.  A query may see a key only in
-    its own batch row; there it sees the row's anchor, and keys of its own
-    document that are not in its future.
+    its own batch row; there it sees the row's anchor (unless anchor=False),
+    and keys of its own document that are not in its future.
     """
-    seg = segment_ids(cu, B, S)
+    seg = segment_ids(cu, B, S, anchor)
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
     anchor_of_row = (rows // S) * S
@@ -153,17 +168,20 @@ def allowed(cu, B: int, S: int, rows, cols, causal: bool = True) -> np.ndarray:
     same_doc = seg[rows][:, None] == seg[cols][None, :]
     if causal:
         same_doc &= cols[None, :] <= rows[:, None]
+    if not anchor:
+        return same_batch_row & same_doc
     return same_batch_row & (sees_anchor | same_doc)
 
 
-def unmasked_pairs(cu, B: int, S: int, causal: bool = True, block: int = 1024) -> int:
+def unmasked_pairs(cu, B: int, S: int, causal: bool = True, block: int = 1024,
+                   anchor: bool = True) -> int:
     """Number of allowed (query, key) pairs, counted on the explicit mask."""
     total = 0
     for b in range(B):
         cols = np.arange(b * S, (b + 1) * S)
         for r0 in range(0, S, block):
             rows = np.arange(b * S + r0, b * S + min(S, r0 + block))
-            total += int(allowed(cu, B, S, rows, cols, causal).sum())
+            total += int(allowed(cu, B, S, rows, cols, causal, anchor).sum())
     return total
 
 
@@ -186,7 +204,7 @@ def _blocks_of(rows: np.ndarray, S: int, block: int):
             yield int(b), rb[i:i + block]
 
 
-def _row_block_forward(qh, kr, vv, cu, B, S, rows_b, b, pos, base, scale, causal):
+def _row_block_forward(qh, kr, vv, cu, B, S, rows_b, b, pos, base, scale, causal, anchor=True):
     """Logits, probabilities, output and log-sum-exp for a block of query rows."""
     qr = rope(qh[rows_b - b * S], pos[rows_b], base)               # [R, D]
     # Under the causal rule every key after the block's last query is masked
@@ -194,7 +212,7 @@ def _row_block_forward(qh, kr, vv, cu, B, S, rows_b, b, pos, base, scale, causal
     ncols = int(rows_b.max() - b * S + 1) if causal else S
     cols = np.arange(b * S, b * S + ncols)
     s = scale * (qr @ kr[:ncols].T)                                 # [R, ncols]
-    m_allowed = allowed(cu, B, S, rows_b, cols, causal)
+    m_allowed = allowed(cu, B, S, rows_b, cols, causal, anchor)
     s = np.where(m_allowed, s, -np.inf)
     m = s.max(axis=1)
     p = np.exp(s - m[:, None])
@@ -206,10 +224,12 @@ def _row_block_forward(qh, kr, vv, cu, B, S, rows_b, b, pos, base, scale, causal
 
 
 def forward(q, k, v, cu, rope_base: float, causal: bool = True, scale: float | None = None,
-            heads=None, rows=None, block: int = 512, pos_mode: str = "reset", pos=None):
+            heads=None, rows=None, block: int = 512, pos_mode: str = "reset", pos=None,
+            anchor: bool = True):
     """O and LSE (float64) for the chosen q heads and flattened query rows.
 
-    ``pos`` optionally overrides the position IDs (one per flattened token).
+    ``pos`` optionally overrides the position IDs (one per flattened token);
+    ``anchor=False`` computes the intra-document baselines without an anchor.
     Returns (o [len(rows), len(heads), D], lse [len(heads), len(rows)], rows, heads).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -218,7 +238,7 @@ def forward(q, k, v, cu, rope_base: float, causal: bool = True, scale: float | N
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
-    pos = position_ids(cu, B, S, pos_mode) if pos is None else np.asarray(pos, dtype=np.int64)
+    pos = position_ids(cu, B, S, pos_mode, anchor) if pos is None else np.asarray(pos, dtype=np.int64)
     heads = list(range(Hq)) if heads is None else list(heads)
     rows = np.arange(B * S) if rows is None else np.unique(np.asarray(rows, dtype=np.int64))
     where = {int(r): n for n, r in enumerate(rows)}
@@ -233,7 +253,7 @@ def forward(q, k, v, cu, rope_base: float, causal: bool = True, scale: float | N
             kr = kr_of[b]
             vv = v[b, :, g, :]
             _, _, _, _, ob, lb = _row_block_forward(q[b, :, h, :], kr, vv, cu, B, S, rb, b, pos,
-                                                     rope_base, scale, causal)
+                                                     rope_base, scale, causal, anchor)
             idx = [where[int(r)] for r in rb]
             o[idx, hi, :] = ob
             lse[hi, idx] = lb
@@ -242,7 +262,7 @@ def forward(q, k, v, cu, rope_base: float, causal: bool = True, scale: float | N
 
 def backward(q, k, v, do, cu, rope_base: float, causal: bool = True, scale: float | None = None,
              heads=None, q_rows=None, k_cols=None, block: int = 512, pos_mode: str = "reset",
-             pos=None):
+             pos=None, anchor: bool = True):
     """Analytic gradients (float64) of sum(O * dO) with respect to q, k, v.
 
     dV_j = sum_i P_ij dO_i;  dP_ij = dO_i . v_j;  Dv_i = dO_i . O_i;
@@ -257,7 +277,7 @@ def backward(q, k, v, do, cu, rope_base: float, causal: bool = True, scale: floa
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
-    pos = position_ids(cu, B, S, pos_mode) if pos is None else np.asarray(pos, dtype=np.int64)
+    pos = position_ids(cu, B, S, pos_mode, anchor) if pos is None else np.asarray(pos, dtype=np.int64)
     heads = list(range(Hq)) if heads is None else list(heads)
     q_rows = np.arange(B * S) if q_rows is None else np.unique(np.asarray(q_rows, dtype=np.int64))
     k_cols = np.arange(B * S) if k_cols is None else np.unique(np.asarray(k_cols, dtype=np.int64))
@@ -274,7 +294,7 @@ def backward(q, k, v, do, cu, rope_base: float, causal: bool = True, scale: floa
         kc = k_cols[k_cols // S == b]
         for r0 in range(0, S, 2048):
             rr = np.arange(b * S + r0, b * S + min(S, r0 + 2048))
-            hit = allowed(cu, B, S, rr, kc, causal).any(axis=1)
+            hit = allowed(cu, B, S, rr, kc, causal, anchor).any(axis=1)
             need.update(int(x) for x in rr[hit])
     need_rows = np.array(sorted(need), dtype=np.int64)
 
@@ -287,7 +307,7 @@ def backward(q, k, v, do, cu, rope_base: float, causal: bool = True, scale: floa
             kr = kr_of[b]
             vv = v[b, :, g, :]
             qr, cols, m_allowed, p, o, _ = _row_block_forward(q[b, :, h, :], kr, vv, cu, B, S, rb, b,
-                                                               pos, rope_base, scale, causal)
+                                                               pos, rope_base, scale, causal, anchor)
             dob = do[b, rb - b * S, h, :]                                # [R, D]
             dv_i = np.sum(dob * o, axis=1)                              # Dv
             dp = dob @ vv[:len(cols)].T
@@ -317,46 +337,46 @@ def rotated_bf16_reference(x, pos, base: float) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # Block-sparse tile plan, by brute force over the explicit mask
 # ----------------------------------------------------------------------------
-def _classify(m: np.ndarray, e: np.ndarray, kt: int) -> int:
+def _classify(m: np.ndarray, e: np.ndarray, kt: int, anchor: bool = True) -> int:
     """Kind of one tile from its allowed / exists element masks [BM, BN]."""
     if not m.any():
         return KIND_NONE
     if e.all() and m.all():
         return KIND_FULL
-    if kt == 0 and not m[:, 1:].any():
+    if anchor and kt == 0 and not m[:, 1:].any():
         return KIND_ANCHOR
     return KIND_PARTIAL
 
 
 def tile_kinds_row(cu, B: int, S: int, BM: int, BN: int, b: int, qt: int,
-                   causal: bool = True) -> np.ndarray:
+                   causal: bool = True, anchor: bool = True) -> np.ndarray:
     """Kinds of every key tile for query tile qt of row b, from the dense mask."""
     nk = -(-S // BN)
     rows = np.arange(b * S + qt * BM, b * S + min(S, (qt + 1) * BM))
     cols = np.arange(b * S, (b + 1) * S)
     m = np.zeros((BM, nk * BN), dtype=bool)
     e = np.zeros((BM, nk * BN), dtype=bool)
-    m[:len(rows), :S] = allowed(cu, B, S, rows, cols, causal)
+    m[:len(rows), :S] = allowed(cu, B, S, rows, cols, causal, anchor)
     e[:len(rows), :S] = True
-    return np.array([_classify(m[:, kt * BN:(kt + 1) * BN], e[:, kt * BN:(kt + 1) * BN], kt)
+    return np.array([_classify(m[:, kt * BN:(kt + 1) * BN], e[:, kt * BN:(kt + 1) * BN], kt, anchor)
                      for kt in range(nk)], dtype=np.uint8)
 
 
 def tile_kinds_col(cu, B: int, S: int, BM: int, BN: int, b: int, kt: int,
-                   causal: bool = True) -> np.ndarray:
+                   causal: bool = True, anchor: bool = True) -> np.ndarray:
     """Kinds of every query tile for key tile kt of row b, from the dense mask."""
     nq = -(-S // BM)
     cols = np.arange(b * S + kt * BN, b * S + min(S, (kt + 1) * BN))
     rows = np.arange(b * S, (b + 1) * S)
     m = np.zeros((nq * BM, BN), dtype=bool)
     e = np.zeros((nq * BM, BN), dtype=bool)
-    m[:S, :len(cols)] = allowed(cu, B, S, rows, cols, causal)
+    m[:S, :len(cols)] = allowed(cu, B, S, rows, cols, causal, anchor)
     e[:S, :len(cols)] = True
-    return np.array([_classify(m[qt * BM:(qt + 1) * BM], e[qt * BM:(qt + 1) * BM], kt)
+    return np.array([_classify(m[qt * BM:(qt + 1) * BM], e[qt * BM:(qt + 1) * BM], kt, anchor)
                      for qt in range(nq)], dtype=np.uint8)
 
 
-def tile_plan(cu, B: int, S: int, BM: int, BN: int, causal: bool = True):
+def tile_plan(cu, B: int, S: int, BM: int, BN: int, causal: bool = True, anchor: bool = True):
     """Live (query-tile, key-tile) pairs and their kinds, from the dense mask.
 
     A tile is live when it holds at least one allowed element.  FULL: all
@@ -371,7 +391,7 @@ def tile_plan(cu, B: int, S: int, BM: int, BN: int, causal: bool = True):
     kinds = np.zeros((B, nq, nk), dtype=np.uint8)
     for b in range(B):
         for qt in range(nq):
-            kinds[b, qt] = tile_kinds_row(cu, B, S, BM, BN, b, qt, causal)
+            kinds[b, qt] = tile_kinds_row(cu, B, S, BM, BN, b, qt, causal, anchor)
     qptr = [0]
     kidx, kkind = [], []
     for b in range(B):

@@ -23,8 +23,17 @@ MUTANTS = [
     ("dK not un-rotated", "dk[:, gi, :] = rope(dk_rot[:, gi, :], pos[k_cols], rope_base, inverse=True)",
      "dk[:, gi, :] = rope(dk_rot[:, gi, :], pos[k_cols], rope_base)"),
     ("anchor column dropped", "return same_batch_row & (sees_anchor | same_doc)", "return same_batch_row & same_doc"),
-    ("anchor kind on any key tile", "    if kt == 0 and not m[:, 1:].any():", "    if not m[:, 1:].any():"),
+    ("anchor kind on any key tile", "    if anchor and kt == 0 and not m[:, 1:].any():",
+     "    if anchor and not m[:, 1:].any():"),
+    ("anchor kind without an anchor", "    if anchor and kt == 0 and not m[:, 1:].any():",
+     "    if kt == 0 and not m[:, 1:].any():"),
+    ("no-anchor mask keeps the anchor column", "    if not anchor:\n        return same_batch_row & same_doc",
+     "    if False:\n        return same_batch_row & same_doc"),
+    ("no-anchor first token at position 0", "    if anchor:\n        pos = np.where(is_anchor, 0, pos)",
+     "    if True:\n        pos = np.where(is_anchor, 0, pos)"),
+    ("continuous positions off by one", "        pos = t - row_start\n", "        pos = t - row_start + 1\n"),
 ]
+PIN_FILES = ("test_oracle_pins.py", "test_oracle_modes.py")
 
 
 @pytest.mark.slow
@@ -40,7 +49,7 @@ def test_mutant_is_caught(tmp_path, name, old, new):
     env = dict(os.environ)
     env["PYTHONPATH"] = str(tmp_path) + os.pathsep + ROOT
     res = subprocess.run(
-        [sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle_pins.py"), "-x", "-q",
+        [sys.executable, "-m", "pytest", *[os.path.join(ROOT, "tests", f) for f in PIN_FILES], "-x", "-q",
          "-p", "no:cacheprovider", "-m", "not gpu"],
         cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=600)
     assert res.returncode != 0, f"mutant '{name}' survived the pins:\n{res.stdout[-2000:]}"

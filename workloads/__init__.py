@@ -28,7 +28,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "sample_doc_lengths", "cu_doc_lens_from_lengths",
+    "Workload", "WORKLOADS", "sample_doc_lengths", "cu_doc_lens_from_lengths", "cu_doc_lens_no_anchor",
     "make_tensors", "random_partition", "get",
 ]
 
@@ -59,6 +59,18 @@ def cu_doc_lens_from_lengths(rows: list[list[int]], S: int) -> np.ndarray:
         if sum(lens) != S - 1:
             raise ValueError(f"row {b}: document lengths sum to {sum(lens)}, expected {S - 1}")
         cu.append(cu[-1] + 1)
+        for L in lens:
+            cu.append(cu[-1] + L)
+    return np.asarray(cu, dtype=np.int32)
+
+
+def cu_doc_lens_no_anchor(rows: list[list[int]], S: int) -> np.ndarray:
+    """Segment offsets for rows without an anchor: the documents of each row
+    cover it from its first token on, so their lengths add up to S."""
+    cu = [0]
+    for b, lens in enumerate(rows):
+        if sum(lens) != S:
+            raise ValueError(f"row {b}: document lengths sum to {sum(lens)}, expected {S}")
         for L in lens:
             cu.append(cu[-1] + L)
     return np.asarray(cu, dtype=np.int32)
