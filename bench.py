@@ -97,6 +97,26 @@ def cpu_baseline(w, q, k, v, do, budget_s: float) -> dict:
     }
 
 
+def device_peak() -> dict | None:
+    """Dense bf16 MFMA peak re-derived on this machine: compute units x max
+    engine clock (rocminfo) x 4096 flop/clk/CU (gfx950, 32x32x16 bf16)."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except Exception:   # rocminfo missing or hung: report nothing
+        return None
+    for agent in txt.split("Agent ")[1:]:
+        if "gfx950" not in agent:
+            continue
+        cu = re.search(r"Compute Unit:\s*(\d+)", agent)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s*(\d+)", agent)
+        if cu and mhz:
+            cus, clk = int(cu.group(1)), int(mhz.group(1))
+            return {"compute_units": cus, "max_sclk_mhz": clk,
+                    "bf16_dense_peak_tflops": cus * clk * 1e6 * 4096 / 1e12}
+    return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,7 +134,7 @@ def main() -> int:
     import torch
     import workloads
     from long_context_attention_doc_amd import api
-    from long_context_attention_doc_amd.accounting import flops_fwd_bwd
+    from long_context_attention_doc_amd.accounting import algorithmic_bytes, flops_fwd_bwd
 
     w = workloads.get(args.workload)
     dev = torch.device("cuda:0")
@@ -124,10 +144,19 @@ def main() -> int:
     ws_f = torch.empty(api.workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, False), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(api.workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, True), dtype=torch.uint8, device=dev)
 
-    def step():
+    # Events between the forward and the backward call of every step split
+    # the step time; they are on the same stream as the calls.
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+
+    def step(mark=None):
         o, lse = api.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base, True, None, ws_f)
+        if mark is not None:
+            mark[0].record()
         if w.backward:
             api.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base, True, None, ws_b)
+        if mark is not None:
+            mark[1].record()
 
     for _ in range(args.warmup):
         step()
@@ -135,20 +164,21 @@ def main() -> int:
     api.profile_begin(64 * max(1, args.steps))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(marks[i])
     e1.record()
     torch.cuda.synchronize()
     prof = api.profile_end()
     ms = e0.elapsed_time(e1) / args.steps
+    bwd_ms = sum(a.elapsed_time(b) for a, b in marks) / args.steps
+    fwd_ms = ms - bwd_ms
 
     fl = flops_fwd_bwd(w.doc_rows, w.Hq, w.D)
     total_flops = fl["total"] if w.backward else fl["fwd"]
     tflops = total_flops / (ms * 1e-3) / 1e12
     tokens = w.B * w.S
     per_kernel_ms = {k_: v_[0] / max(1, args.steps) for k_, v_ in prof.items()}
-    fwd_ms = sum(per_kernel_ms[k_] for k_ in ("status", "positions", "plan", "rope_table", "rope", "fwd")) \
-        if not w.backward else None
+    nbytes = algorithmic_bytes(w.B, w.S, w.Hq, w.Hkv, w.D, w.backward)
 
     # dominant kernel and its roofline
     cand = [k_ for k_ in KERNEL_FLOPS_PER_PAIR_D if prof[k_][1] > 0]
@@ -172,13 +202,21 @@ def main() -> int:
                    "backward": w.backward, "unmasked_pairs_per_head": fl["pairs_per_head"]},
         "tokens_per_s": tokens / (ms * 1e-3),
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms if w.backward else None,
+        "tflops_no_recompute": ((fl["total_no_recompute"] if w.backward else fl["fwd"])
+                                / (ms * 1e-3) / 1e12),
+        "algorithmic_hbm_bytes": nbytes["total"],
+        "algorithmic_hbm_gbs": nbytes["total"] / (ms * 1e-3) / 1e9,
+        "pct_of_hbm_peak": 100.0 * nbytes["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "device": device_peak(),
         "kernel_ms_per_step": {k_: round(v_, 4) for k_, v_ in per_kernel_ms.items()},
         "roofline": roofline,
     }
-    if fwd_ms is not None:
-        out["fwd_ms"] = fwd_ms
     if args.cpu_budget > 0:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, args.cpu_budget)
+        cb = cpu_baseline(w, q, k, v, do, args.cpu_budget)
+        # the whole workload at the oracle's measured rate
+        cb["full_workload_estimate_s"] = total_flops / (cb["value"] * 1e12)
+        out["cpu_baseline"] = cb
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

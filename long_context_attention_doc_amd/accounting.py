@@ -28,4 +28,20 @@ def flops_fwd_bwd(doc_rows, Hq: int, D: int, causal: bool = True) -> dict:
         "fwd": 4.0 * D * Hq * pairs,
         "bwd": 10.0 * D * Hq * pairs,
         "total": 14.0 * D * Hq * pairs,
+        # without recomputing the scores in the backward: 4*D + 8*D
+        "total_no_recompute": 12.0 * D * Hq * pairs,
     }
+
+
+def algorithmic_bytes(B: int, S: int, Hq: int, Hkv: int, D: int, backward: bool = True) -> dict:
+    """Minimum HBM traffic of one forward (+ backward) call: every operand
+    read once and every result written once, in the library's dtypes (bf16
+    tensors, float32 LSE).  Each call also rotates Q and K once (read the
+    inputs, write the rotated copies)."""
+    xq = 2 * B * S * Hq * D          # one [B,S,Hq,D] bf16 tensor
+    xk = 2 * B * S * Hkv * D
+    lse = 4 * B * Hq * S
+    rope = 2 * (xq + xk)
+    fwd = (xq + 2 * xk) + xq + lse + rope                       # Q K V in, O LSE out
+    bwd = (xq + 2 * xk + xq + xq + lse) + (xq + 2 * xk) + rope  # Q K V O dO LSE in, dQ dK dV out
+    return {"fwd": fwd, "bwd": bwd if backward else 0, "total": fwd + (bwd if backward else 0)}

@@ -13,8 +13,9 @@
 // Four kernels, all without atomics:
 //   pre    per query row: Dv_i, and the anchor column's P_i0 and dS_i0; per
 //          block of 64 rows, partial sums of dS_i0 q'_i and P_i0 dO_i;
-//   dkdv   per (row b, kv head, key tile of 128): K and V stay in registers,
-//          the live query tiles of the key-major plan stream through LDS;
+//   dkdv   per (row b, kv head, key tile of 128): K in LDS and V in
+//          registers for the whole kernel, the live query tiles of the
+//          key-major plan stream through LDS;
 //   dq     per (row b, query head, query tile of 128): the structure of the
 //          forward kernel, recomputing S and dP from LSE; adds the anchor
 //          column's term and un-rotates;
@@ -119,40 +120,34 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
 }
 
 // ---------------------------------------------------------------------------
-// dkdv: one workgroup of eight waves per (row b, kv head, key tile of 128
-// keys).  Wave w owns the 32 keys kg = w % 4 of the tile and the query half
-// p = w / 4: for queries [32p, 32p+32) of each 64-query tile it computes
-// S = Q K^T and dP = dO V^T, and accumulates its share of dV^T = dO^T P and
-// dK^T = Q^T dS over all D features.  The two waves of a key group never
-// talk inside the loop (no exchange, one barrier per tile); their partial
-// key gradients are added through LDS once, at the end.
-//   * The workgroup's 128 K and V rows sit in swizzled LDS for the whole loop
-//     (B operands of S and dP), which keeps the kernel within 256 registers
-//     per lane.
-//   * Q and dO tiles go straight into double-buffered swizzled LDS
-//     (global_load_lds), one tile ahead; row reads feed S and dP, transposing reads feed Q^T
-//     and dO^T.
-//   * P and dS feed the B operand of dV^T = dO^T P and dK^T = Q^T dS straight
-//     from the accumulator layout.
+// dkdv: one workgroup of four waves per (row b, kv head, key tile of 128 keys),
+// two workgroups per CU.  Wave w owns keys [32w, 32w+32) of the tile for
+// every query, so nothing is reduced across waves; a 64-query tile of the
+// plan is taken as two 32-query halves.  The two waves that share a SIMD
+// belong to different workgroups and are not held in step by a barrier.
+//   * The workgroup's K rows sit in swizzled LDS (B operand of S = Q K^T);
+//     the V operand (B of dP = dO V^T) stays in registers.
+//   * Q and dO half tiles go straight into double-buffered swizzled LDS, one
+//     half ahead; row reads feed S and dP, transposing reads feed Q^T, dO^T.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
+__global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ qstats,
     const float* __restrict__ table, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ kptr, const int32_t* __restrict__ qpack,
     const int32_t* __restrict__ status, int S, int Hq, int Hkv,
     int nk, int nblk, int n_items, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
-  constexpr int BM = kDkvBM, BN = kDkvBN;    // 64 queries x 128 keys
+  constexpr int BM = kDkvBM, BN = kDkvBN;    // plan tiles: 64 queries x 128 keys
+  constexpr int BH = BM / 2;                 // queries per step
   constexpr int NKK = D / 16;
-  constexpr int NDB = D / 32;                // 32-feature blocks
-  constexpr int NBUF = 2;                    // current tile + 1 prefetched
+  constexpr int NDB = D / 32;
+  static_assert(BN == 4 * 32 && BH == 32, "four waves of 32 keys, 32-query steps");
   using T = SwzTile<D>;
-  __shared__ __align__(16) bf16 Qs[NBUF][BM * D];
-  __shared__ __align__(16) bf16 Gs[NBUF][BM * D];
-  __shared__ __align__(16) float s_st[NBUF][4][BM];  // LSE*log2(e), Dv, lo, hi (int bits)
+  __shared__ __align__(16) bf16 Qs[2][BH * D];
+  __shared__ __align__(16) bf16 Gs[2][BH * D];
+  __shared__ __align__(16) float s_st[2][4][BM];     // LSE*log2(e), Dv, lo, hi (int bits)
   __shared__ __align__(16) bf16 Ks[BN * D];          // this workgroup's keys (rotated)
-  __shared__ __align__(16) bf16 Vs[BN * D];          // and values
 
   const int item = xcd_work_item(blockIdx.x, n_items);   // (hkv, b, kt), kt fastest
   if (item < 0) return;
@@ -162,20 +157,21 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
   const int group = Hq / Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
-  const int kg = wave & 3, p = wave >> 2;
-  const int key = kt * BN + kg * 32 + col;       // row-local key of this lane's column
+  const int key = kt * BN + wave * 32 + col;     // row-local key of this lane's column
   const bool kvalid = key < S;
   const size_t tok0 = (size_t)b * S;
   const size_t ktok = tok0 + (kvalid ? key : S - 1);
   const bool bad = status[0] != kStatusOk;
   const float scale_log2 = scale * kLog2e;
 
-  // The workgroup's K and V rows live in LDS for the whole loop.
+  // V operand: lane holds key `col`, features 16*kk + 8*h + i; K rows in LDS.
+  bf16x8 vf[NKK];
   {
+    const bf16* vp = v + (ktok * Hkv + hkv) * D + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) vf[kk] = *(const bf16x8*)(vp + 16 * kk);
     const size_t kv_row_stride = (size_t)Hkv * D;
-    tile_load_direct<D, BN, 512>(Ks, kr + tok0 * kv_row_stride + hkv * D, kv_row_stride, kt * BN,
-                                 S - 1);
-    tile_load_direct<D, BN, 512>(Vs, v + tok0 * kv_row_stride + hkv * D, kv_row_stride, kt * BN,
+    tile_load_direct<D, BN, 256>(Ks, kr + tok0 * kv_row_stride + hkv * D, kv_row_stride, kt * BN,
                                  S - 1);
   }
   f32x16 dka[NDB], dva[NDB];
@@ -184,21 +180,24 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
 #pragma unroll
     for (int j = 0; j < 16; ++j) { dka[db][j] = 0.f; dva[db][j] = 0.f; }
 
-  // Q and dO tiles go straight into LDS; wave 0 also fetches the tile's
+  // Q and dO half tiles go straight into LDS; wave 0 also fetches the tile's
   // per-query record (LSE, Dv, visible-key interval).
   const size_t q_row_stride = (size_t)Hq * D;
-  auto issue = [&](int buf, int hq, int qt) {
-    tile_load_direct<D, BM, 512>(Qs[buf], qr + tok0 * q_row_stride + (size_t)hq * D, q_row_stride,
-                                 qt * BM, S - 1);
-    tile_load_direct<D, BM, 512>(Gs[buf], dout + tok0 * q_row_stride + (size_t)hq * D,
-                                 q_row_stride, qt * BM, S - 1);
+  auto issue = [&](int buf, int hq, int qt, int half) {
+    const int row0 = qt * BM + half * BH;
+    tile_load_direct<D, BH, 256>(Qs[buf], qr + tok0 * q_row_stride + (size_t)hq * D, q_row_stride,
+                                 row0, S - 1);
+    tile_load_direct<D, BH, 256>(Gs[buf], dout + tok0 * q_row_stride + (size_t)hq * D,
+                                 q_row_stride, row0, S - 1);
     if (wave == 0) {
       const float* rec = qstats + (((size_t)b * Hq + hq) * nblk + qt) * 4 * BM;
       __builtin_amdgcn_global_load_lds((const void*)(rec + 4 * lane), (lds_void*)(&s_st[buf][0][0]),
                                        16, 0, 0);
     }
   };
-  // Work list: every q head of the group x every live, not anchor-only query tile.
+
+  // Work list: every q head of the group x every live, not anchor-only query
+  // tile x its two halves.
   const int e_begin = kptr[ktile], e_end = kptr[ktile + 1];
   const int h_end = (hkv + 1) * group;
   auto first = [&](int& ee, int& hh) {
@@ -215,45 +214,46 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
     } while (hh < h_end && packed_kind(qpack[ee]) == kTileAnchor);
   };
 
-  int e, hq;
+  int e, hq, half = 0;
   first(e, hq);
-  if (hq < h_end) issue(0, hq, packed_idx(qpack[e]));
+  if (hq < h_end) issue(0, hq, packed_idx(qpack[e]), 0);
   int cur = 0;
   while (hq < h_end) {
     const bool need_mask = packed_kind(qpack[e]) != kTileFull || kt == 0;
-    int e1 = e, h1 = hq;
-    advance(e1, h1);
+    int e1 = e, h1 = hq, half1 = half ^ 1;
+    if (half1 == 0) advance(e1, h1);
     const int qt1 = h1 < h_end ? packed_idx(qpack[e1]) : 0;
     wait_direct_loads();
-    __syncthreads();      // tile in buffer `cur` visible; the other buffer free
-    if (h1 < h_end) issue(cur ^ 1, h1, qt1);
+    __syncthreads();      // half tile in buffer `cur` visible; the other buffer free
+    if (h1 < h_end) issue(cur ^ 1, h1, qt1, half1);
     const bf16* Qc = Qs[cur];
     const bf16* Gc = Gs[cur];
+    const float* stc = &s_st[cur][0][0] + half * BH;
 
-    // S = Q K^T, dP = dO V^T for queries [32p, 32p+32): columns = keys.
+    // S = Q K^T, dP = dO V^T for the 32 queries: columns = this wave's keys.
     f32x16 sp, dp;
 #pragma unroll
     for (int j = 0; j < 16; ++j) { sp[j] = 0.f; dp[j] = 0.f; }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const int off = T::chunk_off(32 * p + col, 2 * kk + h);
-      const int koff = T::chunk_off(32 * kg + col, 2 * kk + h);
-      sp = mfma32(*(const bf16x8*)(Qc + off), *(const bf16x8*)(Ks + koff), sp);
-      dp = mfma32(*(const bf16x8*)(Gc + off), *(const bf16x8*)(Vs + koff), dp);
+      const int off = T::chunk_off(col, 2 * kk + h);
+      const bf16x8 kb = *(const bf16x8*)(Ks + T::chunk_off(32 * wave + col, 2 * kk + h));
+      sp = mfma32(*(const bf16x8*)(Qc + off), kb, sp);
+      dp = mfma32(*(const bf16x8*)(Gc + off), vf[kk], dp);
     }
     // P = exp2(s * scale_log2 - lse_log2), dS = P (dP - Dv).
     bf16x8 pb[2], db_[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int q0 = 32 * p + 8 * g + 4 * h;   // tile-local queries q0 .. q0+3
-      const f32x4 l4 = *(const f32x4*)(&s_st[cur][0][q0]);
-      const f32x4 d4 = *(const f32x4*)(&s_st[cur][1][q0]);
+      const int q0 = 8 * g + 4 * h;            // step-local queries q0 .. q0+3
+      const f32x4 l4 = *(const f32x4*)(stc + q0);
+      const f32x4 d4 = *(const f32x4*)(stc + BM + q0);
       float pv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[4 * g + r], scale_log2, -l4[r]));
       if (need_mask) {
-        const int4 lo4 = *(const int4*)(&s_st[cur][2][q0]);
-        const int4 hi4 = *(const int4*)(&s_st[cur][3][q0]);
+        const int4 lo4 = *(const int4*)(stc + 2 * BM + q0);
+        const int4 hi4 = *(const int4*)(stc + 3 * BM + q0);
         pv[0] = (key >= lo4.x && key <= hi4.x) ? pv[0] : 0.f;
         pv[1] = (key >= lo4.y && key <= hi4.y) ? pv[1] : 0.f;
         pv[2] = (key >= lo4.z && key <= hi4.z) ? pv[2] : 0.f;
@@ -266,53 +266,20 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(
         db_[j >> 3][j & 7] = (bf16)(pv[r] * (dp[j] - d4[r]));
       }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS over this wave's 32 queries.
+    // dV^T += dO^T P, dK^T += Q^T dS over the 32 queries.
 #pragma unroll
     for (int dblk = 0; dblk < NDB; ++dblk)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        dva[dblk] = mfma32(tr_operand<D>(Gc, 32 * p + 16 * c, 32 * dblk), pb[c], dva[dblk]);
-        dka[dblk] = mfma32(tr_operand<D>(Qc, 32 * p + 16 * c, 32 * dblk), db_[c], dka[dblk]);
+        dva[dblk] = mfma32(tr_operand<D>(Gc, 16 * c, 32 * dblk), pb[c], dva[dblk]);
+        dka[dblk] = mfma32(tr_operand<D>(Qc, 16 * c, 32 * dblk), db_[c], dka[dblk]);
       }
-    e = e1; hq = h1;
+    e = e1; hq = h1; half = half1;
     cur ^= 1;
   }
 
-  // Add the two query halves: waves p = 1 hand their partial sums to p = 0
-  // through LDS (the tile buffers are free now), dK first, then dV.
-  float* red = reinterpret_cast<float*>(&Qs[0][0]);    // [4 key groups][NDB][16][64] floats
-  const int red_off = ((kg * NDB) * 16) * 64 + lane;
-  __syncthreads();
-  if (p == 1) {
-#pragma unroll
-    for (int dblk = 0; dblk < NDB; ++dblk)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) red[red_off + (dblk * 16 + j) * 64] = dka[dblk][j];
-  }
-  __syncthreads();
-  if (p == 0) {
-#pragma unroll
-    for (int dblk = 0; dblk < NDB; ++dblk)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) dka[dblk][j] += red[red_off + (dblk * 16 + j) * 64];
-  }
-  __syncthreads();
-  if (p == 1) {
-#pragma unroll
-    for (int dblk = 0; dblk < NDB; ++dblk)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) red[red_off + (dblk * 16 + j) * 64] = dva[dblk][j];
-  }
-  __syncthreads();
-  if (p == 0) {
-#pragma unroll
-    for (int dblk = 0; dblk < NDB; ++dblk)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) dva[dblk][j] += red[red_off + (dblk * 16 + j) * 64];
-  }
-
-  // Epilogue (waves p = 0): dK = R(pos)^T (scale * dK'), dV as accumulated.
-  if (p == 0 && kvalid) {
+  // Epilogue: dK = R(pos)^T (scale * dK'), dV as accumulated.
+  if (kvalid) {
     const int pk = pos[ktok];
     const float* tb = table + (size_t)pk * D;      // (D/2) pairs of {cos, sin}
     bf16* dkp = dk + (ktok * Hkv + hkv) * D;
@@ -553,11 +520,11 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, hipStream_t st)
   const int n_items = a.B * pk.nk * a.Hkv;
   const dim3 grid(padded_grid(n_items));
   if (a.D == 128)
-    hipLaunchKernelGGL(k_bwd_dkdv<128>, grid, dim3(512), 0, st, a.qr, a.kr, a.v, a.dout,
+    hipLaunchKernelGGL(k_bwd_dkdv<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout,
                        a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, a.status, a.S,
                        a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.dk, a.dv);
   else
-    hipLaunchKernelGGL(k_bwd_dkdv<64>, grid, dim3(512), 0, st, a.qr, a.kr, a.v, a.dout,
+    hipLaunchKernelGGL(k_bwd_dkdv<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout,
                        a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, a.status, a.S,
                        a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.dk, a.dv);
   return hipGetLastError();
