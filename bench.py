@@ -97,6 +97,18 @@ def cpu_baseline(w, q, k, v, do, budget_s: float) -> dict:
     }
 
 
+# Attention paradigms (the pages' Figure 2 and the full-attention baseline):
+# library flags, whether rows carry the shared anchor, and whether the
+# documents are replaced by one document per row.
+MODES = {
+    "anchor": (0, True, False),
+    "anchor_continuous": (1, True, False),
+    "intra_doc_reset": (2, False, False),
+    "intra_doc_continuous": (3, False, False),
+    "full_causal": (2, False, True),
+}
+
+
 def device_peak() -> dict | None:
     """Dense bf16 MFMA peak re-derived on this machine: compute units x max
     engine clock (rocminfo) x 4096 flop/clk/CU (gfx950, 32x32x16 bf16)."""
@@ -125,6 +137,10 @@ def main() -> int:
     ap.add_argument("--workload", default="64k",
                     help="tiny | 8k | 64k | 128k_gqa | short_docs (default: 64k, the headline)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--mode", default="anchor", choices=sorted(MODES),
+                    help="anchor (default, the method) | anchor_continuous | intra_doc_reset | "
+                         "intra_doc_continuous | full_causal: the pages' other attention paradigms "
+                         "through the same kernels, on the same documents")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
@@ -137,10 +153,17 @@ def main() -> int:
     from long_context_attention_doc_amd.accounting import algorithmic_bytes, flops_fwd_bwd
 
     w = workloads.get(args.workload)
+    flags, anchor, one_doc = MODES[args.mode]
     dev = torch.device("cuda:0")
     q, k, v, do = workloads.make_tensors(w.B, w.S, w.Hq, w.Hkv, w.D, w.tensor_seed)
     qc, kc, vc, doc = (t.to(dev) for t in (q, k, v, do))
-    cu = torch.from_numpy(w.cu_doc_lens).to(dev)
+    doc_rows = [list(r) for r in w.doc_rows]
+    if one_doc:
+        doc_rows = [[w.S]] * w.B
+    elif not anchor:
+        doc_rows = workloads.rows_without_anchor(doc_rows)
+    cu_np = (w.cu_doc_lens if anchor else workloads.cu_doc_lens_no_anchor(doc_rows, w.S))
+    cu = torch.from_numpy(cu_np).to(dev)
     ws_f = torch.empty(api.workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, False), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(api.workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, True), dtype=torch.uint8, device=dev)
 
@@ -150,11 +173,12 @@ def main() -> int:
              for _ in range(args.steps)]
 
     def step(mark=None):
-        o, lse = api.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base, True, None, ws_f)
+        o, lse = api.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base, True, None, ws_f, flags=flags)
         if mark is not None:
             mark[0].record()
         if w.backward:
-            api.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base, True, None, ws_b)
+            api.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base, True, None, ws_b,
+                                flags=flags)
         if mark is not None:
             mark[1].record()
 
@@ -173,7 +197,7 @@ def main() -> int:
     bwd_ms = sum(a.elapsed_time(b) for a, b in marks) / args.steps
     fwd_ms = ms - bwd_ms
 
-    fl = flops_fwd_bwd(w.doc_rows, w.Hq, w.D)
+    fl = flops_fwd_bwd(doc_rows, w.Hq, w.D, anchor=anchor)
     total_flops = fl["total"] if w.backward else fl["fwd"]
     tflops = total_flops / (ms * 1e-3) / 1e12
     tokens = w.B * w.S
@@ -189,16 +213,20 @@ def main() -> int:
     achieved = algo / (avg_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": f"k_{dom}", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": _traffic(dom, w.name), "avg_launch_ms": avg_ms,
+                "traffic": _traffic(dom, w.name) if args.mode == "anchor" else None,
+                "avg_launch_ms": avg_ms,
                 "algorithmic_flops_per_launch": algo}
 
     out = {
-        "metric": "AnchorAttention fwd+bwd unmasked TFLOP/s at 64K (also tokens/s, % of dense bf16 MFMA peak)",
+        "metric": ("AnchorAttention fwd+bwd unmasked TFLOP/s at 64K (also tokens/s, % of dense bf16 MFMA peak)"
+                   if args.mode == "anchor" else
+                   f"{args.mode} baseline fwd+bwd unmasked TFLOP/s (same kernels; also tokens/s)"),
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.B, "seq_len": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv,
-                   "head_dim": w.D, "rope_base": w.rope_base, "documents_per_row": len(w.doc_rows[0]),
+        "config": {"workload": w.name if args.mode == "anchor" else f"{w.name}_{args.mode}",
+                   "mode": args.mode, "batch": w.B, "seq_len": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "rope_base": w.rope_base, "documents_per_row": len(doc_rows[0]),
                    "backward": w.backward, "unmasked_pairs_per_head": fl["pairs_per_head"]},
         "tokens_per_s": tokens / (ms * 1e-3),
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
@@ -212,7 +240,7 @@ def main() -> int:
         "kernel_ms_per_step": {k_: round(v_, 4) for k_, v_ in per_kernel_ms.items()},
         "roofline": roofline,
     }
-    if args.cpu_budget > 0:
+    if args.cpu_budget > 0 and args.mode == "anchor":
         cb = cpu_baseline(w, q, k, v, do, args.cpu_budget)
         # the whole workload at the oracle's measured rate
         cb["full_workload_estimate_s"] = total_flops / (cb["value"] * 1e12)

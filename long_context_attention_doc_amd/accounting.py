@@ -12,17 +12,19 @@ scores), 14*D in total.
 from __future__ import annotations
 
 
-def unmasked_pairs_closed_form(doc_rows, causal: bool = True) -> int:
+def unmasked_pairs_closed_form(doc_rows, causal: bool = True, anchor: bool = True) -> int:
+    """Without an anchor (the intra-document baselines) a document of N tokens
+    contributes only its N(N+1)/2 causal pairs."""
     total = 0
     for lens in doc_rows:
-        total += 1
+        total += 1 if anchor else 0
         for n in lens:
-            total += (n * (n + 1) // 2 if causal else n * n) + n
+            total += (n * (n + 1) // 2 if causal else n * n) + (n if anchor else 0)
     return total
 
 
-def flops_fwd_bwd(doc_rows, Hq: int, D: int, causal: bool = True) -> dict:
-    pairs = unmasked_pairs_closed_form(doc_rows, causal)
+def flops_fwd_bwd(doc_rows, Hq: int, D: int, causal: bool = True, anchor: bool = True) -> dict:
+    pairs = unmasked_pairs_closed_form(doc_rows, causal, anchor)
     return {
         "pairs_per_head": pairs,
         "fwd": 4.0 * D * Hq * pairs,

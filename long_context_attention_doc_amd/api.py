@@ -16,6 +16,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libanchor_attn.so")
 
 AA_OK, AA_EINVAL, AA_EDOCS, AA_EUNSUPPORTED, AA_EWORKSPACE, AA_EHIP = range(6)
+# Options (anchor_attn.h): continuous position IDs; rows without a shared anchor.
+FLAG_CONTINUOUS_POS, FLAG_NO_ANCHOR = 1, 2
 TILE_FULL, TILE_PARTIAL, TILE_ANCHOR = 1, 2, 3
 
 # Tile shapes the attention kernels run with (query tile x key tile).
@@ -24,7 +26,8 @@ DKV_TILE = (64, 128)
 
 EXPORTS = (
     "anchor_attn_strerror", "anchor_attn_version", "anchor_attn_workspace_size",
-    "anchor_attn_fwd", "anchor_attn_bwd", "anchor_attn_position_ids",
+    "anchor_attn_fwd", "anchor_attn_bwd", "anchor_attn_fwd_ex", "anchor_attn_bwd_ex",
+    "anchor_attn_position_ids",
     "anchor_attn_plan_workspace_size", "anchor_attn_plan_capacity", "anchor_attn_tile_plan",
     "anchor_attn_rope", "anchor_attn_device_status", "anchor_attn_profile_begin",
     "anchor_attn_profile_end",
@@ -58,10 +61,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "anchor_attn_workspace_size": (Z, [I, I, I, I, I, I]),
         "anchor_attn_fwd": (I, [P, P, P, P, I, D, I, I, I, I, I, I, F, P, P, P, Z, P]),
         "anchor_attn_bwd": (I, [P, P, P, P, P, P, P, I, D, I, I, I, I, I, I, F, P, P, P, P, Z, P]),
+        "anchor_attn_fwd_ex": (I, [P, P, P, P, I, D, I, I, I, I, I, I, I, F, P, P, P, Z, P]),
+        "anchor_attn_bwd_ex": (I, [P, P, P, P, P, P, P, I, D, I, I, I, I, I, I, I, F, P, P, P, P, Z,
+                                   P]),
         "anchor_attn_position_ids": (I, [P, I, I, I, I, P, P, Z, P]),
         "anchor_attn_plan_workspace_size": (Z, [I, I, I, I]),
         "anchor_attn_plan_capacity": (Z, [I, I, I, I]),
-        "anchor_attn_tile_plan": (I, [P, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P]),
+        "anchor_attn_tile_plan": (I, [P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P]),
         "anchor_attn_rope": (I, [P, P, I, I, I, I, D, P, P, P]),
         "anchor_attn_device_status": (I, [P, P, P]),
         "anchor_attn_profile_begin": (I, [I]),
@@ -116,8 +122,10 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def anchor_attn_fwd(q, k, v, cu_doc_lens, rope_base: float, causal: bool = True,
-                    softmax_scale: float | None = None, workspace: torch.Tensor | None = None):
-    """Forward pass; returns (o [B,S,Hq,D] bf16, lse [B,Hq,S] fp32)."""
+                    softmax_scale: float | None = None, workspace: torch.Tensor | None = None,
+                    flags: int = 0):
+    """Forward pass; returns (o [B,S,Hq,D] bf16, lse [B,Hq,S] fp32).  flags: OR of
+    FLAG_CONTINUOUS_POS / FLAG_NO_ANCHOR (0 = the method, anchor_attn_fwd)."""
     lib = load()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _need_bf16(n, t)
@@ -131,16 +139,24 @@ def anchor_attn_fwd(q, k, v, cu_doc_lens, rope_base: float, causal: bool = True,
         workspace = _workspace(ws_n, q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    _check(lib.anchor_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), cu.numel() - 1,
-                               float(rope_base), int(bool(causal)), B, S, Hq, Hkv, D,
-                               float(softmax_scale or 0.0), _ptr(o), _ptr(lse), _ptr(workspace),
-                               workspace.numel(), _stream(q.device)), "anchor_attn_fwd")
+    if flags:
+        _check(lib.anchor_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), cu.numel() - 1,
+                                      float(rope_base), int(bool(causal)), int(flags), B, S, Hq,
+                                      Hkv, D, float(softmax_scale or 0.0), _ptr(o), _ptr(lse),
+                                      _ptr(workspace), workspace.numel(), _stream(q.device)),
+               "anchor_attn_fwd_ex")
+    else:
+        _check(lib.anchor_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), cu.numel() - 1,
+                                   float(rope_base), int(bool(causal)), B, S, Hq, Hkv, D,
+                                   float(softmax_scale or 0.0), _ptr(o), _ptr(lse), _ptr(workspace),
+                                   workspace.numel(), _stream(q.device)), "anchor_attn_fwd")
     return o, lse
 
 
 def anchor_attn_bwd(q, k, v, o, lse, dout, cu_doc_lens, rope_base: float, causal: bool = True,
-                    softmax_scale: float | None = None, workspace: torch.Tensor | None = None):
-    """Backward pass; returns (dq, dk, dv) bf16."""
+                    softmax_scale: float | None = None, workspace: torch.Tensor | None = None,
+                    flags: int = 0):
+    """Backward pass; returns (dq, dk, dv) bf16.  flags as for anchor_attn_fwd."""
     lib = load()
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _need_bf16(n, t)
@@ -155,28 +171,35 @@ def anchor_attn_bwd(q, k, v, o, lse, dout, cu_doc_lens, rope_base: float, causal
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    _check(lib.anchor_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(cu),
-                               cu.numel() - 1, float(rope_base), int(bool(causal)), B, S, Hq, Hkv,
-                               D, float(softmax_scale or 0.0), _ptr(dq), _ptr(dk), _ptr(dv),
-                               _ptr(workspace), workspace.numel(), _stream(q.device)),
-           "anchor_attn_bwd")
+    if flags:
+        _check(lib.anchor_attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                      _ptr(cu), cu.numel() - 1, float(rope_base), int(bool(causal)),
+                                      int(flags), B, S, Hq, Hkv, D, float(softmax_scale or 0.0),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                      workspace.numel(), _stream(q.device)), "anchor_attn_bwd_ex")
+    else:
+        _check(lib.anchor_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                   _ptr(cu), cu.numel() - 1, float(rope_base), int(bool(causal)), B,
+                                   S, Hq, Hkv, D, float(softmax_scale or 0.0), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q.device)),
+               "anchor_attn_bwd")
     return dq, dk, dv
 
 
-def anchor_attn_position_ids(cu_doc_lens, B: int, S: int, mode: int = 0, device="cuda"):
-    """Position IDs int32 [B*S] (mode 0 reset, 1 continuous)."""
+def anchor_attn_position_ids(cu_doc_lens, B: int, S: int, flags: int = 0, device="cuda"):
+    """Position IDs int32 [B*S]; flags as for anchor_attn_fwd (0: reset, with anchor)."""
     lib = load()
     cu = _dev_cu(cu_doc_lens, device)
     pos = torch.empty(B * S, dtype=torch.int32, device=device)
     ws = _workspace(lib.anchor_attn_plan_workspace_size(B, S, 64, 64), device)
-    _check(lib.anchor_attn_position_ids(_ptr(cu), cu.numel() - 1, B, S, mode, _ptr(pos), _ptr(ws),
+    _check(lib.anchor_attn_position_ids(_ptr(cu), cu.numel() - 1, B, S, flags, _ptr(pos), _ptr(ws),
                                         ws.numel(), _stream(pos.device)),
            "anchor_attn_position_ids")
     return pos, ws
 
 
 def anchor_attn_tile_plan(cu_doc_lens, B: int, S: int, BM: int, BN: int, causal: bool = True,
-                          device="cuda"):
+                          device="cuda", flags: int = 0):
     """Tile plan as a dict of device tensors (query-major and key-major CSR)."""
     lib = load()
     cu = _dev_cu(cu_doc_lens, device)
@@ -194,6 +217,7 @@ def anchor_attn_tile_plan(cu_doc_lens, B: int, S: int, BM: int, BN: int, causal:
     }
     ws = _workspace(lib.anchor_attn_plan_workspace_size(B, S, BM, BN), device)
     _check(lib.anchor_attn_tile_plan(_ptr(cu), cu.numel() - 1, B, S, BM, BN, int(bool(causal)),
+                                     int(flags),
                                      _ptr(out["qptr"]), _ptr(out["kidx"]), _ptr(out["kkind"]),
                                      _ptr(out["kptr"]), _ptr(out["qidx"]), _ptr(out["qkind"]),
                                      _ptr(out["n_live"]), _ptr(ws), ws.numel(),
@@ -239,22 +263,23 @@ def profile_end() -> dict:
 
 class _AnchorAttnFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, cu, rope_base, causal, softmax_scale):
-        o, lse = anchor_attn_fwd(q, k, v, cu, rope_base, causal, softmax_scale)
+    def forward(ctx, q, k, v, cu, rope_base, causal, softmax_scale, flags):
+        o, lse = anchor_attn_fwd(q, k, v, cu, rope_base, causal, softmax_scale, flags=flags)
         ctx.save_for_backward(q, k, v, o, lse, cu)
-        ctx.cfg = (rope_base, causal, softmax_scale)
+        ctx.cfg = (rope_base, causal, softmax_scale, flags)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse, cu = ctx.saved_tensors
-        rope_base, causal, scale = ctx.cfg
-        dq, dk, dv = anchor_attn_bwd(q, k, v, o, lse, do.contiguous(), cu, rope_base, causal, scale)
-        return dq, dk, dv, None, None, None, None
+        rope_base, causal, scale, flags = ctx.cfg
+        dq, dk, dv = anchor_attn_bwd(q, k, v, o, lse, do.contiguous(), cu, rope_base, causal, scale,
+                                     flags=flags)
+        return dq, dk, dv, None, None, None, None, None
 
 
 def anchor_attention(q, k, v, cu_doc_lens, rope_base: float, causal: bool = True,
-                     softmax_scale: float | None = None):
+                     softmax_scale: float | None = None, flags: int = 0):
     """AnchorAttention with autograd: q [B,S,Hq,D], k/v [B,S,Hkv,D] bf16 on the GPU."""
     cu = _dev_cu(cu_doc_lens, q.device)
-    return _AnchorAttnFn.apply(q, k, v, cu, float(rope_base), bool(causal), softmax_scale)
+    return _AnchorAttnFn.apply(q, k, v, cu, float(rope_base), bool(causal), softmax_scale, int(flags))

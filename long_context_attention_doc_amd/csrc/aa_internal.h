@@ -60,15 +60,15 @@ struct PlanBufs {
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_positions(const int32_t* cu, int n_seg, int B, int S, int causal, int mode,
-                            TokenTables tt, int32_t* status, hipStream_t st);
-hipError_t launch_plan(const int32_t* lo, const int32_t* hi, int B, int S, PlanBufs pb,
+                            int anchor, TokenTables tt, int32_t* status, hipStream_t st);
+hipError_t launch_plan(const int32_t* lo, const int32_t* hi, int B, int S, int anchor, PlanBufs pb,
                        bool key_major, hipStream_t st);
 hipError_t launch_rope_table(int S, int D, const RopeTheta& th, float* table, hipStream_t st);
-hipError_t launch_rope_apply(const bf16* x, const int32_t* pos, const float* table, int B, int S,
+hipError_t launch_rope_apply(const bf16* x, const int32_t* pos, const float* table, int npos, int B, int S,
                              int H, int D, bf16* x_rot, hipStream_t st);
 hipError_t launch_fwd(const bf16* qr, const bf16* kr, const bf16* v, TokenTables tt,
                       const PlanBufs& pb, const int32_t* status, int B, int S, int Hq, int Hkv,
-                      int D, float scale, bf16* o, float* lse, hipStream_t st);
+                      int D, float scale, int anchor, bf16* o, float* lse, hipStream_t st);
 
 struct BwdArgs {
   const bf16* qr;      // rotated q [B,S,Hq,D]
@@ -91,6 +91,7 @@ struct BwdArgs {
   bf16* dv;
   int B, S, Hq, Hkv, D;
   float scale;
+  int anchor;          // 0: rows without a shared anchor (intra-document attention)
 };
 constexpr int kPreRows = 64;    // rows per block of the backward preprocess
 

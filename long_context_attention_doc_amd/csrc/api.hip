@@ -82,7 +82,7 @@ Layout layout(int B, int S, int Hq, int Hkv, int D, bool bwd) {
   L.pos = o;    o = up(o + T * 4);
   L.lo = o;     o = up(o + T * 4);
   L.hi = o;     o = up(o + T * 4);
-  L.table = o;  o = up(o + (size_t)S * D * 4);
+  L.table = o;  o = up(o + (size_t)(S + 1) * D * 4);   // positions 0 .. S
   L.qrot = o;   o = up(o + T * Hq * D * 2);
   L.krot = o;   o = up(o + T * Hkv * D * 2);
   L.pq = plan_layout(B, S, kFwdBM, kFwdBN, o);
@@ -158,20 +158,31 @@ hipError_t launch_zero_status(int32_t* status, hipStream_t st) {
 // Positions, plan(s), RoPE table, rotated q and k: the prologue shared by
 // the forward and the backward.
 aa_status prologue(const Layout& L, char* ws, const void* q, const void* k,
-                   const int32_t* cu, int n_seg, double rope_base, int causal, int B, int S,
-                   int Hq, int Hkv, int D, bool bwd, hipStream_t st) {
+                   const int32_t* cu, int n_seg, double rope_base, int causal, int flags, int B,
+                   int S, int Hq, int Hkv, int D, bool bwd, hipStream_t st) {
   int32_t* status = (int32_t*)(ws + L.status);
   TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
+  const int mode = (flags & AA_FLAG_CONTINUOUS_POS) ? 1 : 0;
+  const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   AA_LAUNCH(AA_K_STATUS, st, launch_zero_status(status, st));
-  AA_LAUNCH(AA_K_POSITIONS, st, launch_positions(cu, n_seg, B, S, causal, 0, tt, status, st));
-  AA_LAUNCH(AA_K_PLAN, st, launch_plan(tt.lo, tt.hi, B, S, plan_bufs(L.pq, ws), false, st));
-  if (bwd) AA_LAUNCH(AA_K_PLAN, st, launch_plan(tt.lo, tt.hi, B, S, plan_bufs(L.pk, ws), true, st));
+  AA_LAUNCH(AA_K_POSITIONS, st,
+            launch_positions(cu, n_seg, B, S, causal, mode, anchor, tt, status, st));
+  AA_LAUNCH(AA_K_PLAN, st,
+            launch_plan(tt.lo, tt.hi, B, S, anchor, plan_bufs(L.pq, ws), false, st));
+  if (bwd)
+    AA_LAUNCH(AA_K_PLAN, st,
+              launch_plan(tt.lo, tt.hi, B, S, anchor, plan_bufs(L.pk, ws), true, st));
   float* table = (float*)(ws + L.table);
-  AA_LAUNCH(AA_K_ROPE_TABLE, st, launch_rope_table(S, D, make_theta(D, rope_base), table, st));
+  // Position IDs reach S when a document without an anchor fills a row under
+  // reset IDs (its tokens count 1 .. S), so the table has S + 1 rows.
+  AA_LAUNCH(AA_K_ROPE_TABLE, st,
+            launch_rope_table(S + 1, D, make_theta(D, rope_base), table, st));
   AA_LAUNCH(AA_K_ROPE, st,
-            launch_rope_apply((const bf16*)q, tt.pos, table, B, S, Hq, D, (bf16*)(ws + L.qrot), st));
+            launch_rope_apply((const bf16*)q, tt.pos, table, S + 1, B, S, Hq, D,
+                              (bf16*)(ws + L.qrot), st));
   AA_LAUNCH(AA_K_ROPE, st,
-            launch_rope_apply((const bf16*)k, tt.pos, table, B, S, Hkv, D, (bf16*)(ws + L.krot), st));
+            launch_rope_apply((const bf16*)k, tt.pos, table, S + 1, B, S, Hkv, D,
+                              (bf16*)(ws + L.krot), st));
   return AA_OK;
 }
 
@@ -201,11 +212,16 @@ size_t anchor_attn_workspace_size(int B, int S, int Hq, int Hkv, int D, int for_
   return layout(B, S, Hq, Hkv, D, for_bwd != 0).total;
 }
 
-aa_status anchor_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_doc_lens,
-                          int n_seg, double rope_base, int causal, int B, int S, int Hq, int Hkv,
-                          int D, float softmax_scale, void* o, float* lse, void* workspace,
-                          size_t ws_bytes, hipStream_t stream) {
+static bool flags_ok(int flags) {
+  return (flags & ~(AA_FLAG_CONTINUOUS_POS | AA_FLAG_NO_ANCHOR)) == 0;
+}
+
+static aa_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* cu_doc_lens,
+                          int n_seg, double rope_base, int causal, int flags, int B, int S, int Hq,
+                          int Hkv, int D, float softmax_scale, void* o, float* lse,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !cu_doc_lens || !o || !lse || !workspace) return AA_EINVAL;
+  if (!flags_ok(flags)) return AA_EINVAL;
   if (!shape_ok(B, S, Hq, Hkv, D) || n_seg < B) return AA_EINVAL;
   if (D != 64 && D != 128) return AA_EUNSUPPORTED;
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
@@ -216,24 +232,26 @@ aa_status anchor_attn_fwd(const void* q, const void* k, const void* v, const int
   if (ws_bytes < L.total) return AA_EWORKSPACE;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)D);
   char* ws = (char*)workspace;
-  aa_status s = prologue(L, ws, q, k, cu_doc_lens, n_seg, rope_base, causal, B, S, Hq, Hkv, D,
-                         false, stream);
+  aa_status s = prologue(L, ws, q, k, cu_doc_lens, n_seg, rope_base, causal, flags, B, S, Hq,
+                         Hkv, D, false, stream);
   if (s != AA_OK) return s;
   TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
+  const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   AA_LAUNCH(AA_K_FWD, stream,
             launch_fwd((const bf16*)(ws + L.qrot), (const bf16*)(ws + L.krot), (const bf16*)v, tt,
                        plan_bufs(L.pq, ws), (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D,
-                       scale, (bf16*)o, lse, stream));
+                       scale, anchor, (bf16*)o, lse, stream));
   return AA_OK;
 }
 
-aa_status anchor_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+static aa_status bwd_impl(const void* q, const void* k, const void* v, const void* o,
                           const float* lse, const void* dout, const int32_t* cu_doc_lens,
-                          int n_seg, double rope_base, int causal, int B, int S, int Hq, int Hkv,
-                          int D, float softmax_scale, void* dq, void* dk, void* dv,
+                          int n_seg, double rope_base, int causal, int flags, int B, int S, int Hq,
+                          int Hkv, int D, float softmax_scale, void* dq, void* dk, void* dv,
                           void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !dout || !cu_doc_lens || !dq || !dk || !dv || !workspace)
     return AA_EINVAL;
+  if (!flags_ok(flags)) return AA_EINVAL;
   if (!shape_ok(B, S, Hq, Hkv, D) || n_seg < B) return AA_EINVAL;
   if (D != 64 && D != 128) return AA_EUNSUPPORTED;
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
@@ -245,8 +263,8 @@ aa_status anchor_attn_bwd(const void* q, const void* k, const void* v, const voi
   if (ws_bytes < L.total) return AA_EWORKSPACE;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)D);
   char* ws = (char*)workspace;
-  aa_status s = prologue(L, ws, q, k, cu_doc_lens, n_seg, rope_base, causal, B, S, Hq, Hkv, D,
-                         true, stream);
+  aa_status s = prologue(L, ws, q, k, cu_doc_lens, n_seg, rope_base, causal, flags, B, S, Hq,
+                         Hkv, D, true, stream);
   if (s != AA_OK) return s;
   BwdArgs a;
   a.qr = (const bf16*)(ws + L.qrot);
@@ -269,19 +287,58 @@ aa_status anchor_attn_bwd(const void* q, const void* k, const void* v, const voi
   a.dv = (bf16*)dv;
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
   a.scale = scale;
+  a.anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   AA_LAUNCH(AA_K_BWD_PRE, stream, launch_bwd_pre(a, stream));
   AA_LAUNCH(AA_K_BWD_DKDV, stream, launch_bwd_dkdv(a, plan_bufs(L.pk, ws), stream));
   AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
-  AA_LAUNCH(AA_K_BWD_ANCHOR, stream, launch_bwd_anchor(a, stream));
+  // without an anchor, key 0 is an ordinary key and dk/dv of it are complete
+  if (a.anchor) AA_LAUNCH(AA_K_BWD_ANCHOR, stream, launch_bwd_anchor(a, stream));
   return AA_OK;
 }
 
-aa_status anchor_attn_position_ids(const int32_t* cu_doc_lens, int n_seg, int B, int S, int mode,
+aa_status anchor_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_doc_lens,
+                          int n_seg, double rope_base, int causal, int B, int S, int Hq, int Hkv,
+                          int D, float softmax_scale, void* o, float* lse, void* workspace,
+                          size_t ws_bytes, hipStream_t stream) {
+  return fwd_impl(q, k, v, cu_doc_lens, n_seg, rope_base, causal, 0, B, S, Hq, Hkv, D,
+                  softmax_scale, o, lse, workspace, ws_bytes, stream);
+}
+
+aa_status anchor_attn_fwd_ex(const void* q, const void* k, const void* v,
+                             const int32_t* cu_doc_lens, int n_seg, double rope_base, int causal,
+                             int flags, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+                             void* o, float* lse, void* workspace, size_t ws_bytes,
+                             hipStream_t stream) {
+  return fwd_impl(q, k, v, cu_doc_lens, n_seg, rope_base, causal, flags, B, S, Hq, Hkv, D,
+                  softmax_scale, o, lse, workspace, ws_bytes, stream);
+}
+
+aa_status anchor_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, const int32_t* cu_doc_lens,
+                          int n_seg, double rope_base, int causal, int B, int S, int Hq, int Hkv,
+                          int D, float softmax_scale, void* dq, void* dk, void* dv,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return bwd_impl(q, k, v, o, lse, dout, cu_doc_lens, n_seg, rope_base, causal, 0, B, S, Hq, Hkv,
+                  D, softmax_scale, dq, dk, dv, workspace, ws_bytes, stream);
+}
+
+aa_status anchor_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, const int32_t* cu_doc_lens,
+                             int n_seg, double rope_base, int causal, int flags, int B, int S,
+                             int Hq, int Hkv, int D, float softmax_scale, void* dq, void* dk,
+                             void* dv, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return bwd_impl(q, k, v, o, lse, dout, cu_doc_lens, n_seg, rope_base, causal, flags, B, S, Hq,
+                  Hkv, D, softmax_scale, dq, dk, dv, workspace, ws_bytes, stream);
+}
+
+aa_status anchor_attn_position_ids(const int32_t* cu_doc_lens, int n_seg, int B, int S, int flags,
                                    int32_t* pos, void* workspace, size_t ws_bytes,
                                    hipStream_t stream) {
   if (!cu_doc_lens || !pos || !workspace) return AA_EINVAL;
   if (B < 1 || S < 1 || (long long)B * S > 0x7fffffffLL || n_seg < B) return AA_EINVAL;
-  if (mode != 0 && mode != 1) return AA_EINVAL;
+  if (!flags_ok(flags)) return AA_EINVAL;
+  const int mode = (flags & AA_FLAG_CONTINUOUS_POS) ? 1 : 0;
+  const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   if (!aligned(workspace, kAlign) || !aligned(pos, 4) || !aligned(cu_doc_lens, 4)) return AA_EINVAL;
   const size_t T = (size_t)B * S;
   const size_t need = up(4) + 2 * up(T * 4);
@@ -291,7 +348,7 @@ aa_status anchor_attn_position_ids(const int32_t* cu_doc_lens, int n_seg, int B,
   TokenTables tt{pos, (int32_t*)(ws + up(4)), (int32_t*)(ws + up(4) + up(T * 4))};
   hipLaunchKernelGGL(k_zero_status, dim3(1), dim3(64), 0, stream, status);
   AA_HIP(hipGetLastError());
-  AA_HIP(launch_positions(cu_doc_lens, n_seg, B, S, 1, mode, tt, status, stream));
+  AA_HIP(launch_positions(cu_doc_lens, n_seg, B, S, 1, mode, anchor, tt, status, stream));
   return AA_OK;
 }
 
@@ -310,13 +367,14 @@ size_t anchor_attn_plan_workspace_size(int B, int S, int BM, int BN) {
 }
 
 aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, int S, int BM, int BN,
-                                int causal, int32_t* qptr, int32_t* kidx, uint8_t* kkind,
+                                int causal, int flags, int32_t* qptr, int32_t* kidx, uint8_t* kkind,
                                 int32_t* kptr, int32_t* qidx, uint8_t* qkind, int32_t* n_live,
                                 void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!cu_doc_lens || !qptr || !kidx || !kkind || !kptr || !qidx || !qkind || !n_live || !workspace)
     return AA_EINVAL;
   if (B < 1 || S < 1 || (long long)B * S > 0x7fffffffLL || n_seg < B) return AA_EINVAL;
   if (!tile_ok(BM) || !tile_ok(BN)) return AA_EUNSUPPORTED;
+  if (!flags_ok(flags)) return AA_EINVAL;
   if (!aligned(workspace, kAlign)) return AA_EINVAL;
   const size_t need = anchor_attn_plan_workspace_size(B, S, BM, BN);
   if (ws_bytes < need) return AA_EWORKSPACE;
@@ -333,8 +391,9 @@ aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, in
   pb.kpack = nullptr; pb.qpack = nullptr;
   hipLaunchKernelGGL(k_zero_status, dim3(1), dim3(64), 0, stream, status);
   AA_HIP(hipGetLastError());
-  AA_HIP(launch_positions(cu_doc_lens, n_seg, B, S, causal, 0, tt, status, stream));
-  AA_HIP(launch_plan(tt.lo, tt.hi, B, S, pb, true, stream));
+  const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
+  AA_HIP(launch_positions(cu_doc_lens, n_seg, B, S, causal, 0, anchor, tt, status, stream));
+  AA_HIP(launch_plan(tt.lo, tt.hi, B, S, anchor, pb, true, stream));
   return AA_OK;
 }
 
@@ -347,7 +406,7 @@ aa_status anchor_attn_rope(const void* x, const int32_t* pos, int B, int S, int 
   if (!aligned(x, 16) || !aligned(x_rot, 16) || !aligned(table, 16) || !aligned(pos, 4))
     return AA_EINVAL;
   AA_HIP(launch_rope_table(S, D, make_theta(D, rope_base), table, stream));
-  AA_HIP(launch_rope_apply((const bf16*)x, pos, table, B, S, H, D, (bf16*)x_rot, stream));
+  AA_HIP(launch_rope_apply((const bf16*)x, pos, table, S, B, S, H, D, (bf16*)x_rot, stream));
   return AA_OK;
 }
 

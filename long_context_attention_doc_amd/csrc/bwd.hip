@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
     const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi, int S, int Hq, int Hkv,
-    int nblk, float scale, float* __restrict__ dvec, float* __restrict__ ds0,
+    int nblk, float scale, int anchor, float* __restrict__ dvec, float* __restrict__ ds0,
     float* __restrict__ part_dk, float* __restrict__ part_dv, float* __restrict__ qstats) {
   constexpr int LPR = D / 8;                // lanes per row
   constexpr int RPP = 256 / LPR;            // rows per pass of the workgroup
@@ -83,7 +83,8 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
       dp0 += __shfl_xor(dp0, off2);
     }
     const float L = lse[((size_t)b * Hq + hq) * S + (valid ? row : S - 1)];
-    float p0 = valid ? __builtin_amdgcn_exp2f((s0 * scale - L) * kLog2e) : 0.f;
+    // without an anchor there is no anchor column: its weight and dS are zero
+    float p0 = valid && anchor ? __builtin_amdgcn_exp2f((s0 * scale - L) * kLog2e) : 0.f;
     const float dsv = p0 * (dp0 - d_o);
     if (valid && (tid % LPR) == 0) {
       dvec[((size_t)b * Hq + hq) * S + row] = d_o;
@@ -137,7 +138,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     const float* __restrict__ table, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ kptr, const int32_t* __restrict__ qpack,
     const int32_t* __restrict__ status, int S, int Hq, int Hkv,
-    int nk, int nblk, int n_items, float scale, bf16* __restrict__ dk, bf16* __restrict__ dv) {
+    int nk, int nblk, int n_items, float scale, int anchor, bf16* __restrict__ dk,
+    bf16* __restrict__ dv) {
   constexpr int BM = kDkvBM, BN = kDkvBN;    // plan tiles: 64 queries x 128 keys
   constexpr int BH = BM / 2;                 // queries per step
   constexpr int NKK = D / 16;
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   if (hq < h_end) issue(0, hq, packed_idx(qpack[e]), 0);
   int cur = 0;
   while (hq < h_end) {
-    const bool need_mask = packed_kind(qpack[e]) != kTileFull || kt == 0;
+    const bool need_mask = packed_kind(qpack[e]) != kTileFull || (anchor && kt == 0);
     int e1 = e, h1 = hq, half1 = half ^ 1;
     if (half1 == 0) advance(e1, h1);
     const int qt1 = h1 < h_end ? packed_idx(qpack[e1]) : 0;
@@ -321,6 +323,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const int32_t* __restrict__ hi, const int32_t* __restrict__ qptr,
     const int32_t* __restrict__ kpack,
     const int32_t* __restrict__ status, int S, int Hq, int Hkv, int nq, int n_items, float scale,
+    int anchor,
     bf16* __restrict__ dq) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int NKK = D / 16;
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     constexpr int BUF = decltype(bufc)::value;
     const int ent = kpack[e_first + i];
     const int kt = packed_idx(ent);
-    const bool need_mask = packed_kind(ent) != kTileFull || kt == 0;
+    const bool need_mask = packed_kind(ent) != kTileFull || (anchor && kt == 0);
     const bool more = i + 1 < n_tiles;
     const int ent_next = more ? kpack[e_first + i + 1] : 0;
     wait_direct_loads();
@@ -507,11 +510,11 @@ hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st) {
   const dim3 grid(a.B * a.nblk, a.Hq);
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_pre<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.dout,
-                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.dvec, a.ds0,
+                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.dvec, a.ds0,
                        a.part_dk, a.part_dv, a.qstats);
   else
     hipLaunchKernelGGL(k_bwd_pre<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.dout,
-                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.dvec, a.ds0,
+                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.dvec, a.ds0,
                        a.part_dk, a.part_dv, a.qstats);
   return hipGetLastError();
 }
@@ -522,11 +525,11 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, hipStream_t st)
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_dkdv<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout,
                        a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, a.status, a.S,
-                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.dk, a.dv);
+                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, a.dk, a.dv);
   else
     hipLaunchKernelGGL(k_bwd_dkdv<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout,
                        a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, a.status, a.S,
-                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.dk, a.dv);
+                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, a.dk, a.dv);
   return hipGetLastError();
 }
 
@@ -536,11 +539,11 @@ hipError_t launch_bwd_dq(const BwdArgs& a, const PlanBufs& pq, hipStream_t st) {
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
-                       a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.dq);
+                       a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.dq);
   else
     hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
-                       a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.dq);
+                       a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.dq);
   return hipGetLastError();
 }
 

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
     const int32_t* __restrict__ qptr, const int32_t* __restrict__ kpack,
     const int32_t* __restrict__ status, int S, int Hq, int Hkv,
-    int nq, int n_items, float scale_log2, bf16* __restrict__ o, float* __restrict__ lse) {
+    int nq, int n_items, float scale_log2, int anchor, bf16* __restrict__ o,
+    float* __restrict__ lse) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int NKK = D / 16;    // 16-wide reduction steps over d
   constexpr int NDB = D / 32;    // 32-row blocks of d in O^T
@@ -79,11 +80,19 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk);
   }
 
-  // Anchor column: s_i0 = q'_i . k'_0 (k'_0 = k_0, its position is 0).
+  // Anchor column: s_i0 = q'_i . k'_0 (k'_0 = k_0, its position is 0).  Rows
+  // without an anchor start from an empty softmax instead.
   const size_t tok0 = (size_t)b * S;
   float m, l;
   f32x16 acc[NDB];
-  {
+  if (!anchor) {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
+  } else {
     const bf16* k0 = kr + (tok0 * Hkv + hkv) * D + 8 * h;
     float s0 = 0.f;
 #pragma unroll
@@ -130,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     constexpr int BUF = decltype(bufc)::value;
     const int ent = kpack[e_first + i];
     const int kt = packed_idx(ent);
-    const bool need_mask = packed_kind(ent) != kTileFull || kt == 0;
+    const bool need_mask = packed_kind(ent) != kTileFull || (anchor && kt == 0);
     const bool more = i + 1 < n_tiles;
     const int ent_next = more ? kpack[e_first + i + 1] : 0;
     wait_direct_loads();
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     const bool raise = mt > m;
     if (__builtin_amdgcn_ballot_w64(raise)) {
       const float m_new = raise ? mt : m;
-      const float factor = __builtin_amdgcn_exp2f(m - m_new);
+      const float factor = raise ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;  // m may be -inf
       m = m_new;
       l *= factor;
 #pragma unroll
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     // The row sum adds the same bf16 weights that multiply V (pairwise dot
     // products with ones), so numerator and denominator see identical P.
     bf16x8 pb[BN / 16];
-    const float nm = -m;
+    const float nm = m == -INFINITY ? 0.f : -m;   // a row that has seen no key yet
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -244,16 +253,16 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
 
 hipError_t launch_fwd(const bf16* qr, const bf16* kr, const bf16* v, TokenTables tt,
                       const PlanBufs& pb, const int32_t* status, int B, int S, int Hq, int Hkv,
-                      int D, float scale, bf16* o, float* lse, hipStream_t st) {
+                      int D, float scale, int anchor, bf16* o, float* lse, hipStream_t st) {
   const float scale_log2 = scale * 1.44269504088896340736f;
   const int n_items = B * pb.nq * Hq;
   const dim3 grid(padded_grid(n_items));
   if (D == 128) {
     hipLaunchKernelGGL(k_fwd<128>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
-                       pb.kpack, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, o, lse);
+                       pb.kpack, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, anchor, o, lse);
   } else {
     hipLaunchKernelGGL(k_fwd<64>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
-                       pb.kpack, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, o, lse);
+                       pb.kpack, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, anchor, o, lse);
   }
   return hipGetLastError();
 }

@@ -10,6 +10,13 @@
 // Because documents are contiguous segments, what query t sees besides the
 // anchor is one closed interval of keys [lo[t], hi[t]] (row-local); the tile
 // plan and the attention kernels use only these intervals.
+//
+// Two options follow the other paradigms of the page's Figure 2: continuous
+// position IDs (the row-local index, as in the page's "Core design" of
+// AnchorAttention and in standard intra-document attention), and rows
+// without an anchor (intra-document attention, Figure 2 left and middle),
+// where the row's first token is an ordinary document token and a query sees
+// only its own document.
 #include "aa_internal.h"
 
 namespace aa {
@@ -18,9 +25,12 @@ namespace aa {
 // position ID, visible-key interval, and validation of the segment layout.
 // Every derived index is clamped into the row so that later kernels stay in
 // bounds even when cu_doc_lens is invalid (the status word reports it).
+// mode 0: reset (a document's first token gets 1); 1: continuous (row-local
+// index).  anchor 0: no anchor, every token belongs to a document.
 __global__ void k_positions(const int32_t* __restrict__ cu, int n_seg, int B, int S, int causal,
-                            int mode, int32_t* __restrict__ pos, int32_t* __restrict__ lo,
-                            int32_t* __restrict__ hi, int32_t* __restrict__ status) {
+                            int mode, int anchor, int32_t* __restrict__ pos,
+                            int32_t* __restrict__ lo, int32_t* __restrict__ hi,
+                            int32_t* __restrict__ status) {
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)B * S;
   if (t < n_seg) {
@@ -38,16 +48,19 @@ __global__ void k_positions(const int32_t* __restrict__ cu, int n_seg, int B, in
   const long long s = cu[a], e = cu[a + 1];
   const long long rs = (t / S) * (long long)S;
   bool bad = !(s <= t && t < e && s >= rs && e <= rs + S);
-  if (t == rs && e != rs + 1) bad = true;          // the anchor is a segment of its own
-  if (t == rs + 1 && s != t) bad = true;           // so the next segment starts right after it
+  if (anchor) {
+    if (t == rs && e != rs + 1) bad = true;        // the anchor is a segment of its own
+    if (t == rs + 1 && s != t) bad = true;         // so the next segment starts right after it
+  }
   if (bad) status[0] = kStatusBadDocs;
   const int local = (int)(t - rs);
+  const int first = anchor ? 1 : 0;                // first row-local index of a document
   int p, l, h;
-  if (t == rs) {
+  if (anchor && t == rs) {
     p = 0; l = 1; h = 0;                           // anchor: sees only itself (column 0)
   } else {
     long long sl = s - rs, el = e - rs;            // row-local segment [sl, el)
-    sl = sl < 1 ? 1 : (sl > local ? local : sl);
+    sl = sl < first ? first : (sl > local ? local : sl);
     el = el > S ? S : (el <= local ? local + 1 : el);
     p = mode == 0 ? (int)(local - sl + 1) : local;
     l = (int)sl;
@@ -64,8 +77,8 @@ __global__ void k_positions(const int32_t* __restrict__ cu, int n_seg, int B, in
 // are seen; ANCHOR when it is key tile 0 and only column 0 is seen; PARTIAL
 // otherwise.  Also counts the live tiles of the query tile.
 __global__ void k_tile_kinds(const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
-                             int S, int BM, int BN, int nq, int nk, uint8_t* __restrict__ kinds,
-                             int32_t* __restrict__ cntq) {
+                             int S, int BM, int BN, int nq, int nk, int anchor,
+                             uint8_t* __restrict__ kinds, int32_t* __restrict__ cntq) {
   __shared__ int slo[256], shi[256];
   __shared__ int wcount[8];
   const int tile = blockIdx.x;            // b * nq + qt
@@ -89,13 +102,14 @@ __global__ void k_tile_kinds(const int32_t* __restrict__ lo, const int32_t* __re
     for (int r = 0; r < nrows; ++r) {
       const int a = max(slo[r], c0), z = min(shi[r], c1);
       const int ndoc = z >= a ? z - a + 1 : 0;
-      const int n = ndoc + (kt == 0 ? 1 : 0);
+      const int n = ndoc + (anchor && kt == 0 ? 1 : 0);
       any_live |= n > 0;
       any_doc |= ndoc > 0;
       all_full &= n == BN;
     }
     uint8_t kind = 0;
-    if (any_live) kind = all_full ? kTileFull : ((kt == 0 && !any_doc) ? kTileAnchor : kTilePartial);
+    if (any_live)
+      kind = all_full ? kTileFull : ((anchor && kt == 0 && !any_doc) ? kTileAnchor : kTilePartial);
     kinds[(size_t)tile * nk + kt] = kind;
     cnt += kind != 0;
   }
@@ -198,21 +212,21 @@ __global__ void k_row_compact(const uint8_t* __restrict__ m, int rows, int n,
 }
 
 hipError_t launch_positions(const int32_t* cu, int n_seg, int B, int S, int causal, int mode,
-                            TokenTables tt, int32_t* status, hipStream_t st) {
+                            int anchor, TokenTables tt, int32_t* status, hipStream_t st) {
   const long long total = (long long)B * S;
   const long long n = total > n_seg ? total : n_seg;
   const int threads = 256;
   const unsigned blocks = (unsigned)((n + threads - 1) / threads);
   hipLaunchKernelGGL(k_positions, dim3(blocks), dim3(threads), 0, st, cu, n_seg, B, S, causal,
-                     mode, tt.pos, tt.lo, tt.hi, status);
+                     mode, anchor, tt.pos, tt.lo, tt.hi, status);
   return hipGetLastError();
 }
 
-hipError_t launch_plan(const int32_t* lo, const int32_t* hi, int B, int S, PlanBufs pb,
+hipError_t launch_plan(const int32_t* lo, const int32_t* hi, int B, int S, int anchor, PlanBufs pb,
                        bool key_major, hipStream_t st) {
   const int nq = pb.nq, nk = pb.nk;
   hipLaunchKernelGGL(k_tile_kinds, dim3(B * nq), dim3(256), 0, st, lo, hi, S, pb.BM, pb.BN, nq,
-                     nk, pb.kinds, pb.cntq);
+                     nk, anchor, pb.kinds, pb.cntq);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pb.cntq, B * nq, pb.qptr, pb.n_live);
   hipLaunchKernelGGL(k_row_compact, dim3((B * nq + 3) / 4), dim3(256), 0, st, pb.kinds, B * nq, nk,
                      pb.qptr, pb.kidx, pb.kkind, pb.kpack);

@@ -31,8 +31,9 @@ __global__ void k_rope_table(int S, int half, RopeTheta th, float* __restrict__ 
 }
 
 // One thread per 8 consecutive features (4 pairs) of one (token, head).
+// Positions are clamped into the table's npos rows.
 __global__ void k_rope_apply(const bf16* __restrict__ x, const int32_t* __restrict__ pos,
-                             const float* __restrict__ table, long long n_chunks, int S, int H,
+                             const float* __restrict__ table, long long n_chunks, int npos, int H,
                              int D, bf16* __restrict__ y) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_chunks) return;
@@ -40,7 +41,7 @@ __global__ void k_rope_apply(const bf16* __restrict__ x, const int32_t* __restri
   const long long tok = i / chunks_per_tok;
   const int within = (int)(i % chunks_per_tok);
   const int d0 = (within % (D / 8)) * 8;
-  const int p = min(max(pos[tok], 0), S - 1);     // table rows exist for 0 <= pos < S
+  const int p = min(max(pos[tok], 0), npos - 1);  // table rows exist for 0 <= pos < npos
   const bf16x8 xv = *(const bf16x8*)(x + i * 8);
   const f32x4* tb = (const f32x4*)(table + ((size_t)p * (D / 2) + d0 / 2) * 2);
   const f32x4 cs01 = tb[0];   // cos0 sin0 cos1 sin1
@@ -65,12 +66,12 @@ hipError_t launch_rope_table(int S, int D, const RopeTheta& th, float* table, hi
   return hipGetLastError();
 }
 
-hipError_t launch_rope_apply(const bf16* x, const int32_t* pos, const float* table, int B, int S,
-                             int H, int D, bf16* x_rot, hipStream_t st) {
+hipError_t launch_rope_apply(const bf16* x, const int32_t* pos, const float* table, int npos, int B,
+                             int S, int H, int D, bf16* x_rot, hipStream_t st) {
   const long long n = (long long)B * S * H * D / 8;
   const int threads = 256;
   hipLaunchKernelGGL(k_rope_apply, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0,
-                     st, x, pos, table, n, S, H, D, x_rot);
+                     st, x, pos, table, n, npos, H, D, x_rot);
   return hipGetLastError();
 }
 

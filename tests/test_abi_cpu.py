@@ -72,8 +72,20 @@ def test_argument_errors_before_launch(lib):
     rc = lib.anchor_attn_bwd(fake, fake, fake, fake, fake, None, fake, 4, 1e4, 1, 1, 256, 4, 2, 128,
                              0.0, fake, fake, fake, fake, 1 << 40, None)
     assert rc == api.AA_EINVAL
-    rc = lib.anchor_attn_tile_plan(fake, 4, 1, 256, 48, 64, 1, fake, fake, fake, fake, fake, fake,
+    rc = lib.anchor_attn_tile_plan(fake, 4, 1, 256, 48, 64, 1, 0, fake, fake, fake, fake, fake, fake,
                                    fake, fake, 1 << 40, None)
     assert rc == api.AA_EUNSUPPORTED
+    # unknown option bits are rejected before anything is launched
+    rc = lib.anchor_attn_tile_plan(fake, 4, 1, 256, 64, 64, 1, 4, fake, fake, fake, fake, fake, fake,
+                                   fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    rc = lib.anchor_attn_fwd_ex(fake, fake, fake, fake, 4, 1e4, 1, 4, 1, 256, 4, 2, 128, 0.0,
+                                fake, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    rc = lib.anchor_attn_bwd_ex(fake, fake, fake, fake, fake, fake, fake, 4, 1e4, 1, 8, 1, 256, 4, 2,
+                                128, 0.0, fake, fake, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    rc = lib.anchor_attn_position_ids(fake, 4, 1, 256, 4, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
     rc = lib.anchor_attn_rope(fake, fake, 1, 256, 2, 80, 1e4, fake, fake, None)
     assert rc == api.AA_EUNSUPPORTED

@@ -58,6 +58,56 @@ def test_fwd_bwd_small_full_compare(gpu_lib, case):
     assert max(e) <= G_TOL, e
 
 
+def _mode_cases():
+    rng = np.random.default_rng(2025)
+    NA, CP = 2, 1     # FLAG_NO_ANCHOR, FLAG_CONTINUOUS_POS
+    return [
+        # name, B, S, Hq, Hkv, D, rows, base, causal, flags (rows cover S without an anchor)
+        ("noanchor_reset_gqa", 2, 1000, 4, 2, 128, [W.random_partition(rng, 1001, 30) for _ in range(2)], 5e6, True, NA),
+        ("noanchor_continuous", 1, 777, 2, 2, 64, [[100, 1, 676]], 1e4, True, NA | CP),
+        ("noanchor_one_doc", 1, 513, 2, 1, 128, [[513]], 5e6, True, NA),      # plain causal attention
+        ("noanchor_len1", 1, 300, 2, 2, 64, [[1] * 300], 1e4, True, NA),
+        ("noanchor_noncausal", 1, 600, 2, 2, 128, [[101, 1, 250, 248]], 1e4, False, NA),
+        ("noanchor_s1", 2, 1, 2, 2, 64, [[1], [1]], 1e4, True, NA),
+        ("anchor_continuous", 2, 1000, 4, 2, 128, [W.random_partition(rng, 1000, 30) for _ in range(2)], 5e6, True, CP),
+        ("anchor_continuous_mixed", 2, 640, 2, 2, 128, [[1, 300, 1, 337], [639]], 5e5, True, CP),
+    ]
+
+
+@pytest.mark.parametrize("case", _mode_cases(), ids=lambda c: c[0])
+def test_fwd_bwd_modes_full_compare(gpu_lib, case):
+    """The pages' other paradigms through the same kernels (options of the
+    *_ex entry points) against the oracle's matching modes."""
+    name, B, S, Hq, Hkv, D, rows, base, causal, flags = case
+    anchor = not flags & 2
+    mode = "continuous" if flags & 1 else "reset"
+    say(f"[modes] {name} B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} causal={causal} flags={flags}")
+    cu = W.cu_doc_lens_from_lengths(rows, S) if anchor else W.cu_doc_lens_no_anchor(rows, S)
+    q, k, v, do = _inputs(B, S, Hq, Hkv, D, 4321)
+    o, lse = gpu_lib.anchor_attn_fwd(q.cuda(), k.cuda(), v.cuda(), cu, base, causal, flags=flags)
+    o_ref, lse_ref, _, _ = oracle.forward(q, k, v, cu, base, causal, pos_mode=mode, anchor=anchor)
+    o_g = f64(o).reshape(B * S, Hq, D)
+    assert o_err(o_g, o_ref) <= O_TOL, o_err(o_g, o_ref)
+    lse_g = f64(lse).transpose(1, 0, 2).reshape(Hq, B * S)
+    assert np.abs(lse_g - lse_ref).max() <= LSE_TOL
+    dq, dk, dv = gpu_lib.anchor_attn_bwd(q.cuda(), k.cuda(), v.cuda(), o, lse, do.cuda(), cu, base,
+                                         causal, flags=flags)
+    dq_r, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, base, causal, pos_mode=mode, anchor=anchor)
+    g = (f64(dq).reshape(B * S, Hq, D), f64(dk).reshape(B * S, Hkv, D), f64(dv).reshape(B * S, Hkv, D))
+    if all(len(r) == r.count(1) for r in rows):
+        # Every query sees only itself: P = 1, so dS = dP - Dv = 0 and the
+        # exact dq, dk vanish.  A relative error is undefined there; the GPU's
+        # result must be rounding noise next to the O(1) entries of dv = dO.
+        assert np.abs(dq_r).max() < 1e-12 and np.abs(dk_r).max() < 1e-12
+        noise = max(np.abs(g[0]).max(), np.abs(g[1]).max())
+        say(f"[modes] {name} O {o_err(o_g, o_ref):.2e} |dq|,|dk| max {noise:.2e} dv {rel_frob(g[2], dv_r):.2e}")
+        assert noise <= 1e-3 and rel_frob(g[2], dv_r) <= G_TOL
+        return
+    e = (rel_frob(g[0], dq_r), rel_frob(g[1], dk_r), rel_frob(g[2], dv_r))
+    say(f"[modes] {name} O {o_err(o_g, o_ref):.2e} dq {e[0]:.2e} dk {e[1]:.2e} dv {e[2]:.2e}")
+    assert max(e) <= G_TOL, e
+
+
 def test_determinism(gpu_lib):
     B, S, Hq, Hkv, D = 2, 1000, 4, 2, 128
     rng = np.random.default_rng(3)
@@ -153,4 +203,63 @@ def test_full_size_sampled(gpu_lib, wname):
         e_dv = rel_frob(dv_g, dv_r[:, [g]])
     e_dq = rel_frob(dq_g, dq_r)
     say(f"[full] {wname} dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
+    assert max(e_dq, e_dk, e_dv) <= G_TOL
+
+
+@pytest.mark.parametrize("mode", ["intra_doc_reset", "full_causal", "anchor_continuous"])
+def test_full_size_sampled_modes(gpu_lib, mode):
+    """The 64K shape in the benchmark's baseline modes; sampled outputs.
+    intra_doc_reset: the 64K documents without an anchor; full_causal: the
+    whole row as one document without an anchor (plain causal attention)."""
+    w = W.get("64k")
+    B, S, Hq, Hkv, D = w.B, w.S, w.Hq, w.Hkv, w.D
+    if mode == "anchor_continuous":
+        flags, anchor, pos_mode = 1, True, "continuous"
+        cu = w.cu_doc_lens
+    elif mode == "intra_doc_reset":
+        flags, anchor, pos_mode = 2, False, "reset"
+        cu = W.cu_doc_lens_no_anchor(W.rows_without_anchor([list(r) for r in w.doc_rows]), S)
+    else:
+        flags, anchor, pos_mode = 2, False, "reset"
+        cu = W.cu_doc_lens_no_anchor([[S]] * B, S)
+    say(f"[full-modes] {mode} generating inputs")
+    q, k, v, do = W.make_tensors(B, S, Hq, Hkv, D, w.tensor_seed)
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    say(f"[full-modes] {mode} fwd+bwd on GPU")
+    o, lse = gpu_lib.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base, flags=flags)
+    dq, dk, dv = gpu_lib.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base, flags=flags)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    heads = [0, Hq - 1]
+    # uniformly drawn rows estimate the whole tensor's relative Frobenius
+    # error without bias; rows at document starts (few keys, cancelling dS
+    # terms) join the per-element forward check only
+    urows = np.sort(rng.choice(S, 48, replace=False))
+    rows = np.unique(np.concatenate([[0, 1, S - 1], cu[1:-1], cu[1:-1] - 1, urows]))[:160]
+    rows = rows[(rows >= 0) & (rows < S)]
+    say(f"[full-modes] {mode} oracle forward on {len(rows)} rows")
+    o_ref, lse_ref, _, _ = oracle.forward(q, k, v, cu, w.rope_base, heads=heads, rows=rows,
+                                          pos_mode=pos_mode, anchor=anchor)
+    o_g = f64(o).reshape(B * S, Hq, D)[rows][:, heads]
+    lse_g = f64(lse).transpose(1, 0, 2).reshape(Hq, B * S)[heads][:, rows]
+    say(f"[full-modes] {mode} O err {o_err(o_g, o_ref):.2e} lse err {np.abs(lse_g - lse_ref).max():.2e}")
+    assert o_err(o_g, o_ref) <= O_TOL
+    assert np.abs(lse_g - lse_ref).max() <= LSE_TOL
+    # key gradients need every query that sees the key: take keys near the end
+    # of the row (full causal) or in short documents
+    if mode == "full_causal":
+        keys = np.array(sorted(set([S - 1, S - 2] + list(rng.integers(S - 1500, S, 10)))))
+    else:
+        keys = _sample_keys(w, rng, 16) if anchor else np.array(
+            [int(x) for s_, e_ in zip(cu[:-1], cu[1:]) if e_ - s_ <= 2500 for x in (s_, e_ - 1)])[:16]
+    qrows = urows[:32]
+    say(f"[full-modes] {mode} oracle backward on {len(qrows)} rows, {len(keys)} keys")
+    dq_r, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, w.rope_base, heads=heads, q_rows=qrows,
+                                             k_cols=keys, pos_mode=pos_mode, anchor=anchor)
+    e_dq = rel_frob(f64(dq).reshape(B * S, Hq, D)[qrows][:, heads], dq_r)
+    # key gradients are exact sums over the chosen heads only when those are all
+    # of the group's heads; with MHA (Hq == Hkv) each head is its own group
+    e_dk = rel_frob(f64(dk).reshape(B * S, Hkv, D)[keys][:, heads], dk_r[:, heads])
+    e_dv = rel_frob(f64(dv).reshape(B * S, Hkv, D)[keys][:, heads], dv_r[:, heads])
+    say(f"[full-modes] {mode} dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
     assert max(e_dq, e_dk, e_dv) <= G_TOL

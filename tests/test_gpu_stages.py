@@ -39,6 +39,26 @@ def test_position_ids_bit_exact(gpu_lib, case):
         assert gpu_lib.anchor_attn_device_status(ws) == 0
 
 
+@pytest.mark.parametrize("case", _partitions(), ids=lambda c: c[0])
+def test_position_ids_bit_exact_without_anchor(gpu_lib, case):
+    name, B, S, rows = case
+    say(f"[positions] {name} without anchor B={B} S={S}")
+    cu = W.cu_doc_lens_no_anchor(W.rows_without_anchor(rows), S)
+    for flags, label in ((2, "reset"), (3, "continuous")):
+        pos, ws = gpu_lib.anchor_attn_position_ids(cu, B, S, flags)
+        ref = oracle.position_ids(cu, B, S, label, anchor=False)
+        assert np.array_equal(pos.cpu().numpy().astype(np.int64), ref)
+        assert gpu_lib.anchor_attn_device_status(ws) == 0
+
+
+def test_segment_crossing_rows_is_reported_without_anchor(gpu_lib):
+    S = 100
+    bad = np.array([0, 60, 130, 200], dtype=np.int32)        # [60, 130) crosses into row 1
+    pos, ws = gpu_lib.anchor_attn_position_ids(bad, 2, S, 2)
+    assert gpu_lib.anchor_attn_device_status(ws) == gpu_lib.AA_EDOCS
+    assert int(pos.min()) >= 0 and int(pos.max()) < S + 1    # clamped into the row
+
+
 def _cmp_plan(gp, ref, B):
     qptr = gp["qptr"].cpu().numpy()
     n = int(gp["n_live"].cpu().item())
@@ -61,6 +81,11 @@ def test_tile_plan_bit_exact_small(gpu_lib, case, tile):
     for causal in (True, False):
         gp = gpu_lib.anchor_attn_tile_plan(cu, B, S, BM, BN, causal)
         ref = oracle.tile_plan(cu, B, S, BM, BN, causal)
+        _cmp_plan(gp, ref, B)
+    cu_na = W.cu_doc_lens_no_anchor(W.rows_without_anchor(rows), S)
+    for causal in (True, False):
+        gp = gpu_lib.anchor_attn_tile_plan(cu_na, B, S, BM, BN, causal, flags=gpu_lib.FLAG_NO_ANCHOR)
+        ref = oracle.tile_plan(cu_na, B, S, BM, BN, causal, anchor=False)
         _cmp_plan(gp, ref, B)
 
 

@@ -28,7 +28,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "sample_doc_lengths", "cu_doc_lens_from_lengths", "cu_doc_lens_no_anchor",
+    "Workload", "WORKLOADS", "sample_doc_lengths", "cu_doc_lens_from_lengths", "cu_doc_lens_no_anchor", "rows_without_anchor",
     "make_tensors", "random_partition", "get",
 ]
 
@@ -74,6 +74,12 @@ def cu_doc_lens_no_anchor(rows: list[list[int]], S: int) -> np.ndarray:
         for L in lens:
             cu.append(cu[-1] + L)
     return np.asarray(cu, dtype=np.int32)
+
+
+def rows_without_anchor(rows: list[list[int]]) -> list[list[int]]:
+    """The same documents laid out without an anchor: the first document of
+    each row also takes the anchor's slot, so every row still holds S tokens."""
+    return [[lens[0] + 1] + list(lens[1:]) if len(lens) else [1] for lens in rows]
 
 
 def random_partition(rng: np.random.Generator, S: int, max_docs: int | None = None) -> list[int]:
