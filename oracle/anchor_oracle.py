@@ -34,6 +34,12 @@ Position: BFloat16 Breaks Down RoPE in Long-Context Training"):
 * The paper's own reading of AnchorAttention (arch page, "Core design
   (Figure 2, right)"): continuous document position IDs counting on from 1
   after the anchor; ``mode="continuous"``.
+* arch page §5 "AnchorAttention with Interleaved Chunks" and Figure 5
+  (middle, right): documents cut into chunks that are shuffled across the row,
+  each document keeping its own token order.  ``seg_doc`` gives the document
+  of every segment (chunk); chunks of one row with the same id form one
+  document, and a query sees the keys of its document (in every chunk) that
+  are not after it.
 
 Readings where the pages are silent (listed with reasons in the design notes):
 position IDs are reset per document (first document token = 1, anchor = 0);
@@ -88,21 +94,55 @@ def segment_ids(cu, B: int, S: int, anchor: bool = True) -> np.ndarray:
     return np.searchsorted(cu, t, side="right") - 1
 
 
-def position_ids(cu, B: int, S: int, mode: str = "reset", anchor: bool = True) -> np.ndarray:
+def document_ids(cu, B: int, S: int, anchor: bool = True, seg_doc=None) -> np.ndarray:
+    """A label per token, equal for two tokens exactly when they belong to the
+    same document.  Without ``seg_doc`` every segment is a document.  With it,
+    segment s belongs to document seg_doc[s] of its row (interleaved chunks);
+    the anchor segment carries id -1 and no other segment may."""
+    seg = segment_ids(cu, B, S, anchor)
+    if seg_doc is None:
+        return seg
+    seg_doc = np.asarray(seg_doc, dtype=np.int64)
+    cu = np.asarray(cu, dtype=np.int64)
+    if len(seg_doc) != len(cu) - 1:
+        raise ValueError("seg_doc needs one document id per segment")
+    starts = cu[:-1]
+    is_anchor_seg = (starts % S == 0) & (np.diff(cu) == 1) if anchor else np.zeros(len(starts), bool)
+    if anchor and np.any(seg_doc[is_anchor_seg] != -1):
+        raise ValueError("the anchor segment of every row must have document id -1")
+    if np.any(seg_doc[~is_anchor_seg] < 0):
+        raise ValueError("document ids must be >= 0 (-1 marks the anchor)")
+    row = np.asarray(starts // S, dtype=np.int64)
+    span = int(seg_doc.max()) + 2
+    label_of_seg = row * span + seg_doc + 1
+    return label_of_seg[seg]
+
+
+def position_ids(cu, B: int, S: int, mode: str = "reset", anchor: bool = True,
+                 seg_doc=None) -> np.ndarray:
     """Position ID of every token (arch page §3.4, Figure 2).
 
     reset:      anchor -> 0; document token t in segment [s, e) -> t - s + 1.
     continuous: anchor -> 0; document tokens count on from 1 across documents,
                 i.e. t - (row start).
     Without an anchor the row's first token is an ordinary document token:
-    reset gives it 1, continuous gives it 0 (t - row start).
+    reset gives it 1, continuous gives it 0 (t - row start).  With interleaved
+    chunks (``seg_doc``) reset counts the tokens of the same document before t,
+    across its chunks: t's rank in its document + 1.
     """
     cu = validate_cu(cu, B, S, anchor)
     seg = segment_ids(cu, B, S, anchor)
     t = np.arange(B * S, dtype=np.int64)
     row_start = (t // S) * S
     is_anchor = t == row_start
-    if mode == "reset":
+    if mode == "reset" and seg_doc is not None:
+        doc = document_ids(cu, B, S, anchor, seg_doc)
+        order = np.argsort(doc, kind="stable")            # tokens grouped by document, in order
+        first = np.searchsorted(doc[order], doc[order], side="left")
+        rank = np.empty_like(t)
+        rank[order] = np.arange(len(t)) - first
+        pos = rank + 1
+    elif mode == "reset":
         pos = t - cu[seg] + 1
     elif mode == "continuous":
         pos = t - row_start
@@ -152,14 +192,14 @@ def rope(x: np.ndarray, pos: np.ndarray, base: float, inverse: bool = False) -> 
 # The explicit mask
 # ----------------------------------------------------------------------------
 def allowed(cu, B: int, S: int, rows, cols, causal: bool = True,
-            anchor: bool = True) -> np.ndarray:
+            anchor: bool = True, seg_doc=None) -> np.ndarray:
     """Dense boolean mask block allowed[len(rows), len(cols)] (Mask construction).
 
     rows and cols are flattened token indices.  A query may see a key only in
     its own batch row; there it sees the row's anchor (unless anchor=False),
     and keys of its own document that are not in its future.
     """
-    seg = segment_ids(cu, B, S, anchor)
+    seg = document_ids(cu, B, S, anchor, seg_doc)
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
     anchor_of_row = (rows // S) * S
@@ -174,14 +214,14 @@ def allowed(cu, B: int, S: int, rows, cols, causal: bool = True,
 
 
 def unmasked_pairs(cu, B: int, S: int, causal: bool = True, block: int = 1024,
-                   anchor: bool = True) -> int:
+                   anchor: bool = True, seg_doc=None) -> int:
     """Number of allowed (query, key) pairs, counted on the explicit mask."""
     total = 0
     for b in range(B):
         cols = np.arange(b * S, (b + 1) * S)
         for r0 in range(0, S, block):
             rows = np.arange(b * S + r0, b * S + min(S, r0 + block))
-            total += int(allowed(cu, B, S, rows, cols, causal, anchor).sum())
+            total += int(allowed(cu, B, S, rows, cols, causal, anchor, seg_doc).sum())
     return total
 
 
@@ -204,7 +244,8 @@ def _blocks_of(rows: np.ndarray, S: int, block: int):
             yield int(b), rb[i:i + block]
 
 
-def _row_block_forward(qh, kr, vv, cu, B, S, rows_b, b, pos, base, scale, causal, anchor=True):
+def _row_block_forward(qh, kr, vv, cu, B, S, rows_b, b, pos, base, scale, causal, anchor=True,
+                       seg_doc=None):
     """Logits, probabilities, output and log-sum-exp for a block of query rows."""
     qr = rope(qh[rows_b - b * S], pos[rows_b], base)               # [R, D]
     # Under the causal rule every key after the block's last query is masked
@@ -212,7 +253,7 @@ def _row_block_forward(qh, kr, vv, cu, B, S, rows_b, b, pos, base, scale, causal
     ncols = int(rows_b.max() - b * S + 1) if causal else S
     cols = np.arange(b * S, b * S + ncols)
     s = scale * (qr @ kr[:ncols].T)                                 # [R, ncols]
-    m_allowed = allowed(cu, B, S, rows_b, cols, causal, anchor)
+    m_allowed = allowed(cu, B, S, rows_b, cols, causal, anchor, seg_doc)
     s = np.where(m_allowed, s, -np.inf)
     m = s.max(axis=1)
     p = np.exp(s - m[:, None])
@@ -225,11 +266,12 @@ def _row_block_forward(qh, kr, vv, cu, B, S, rows_b, b, pos, base, scale, causal
 
 def forward(q, k, v, cu, rope_base: float, causal: bool = True, scale: float | None = None,
             heads=None, rows=None, block: int = 512, pos_mode: str = "reset", pos=None,
-            anchor: bool = True):
+            anchor: bool = True, seg_doc=None):
     """O and LSE (float64) for the chosen q heads and flattened query rows.
 
     ``pos`` optionally overrides the position IDs (one per flattened token);
-    ``anchor=False`` computes the intra-document baselines without an anchor.
+    ``anchor=False`` computes the intra-document baselines without an anchor;
+    ``seg_doc`` (a document id per segment) describes interleaved chunks.
     Returns (o [len(rows), len(heads), D], lse [len(heads), len(rows)], rows, heads).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -238,7 +280,8 @@ def forward(q, k, v, cu, rope_base: float, causal: bool = True, scale: float | N
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
-    pos = position_ids(cu, B, S, pos_mode, anchor) if pos is None else np.asarray(pos, dtype=np.int64)
+    pos = (position_ids(cu, B, S, pos_mode, anchor, seg_doc) if pos is None
+           else np.asarray(pos, dtype=np.int64))
     heads = list(range(Hq)) if heads is None else list(heads)
     rows = np.arange(B * S) if rows is None else np.unique(np.asarray(rows, dtype=np.int64))
     where = {int(r): n for n, r in enumerate(rows)}
@@ -253,7 +296,7 @@ def forward(q, k, v, cu, rope_base: float, causal: bool = True, scale: float | N
             kr = kr_of[b]
             vv = v[b, :, g, :]
             _, _, _, _, ob, lb = _row_block_forward(q[b, :, h, :], kr, vv, cu, B, S, rb, b, pos,
-                                                     rope_base, scale, causal, anchor)
+                                                     rope_base, scale, causal, anchor, seg_doc)
             idx = [where[int(r)] for r in rb]
             o[idx, hi, :] = ob
             lse[hi, idx] = lb
@@ -262,7 +305,7 @@ def forward(q, k, v, cu, rope_base: float, causal: bool = True, scale: float | N
 
 def backward(q, k, v, do, cu, rope_base: float, causal: bool = True, scale: float | None = None,
              heads=None, q_rows=None, k_cols=None, block: int = 512, pos_mode: str = "reset",
-             pos=None, anchor: bool = True):
+             pos=None, anchor: bool = True, seg_doc=None):
     """Analytic gradients (float64) of sum(O * dO) with respect to q, k, v.
 
     dV_j = sum_i P_ij dO_i;  dP_ij = dO_i . v_j;  Dv_i = dO_i . O_i;
@@ -277,7 +320,8 @@ def backward(q, k, v, do, cu, rope_base: float, causal: bool = True, scale: floa
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
-    pos = position_ids(cu, B, S, pos_mode, anchor) if pos is None else np.asarray(pos, dtype=np.int64)
+    pos = (position_ids(cu, B, S, pos_mode, anchor, seg_doc) if pos is None
+           else np.asarray(pos, dtype=np.int64))
     heads = list(range(Hq)) if heads is None else list(heads)
     q_rows = np.arange(B * S) if q_rows is None else np.unique(np.asarray(q_rows, dtype=np.int64))
     k_cols = np.arange(B * S) if k_cols is None else np.unique(np.asarray(k_cols, dtype=np.int64))
@@ -294,7 +338,7 @@ def backward(q, k, v, do, cu, rope_base: float, causal: bool = True, scale: floa
         kc = k_cols[k_cols // S == b]
         for r0 in range(0, S, 2048):
             rr = np.arange(b * S + r0, b * S + min(S, r0 + 2048))
-            hit = allowed(cu, B, S, rr, kc, causal, anchor).any(axis=1)
+            hit = allowed(cu, B, S, rr, kc, causal, anchor, seg_doc).any(axis=1)
             need.update(int(x) for x in rr[hit])
     need_rows = np.array(sorted(need), dtype=np.int64)
 
@@ -307,7 +351,8 @@ def backward(q, k, v, do, cu, rope_base: float, causal: bool = True, scale: floa
             kr = kr_of[b]
             vv = v[b, :, g, :]
             qr, cols, m_allowed, p, o, _ = _row_block_forward(q[b, :, h, :], kr, vv, cu, B, S, rb, b,
-                                                               pos, rope_base, scale, causal, anchor)
+                                                               pos, rope_base, scale, causal, anchor,
+                                                               seg_doc)
             dob = do[b, rb - b * S, h, :]                                # [R, D]
             dv_i = np.sum(dob * o, axis=1)                              # Dv
             dp = dob @ vv[:len(cols)].T

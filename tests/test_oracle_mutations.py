@@ -32,8 +32,12 @@ MUTANTS = [
     ("no-anchor first token at position 0", "    if anchor:\n        pos = np.where(is_anchor, 0, pos)",
      "    if True:\n        pos = np.where(is_anchor, 0, pos)"),
     ("continuous positions off by one", "        pos = t - row_start\n", "        pos = t - row_start + 1\n"),
+    ("interleaved reset rank off by one", "        pos = rank + 1\n", "        pos = rank\n"),
+    ("interleaved chunks ignored", "    if seg_doc is None:\n        return seg", "    if True:\n        return seg"),
+    ("document label without its row", "    label_of_seg = row * span + seg_doc + 1",
+     "    label_of_seg = seg_doc + 1"),
 ]
-PIN_FILES = ("test_oracle_pins.py", "test_oracle_modes.py")
+PIN_FILES = ("test_oracle_pins.py", "test_oracle_modes.py", "test_oracle_interleaved.py")
 
 
 @pytest.mark.slow

@@ -28,7 +28,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "sample_doc_lengths", "cu_doc_lens_from_lengths", "cu_doc_lens_no_anchor", "rows_without_anchor",
+    "Workload", "WORKLOADS", "sample_doc_lengths", "cu_doc_lens_from_lengths", "cu_doc_lens_no_anchor", "rows_without_anchor", "interleaved_chunks",
     "make_tensors", "random_partition", "get",
 ]
 
@@ -80,6 +80,39 @@ def rows_without_anchor(rows: list[list[int]]) -> list[list[int]]:
     """The same documents laid out without an anchor: the first document of
     each row also takes the anchor's slot, so every row still holds S tokens."""
     return [[lens[0] + 1] + list(lens[1:]) if len(lens) else [1] for lens in rows]
+
+
+def interleaved_chunks(rows: list[list[int]], S: int, rng: np.random.Generator,
+                       max_chunks_per_doc: int = 4, anchor: bool = True):
+    """Interleaved-chunk packing (documents cut at random points, the chunks of
+    a row shuffled with every document keeping its own order): each document of
+    length L is cut into min(L, 1 + integers(max_chunks_per_doc)) chunks, then
+    the rows are assembled by repeatedly taking the next chunk of a randomly
+    chosen document that still has chunks.  Returns (cu, chunk_doc): segment
+    offsets over the flattened B*S stream and a document id per segment, the
+    anchor segment (when ``anchor``) getting id -1."""
+    cu = [0]
+    doc_ids = []
+    for b, lens in enumerate(rows):
+        if sum(lens) != (S - 1 if anchor else S):
+            raise ValueError(f"row {b}: document lengths do not fill the row")
+        pending = []
+        for d, L in enumerate(lens):
+            n = int(min(L, 1 + rng.integers(max_chunks_per_doc)))
+            cuts = np.sort(rng.choice(np.arange(1, L), size=n - 1, replace=False)) if n > 1 else []
+            edges = [0, *[int(c) for c in cuts], L]
+            pending.append([d, [edges[i + 1] - edges[i] for i in range(n)]])
+        if anchor:
+            cu.append(cu[-1] + 1)
+            doc_ids.append(-1)
+        while pending:
+            i = int(rng.integers(len(pending)))
+            d, chunks = pending[i]
+            cu.append(cu[-1] + chunks.pop(0))
+            doc_ids.append(d)
+            if not chunks:
+                pending.pop(i)
+    return np.asarray(cu, dtype=np.int32), np.asarray(doc_ids, dtype=np.int32)
 
 
 def random_partition(rng: np.random.Generator, S: int, max_docs: int | None = None) -> list[int]:
