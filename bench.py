@@ -106,6 +106,9 @@ MODES = {
     "intra_doc_reset": (2, False, False),
     "intra_doc_continuous": (3, False, False),
     "full_causal": (2, False, True),
+    # AnchorAttention on the same documents cut into up to 4 chunks each and
+    # interleaved across the row (the pages' Figure 5, right)
+    "interleaved": (0, True, False),
 }
 
 
@@ -139,8 +142,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--mode", default="anchor", choices=sorted(MODES),
                     help="anchor (default, the method) | anchor_continuous | intra_doc_reset | "
-                         "intra_doc_continuous | full_causal: the pages' other attention paradigms "
-                         "through the same kernels, on the same documents")
+                         "intra_doc_continuous | full_causal | interleaved: the pages' other "
+                         "attention paradigms through the same kernels, on the same documents")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
@@ -166,6 +169,16 @@ def main() -> int:
     cu = torch.from_numpy(cu_np).to(dev)
     ws_f = torch.empty(api.workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, False), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(api.workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, True), dtype=torch.uint8, device=dev)
+    chunk_doc = None
+    if args.mode == "interleaved":
+        import numpy as np
+        cu_np, cd_np = workloads.interleaved_chunks(doc_rows, w.S, np.random.default_rng(64), 4, True)
+        cu = torch.from_numpy(cu_np).to(dev)
+        chunk_doc = torch.from_numpy(cd_np).to(dev)
+        ws_f = torch.empty(api.chunks_workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, len(cd_np), False),
+                           dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(api.chunks_workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, len(cd_np), True),
+                           dtype=torch.uint8, device=dev)
 
     # Events between the forward and the backward call of every step split
     # the step time; they are on the same stream as the calls.
@@ -173,10 +186,17 @@ def main() -> int:
              for _ in range(args.steps)]
 
     def step(mark=None):
-        o, lse = api.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base, True, None, ws_f, flags=flags)
+        if chunk_doc is not None:
+            o, lse = api.anchor_attn_fwd_chunks(qc, kc, vc, cu, chunk_doc, w.rope_base, True, None,
+                                                ws_f, flags=flags)
+        else:
+            o, lse = api.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base, True, None, ws_f, flags=flags)
         if mark is not None:
             mark[0].record()
-        if w.backward:
+        if w.backward and chunk_doc is not None:
+            api.anchor_attn_bwd_chunks(qc, kc, vc, o, lse, doc, cu, chunk_doc, w.rope_base, True,
+                                       None, ws_b, flags=flags)
+        elif w.backward:
             api.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base, True, None, ws_b,
                                 flags=flags)
         if mark is not None:

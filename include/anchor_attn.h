@@ -138,6 +138,49 @@ aa_status anchor_attn_bwd_ex(const void* q, const void* k, const void* v, const 
                              void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 
+/* ---- interleaved document chunks -----------------------------------------
+ * Arch page §5, "AnchorAttention with Interleaved Chunks" (Figure 5 middle
+ * and right): documents are cut into chunks shuffled across a row, every
+ * document keeping its own token order.  A query sees its row's anchor (unless
+ * AA_FLAG_NO_ANCHOR) and the keys of its own document, in any chunk, that are
+ * not after it (or all of them, causal = 0).  Reset position IDs count the
+ * document's tokens before the query across its chunks (+1); continuous IDs
+ * are the row-local index t - b*S.
+ *   cu_chunks  int32 [n_chunks + 1] (device): chunk boundaries over the
+ *              flattened B*S stream, cu_chunks[0] = 0, strictly increasing,
+ *              cu_chunks[n_chunks] = B*S; no chunk crosses a row.
+ *   chunk_doc  int32 [n_chunks] (device): document id of every chunk; chunks
+ *              of one row with the same id form one document.  With an anchor
+ *              the first chunk of every row is the one-token anchor with id -1
+ *              (and no other chunk has -1); otherwise every id is >= 0.
+ * At most 4096 chunks per row.  A row that breaks these rules is reported
+ * through the device status word (AA_EDOCS) and its outputs are NaN.
+ * Layouts, scale, flags and errors as for anchor_attn_fwd_ex / _bwd_ex; the
+ * workspace size comes from anchor_attn_chunks_workspace_size (for_bwd 0/1).
+ * The library runs the block-sparse kernels on every row permuted so that
+ * each document is contiguous (the order inside a document is kept, so the
+ * mask is unchanged) and scatters the results back. */
+size_t anchor_attn_chunks_workspace_size(int B, int S, int Hq, int Hkv, int D, int n_chunks,
+                                         int for_bwd);
+aa_status anchor_attn_fwd_chunks(const void* q, const void* k, const void* v,
+                                 const int32_t* cu_chunks, const int32_t* chunk_doc, int n_chunks,
+                                 double rope_base, int causal, int flags, int B, int S, int Hq,
+                                 int Hkv, int D, float softmax_scale, void* o, float* lse,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream);
+aa_status anchor_attn_bwd_chunks(const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, const void* dout, const int32_t* cu_chunks,
+                                 const int32_t* chunk_doc, int n_chunks, double rope_base,
+                                 int causal, int flags, int B, int S, int Hq, int Hkv, int D,
+                                 float softmax_scale, void* dq, void* dk, void* dv,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream);
+/* Stage entry point of the chunk layout, for bit-exact tests: src int32 [B*S]
+ * receives, for every token p of the permuted rows, the original token it
+ * came from; pos int32 [B*S] the position ID of permuted token p.  workspace:
+ * anchor_attn_chunks_workspace_size(B, S, 1, 1, 64, n_chunks, 0) bytes. */
+aa_status anchor_attn_chunk_layout(const int32_t* cu_chunks, const int32_t* chunk_doc, int n_chunks,
+                                   int B, int S, int causal, int flags, int32_t* src, int32_t* pos,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Position IDs (arch page §3.4, Figure 2 middle: reset per document; the
  * anchor has ID 0, a document's first token ID 1).  pos: int32 [B*S].
  * flags: AA_FLAG_CONTINUOUS_POS gives the row-local index instead (document
@@ -197,7 +240,8 @@ aa_status anchor_attn_device_status(const void* workspace, hipStream_t stream, i
 enum {
   AA_K_STATUS = 0, AA_K_POSITIONS = 1, AA_K_PLAN = 2, AA_K_ROPE_TABLE = 3, AA_K_ROPE = 4,
   AA_K_FWD = 5, AA_K_BWD_PRE = 6, AA_K_BWD_DKDV = 7, AA_K_BWD_DQ = 8, AA_K_BWD_ANCHOR = 9,
-  AA_K_COUNT = 10
+  AA_K_CHUNKS = 10, AA_K_GATHER = 11,
+  AA_K_COUNT = 12
 };
 aa_status anchor_attn_profile_begin(int max_launches);
 aa_status anchor_attn_profile_end(double* ms, int32_t* count, int n);

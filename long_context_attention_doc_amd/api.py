@@ -27,13 +27,15 @@ DKV_TILE = (64, 128)
 EXPORTS = (
     "anchor_attn_strerror", "anchor_attn_version", "anchor_attn_workspace_size",
     "anchor_attn_fwd", "anchor_attn_bwd", "anchor_attn_fwd_ex", "anchor_attn_bwd_ex",
+    "anchor_attn_chunks_workspace_size", "anchor_attn_fwd_chunks", "anchor_attn_bwd_chunks",
+    "anchor_attn_chunk_layout",
     "anchor_attn_position_ids",
     "anchor_attn_plan_workspace_size", "anchor_attn_plan_capacity", "anchor_attn_tile_plan",
     "anchor_attn_rope", "anchor_attn_device_status", "anchor_attn_profile_begin",
     "anchor_attn_profile_end",
 )
 KERNEL_IDS = ("status", "positions", "plan", "rope_table", "rope", "fwd", "bwd_pre", "bwd_dkdv",
-              "bwd_dq", "bwd_anchor")
+              "bwd_dq", "bwd_anchor", "chunks", "gather")
 
 _lib = None
 
@@ -64,6 +66,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "anchor_attn_fwd_ex": (I, [P, P, P, P, I, D, I, I, I, I, I, I, I, F, P, P, P, Z, P]),
         "anchor_attn_bwd_ex": (I, [P, P, P, P, P, P, P, I, D, I, I, I, I, I, I, I, F, P, P, P, P, Z,
                                    P]),
+        "anchor_attn_chunks_workspace_size": (Z, [I, I, I, I, I, I, I]),
+        "anchor_attn_fwd_chunks": (I, [P, P, P, P, P, I, D, I, I, I, I, I, I, I, F, P, P, P, Z, P]),
+        "anchor_attn_bwd_chunks": (I, [P, P, P, P, P, P, P, P, I, D, I, I, I, I, I, I, I, F, P, P, P, P,
+                                       Z, P]),
+        "anchor_attn_chunk_layout": (I, [P, P, I, I, I, I, I, P, P, P, Z, P]),
         "anchor_attn_position_ids": (I, [P, I, I, I, I, P, P, Z, P]),
         "anchor_attn_plan_workspace_size": (Z, [I, I, I, I]),
         "anchor_attn_plan_capacity": (Z, [I, I, I, I]),
@@ -184,6 +191,83 @@ def anchor_attn_bwd(q, k, v, o, lse, dout, cu_doc_lens, rope_base: float, causal
                                    _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q.device)),
                "anchor_attn_bwd")
     return dq, dk, dv
+
+
+def chunks_workspace_size(B: int, S: int, Hq: int, Hkv: int, D: int, n_chunks: int,
+                          for_bwd: bool) -> int:
+    n = load().anchor_attn_chunks_workspace_size(B, S, Hq, Hkv, D, n_chunks, int(for_bwd))
+    if n == 0:
+        raise ValueError("unsupported shape")
+    return int(n)
+
+
+def anchor_attn_fwd_chunks(q, k, v, cu_chunks, chunk_doc, rope_base: float, causal: bool = True,
+                           softmax_scale: float | None = None, workspace: torch.Tensor | None = None,
+                           flags: int = 0):
+    """Forward pass over interleaved document chunks (cu_chunks [n+1], chunk_doc [n]
+    int32); returns (o, lse) in the caller's token order."""
+    lib = load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_bf16(n, t)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    cu = _dev_cu(cu_chunks, q.device)
+    cd = _dev_cu(chunk_doc, q.device)
+    if cd.numel() != cu.numel() - 1:
+        raise ValueError("chunk_doc needs one id per chunk")
+    ws_n = chunks_workspace_size(B, S, Hq, Hkv, D, cd.numel(), False)
+    if workspace is None or workspace.numel() < ws_n:
+        workspace = _workspace(ws_n, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _check(lib.anchor_attn_fwd_chunks(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), _ptr(cd), cd.numel(),
+                                      float(rope_base), int(bool(causal)), int(flags), B, S, Hq, Hkv,
+                                      D, float(softmax_scale or 0.0), _ptr(o), _ptr(lse),
+                                      _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "anchor_attn_fwd_chunks")
+    return o, lse
+
+
+def anchor_attn_bwd_chunks(q, k, v, o, lse, dout, cu_chunks, chunk_doc, rope_base: float,
+                           causal: bool = True, softmax_scale: float | None = None,
+                           workspace: torch.Tensor | None = None, flags: int = 0):
+    """Backward pass over interleaved document chunks; returns (dq, dk, dv)."""
+    lib = load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need_bf16(n, t)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, S) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B,Hq,S]")
+    cu = _dev_cu(cu_chunks, q.device)
+    cd = _dev_cu(chunk_doc, q.device)
+    ws_n = chunks_workspace_size(B, S, Hq, Hkv, D, cd.numel(), True)
+    if workspace is None or workspace.numel() < ws_n:
+        workspace = _workspace(ws_n, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib.anchor_attn_bwd_chunks(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                      _ptr(cu), _ptr(cd), cd.numel(), float(rope_base),
+                                      int(bool(causal)), int(flags), B, S, Hq, Hkv, D,
+                                      float(softmax_scale or 0.0), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "anchor_attn_bwd_chunks")
+    return dq, dk, dv
+
+
+def anchor_attn_chunk_layout(cu_chunks, chunk_doc, B: int, S: int, causal: bool = True,
+                             flags: int = 0, device="cuda"):
+    """(src, pos, workspace): for every token of the permuted rows its original
+    token and its position ID."""
+    lib = load()
+    cu = _dev_cu(cu_chunks, device)
+    cd = _dev_cu(chunk_doc, device)
+    src = torch.empty(B * S, dtype=torch.int32, device=device)
+    pos = torch.empty(B * S, dtype=torch.int32, device=device)
+    ws = _workspace(chunks_workspace_size(B, S, 1, 1, 64, cd.numel(), False), device)
+    _check(lib.anchor_attn_chunk_layout(_ptr(cu), _ptr(cd), cd.numel(), B, S, int(bool(causal)),
+                                        int(flags), _ptr(src), _ptr(pos), _ptr(ws), ws.numel(),
+                                        _stream(src.device)), "anchor_attn_chunk_layout")
+    return src, pos, ws
 
 
 def anchor_attn_position_ids(cu_doc_lens, B: int, S: int, flags: int = 0, device="cuda"):

@@ -39,6 +39,17 @@ struct TokenTables {
   int32_t* hi;
 };
 
+// Interleaved chunks: per-chunk placement in the permuted row and per-row
+// validity (k_chunk_layout), the permuted row's source tokens (k_chunk_tokens).
+constexpr int kMaxChunksPerRow = 4096;
+struct ChunkBufs {
+  int32_t* new_start;  // [n_chunks] chunk start in the permuted row (row-local)
+  int32_t* doc_start;  // [n_chunks] start of the chunk's document there
+  int32_t* doc_end;    // [n_chunks] end (exclusive) of the chunk's document there
+  int32_t* row_ok;     // [B] 1 when the row's chunks are valid
+  int32_t* src;        // [B*S] permuted token -> original token
+};
+
 // Buffers of one tile plan.
 struct PlanBufs {
   int BM, BN, nq, nk;
@@ -64,7 +75,14 @@ hipError_t launch_positions(const int32_t* cu, int n_seg, int B, int S, int caus
 hipError_t launch_plan(const int32_t* lo, const int32_t* hi, int B, int S, int anchor, PlanBufs pb,
                        bool key_major, hipStream_t st);
 hipError_t launch_rope_table(int S, int D, const RopeTheta& th, float* table, hipStream_t st);
-hipError_t launch_rope_apply(const bf16* x, const int32_t* pos, const float* table, int npos, int B, int S,
+hipError_t launch_chunk_layout(const int32_t* cu, const int32_t* chunk_doc, int n_chunks, int B,
+                               int S, int causal, int mode, int anchor, ChunkBufs cb,
+                               TokenTables tt, int32_t* status, hipStream_t st);
+hipError_t launch_move_rows(const bf16* x, const int32_t* src, int B, int S, int H, int D,
+                            bool scatter, bf16* y, hipStream_t st);
+hipError_t launch_move_lse(const float* x, const int32_t* src, int B, int H, int S, bool scatter,
+                           float* y, hipStream_t st);
+hipError_t launch_rope_apply(const bf16* x, const int32_t* src, const int32_t* pos, const float* table, int npos, int B, int S,
                              int H, int D, bf16* x_rot, hipStream_t st);
 hipError_t launch_fwd(const bf16* qr, const bf16* kr, const bf16* v, TokenTables tt,
                       const PlanBufs& pb, const int32_t* status, int B, int S, int Hq, int Hkv,

@@ -104,6 +104,46 @@ Layout layout(int B, int S, int Hq, int Hkv, int D, bool bwd) {
   return L;
 }
 
+// Extra workspace of the interleaved-chunk entry points, after the Layout.
+struct ChunkLayout {
+  size_t new_start, doc_start, doc_end, row_ok, src, vperm, operm, doperm, lseperm, dqp, dkp, dvp;
+  size_t total;
+};
+
+ChunkLayout chunk_layout(size_t base, int B, int S, int Hq, int Hkv, int D, int n_chunks,
+                         bool bwd) {
+  ChunkLayout C;
+  const size_t T = (size_t)B * S;
+  size_t o = up(base);
+  C.new_start = o; o = up(o + (size_t)n_chunks * 4);
+  C.doc_start = o; o = up(o + (size_t)n_chunks * 4);
+  C.doc_end = o;   o = up(o + (size_t)n_chunks * 4);
+  C.row_ok = o;    o = up(o + (size_t)B * 4);
+  C.src = o;       o = up(o + T * 4);
+  C.vperm = o;     o = up(o + T * Hkv * D * 2);
+  C.operm = o;     o = up(o + T * Hq * D * 2);
+  C.lseperm = o;   o = up(o + (size_t)B * Hq * S * 4);
+  C.doperm = C.dqp = C.dkp = C.dvp = 0;
+  if (bwd) {
+    C.doperm = o;  o = up(o + T * Hq * D * 2);
+    C.dqp = o;     o = up(o + T * Hq * D * 2);
+    C.dkp = o;     o = up(o + T * Hkv * D * 2);
+    C.dvp = o;     o = up(o + T * Hkv * D * 2);
+  }
+  C.total = o;
+  return C;
+}
+
+ChunkBufs chunk_bufs(const ChunkLayout& C, char* ws) {
+  ChunkBufs cb;
+  cb.new_start = (int32_t*)(ws + C.new_start);
+  cb.doc_start = (int32_t*)(ws + C.doc_start);
+  cb.doc_end = (int32_t*)(ws + C.doc_end);
+  cb.row_ok = (int32_t*)(ws + C.row_ok);
+  cb.src = (int32_t*)(ws + C.src);
+  return cb;
+}
+
 bool shape_ok(int B, int S, int Hq, int Hkv, int D) {
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq > 65535) return false;
   if (Hq % Hkv != 0) return false;
@@ -178,11 +218,48 @@ aa_status prologue(const Layout& L, char* ws, const void* q, const void* k,
   AA_LAUNCH(AA_K_ROPE_TABLE, st,
             launch_rope_table(S + 1, D, make_theta(D, rope_base), table, st));
   AA_LAUNCH(AA_K_ROPE, st,
-            launch_rope_apply((const bf16*)q, tt.pos, table, S + 1, B, S, Hq, D,
+            launch_rope_apply((const bf16*)q, nullptr, tt.pos, table, S + 1, B, S, Hq, D,
                               (bf16*)(ws + L.qrot), st));
   AA_LAUNCH(AA_K_ROPE, st,
-            launch_rope_apply((const bf16*)k, tt.pos, table, S + 1, B, S, Hkv, D,
+            launch_rope_apply((const bf16*)k, nullptr, tt.pos, table, S + 1, B, S, Hkv, D,
                               (bf16*)(ws + L.krot), st));
+  return AA_OK;
+}
+
+// The prologue of the interleaved-chunk entry points: the permuted layout of
+// every row (token tables in permuted order), plan(s), RoPE table, q and k
+// gathered and rotated in one pass, v gathered.
+aa_status prologue_chunks(const Layout& L, const ChunkLayout& C, char* ws, const void* q,
+                          const void* k, const void* v, const int32_t* cu,
+                          const int32_t* chunk_doc, int n_chunks, double rope_base, int causal,
+                          int flags, int B, int S, int Hq, int Hkv, int D, bool bwd,
+                          hipStream_t st) {
+  int32_t* status = (int32_t*)(ws + L.status);
+  TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
+  const int mode = (flags & AA_FLAG_CONTINUOUS_POS) ? 1 : 0;
+  const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
+  const ChunkBufs cb = chunk_bufs(C, ws);
+  AA_LAUNCH(AA_K_STATUS, st, launch_zero_status(status, st));
+  AA_LAUNCH(AA_K_CHUNKS, st,
+            launch_chunk_layout(cu, chunk_doc, n_chunks, B, S, causal, mode, anchor, cb, tt,
+                                status, st));
+  AA_LAUNCH(AA_K_PLAN, st,
+            launch_plan(tt.lo, tt.hi, B, S, anchor, plan_bufs(L.pq, ws), false, st));
+  if (bwd)
+    AA_LAUNCH(AA_K_PLAN, st,
+              launch_plan(tt.lo, tt.hi, B, S, anchor, plan_bufs(L.pk, ws), true, st));
+  float* table = (float*)(ws + L.table);
+  AA_LAUNCH(AA_K_ROPE_TABLE, st,
+            launch_rope_table(S + 1, D, make_theta(D, rope_base), table, st));
+  AA_LAUNCH(AA_K_ROPE, st,
+            launch_rope_apply((const bf16*)q, cb.src, tt.pos, table, S + 1, B, S, Hq, D,
+                              (bf16*)(ws + L.qrot), st));
+  AA_LAUNCH(AA_K_ROPE, st,
+            launch_rope_apply((const bf16*)k, cb.src, tt.pos, table, S + 1, B, S, Hkv, D,
+                              (bf16*)(ws + L.krot), st));
+  AA_LAUNCH(AA_K_GATHER, st,
+            launch_move_rows((const bf16*)v, cb.src, B, S, Hkv, D, false, (bf16*)(ws + C.vperm),
+                             st));
   return AA_OK;
 }
 
@@ -331,6 +408,146 @@ aa_status anchor_attn_bwd_ex(const void* q, const void* k, const void* v, const 
                   Hkv, D, softmax_scale, dq, dk, dv, workspace, ws_bytes, stream);
 }
 
+size_t anchor_attn_chunks_workspace_size(int B, int S, int Hq, int Hkv, int D, int n_chunks,
+                                         int for_bwd) {
+  if (!shape_ok(B, S, Hq, Hkv, D) || (D != 64 && D != 128) || n_chunks < B) return 0;
+  const Layout L = layout(B, S, Hq, Hkv, D, for_bwd != 0);
+  return chunk_layout(L.total, B, S, Hq, Hkv, D, n_chunks, for_bwd != 0).total;
+}
+
+static aa_status chunk_args_ok(const int32_t* cu, const int32_t* chunk_doc, int n_chunks, int flags,
+                               int B, int S, int Hq, int Hkv, int D, double rope_base) {
+  if (!cu || !chunk_doc) return AA_EINVAL;
+  if (!shape_ok(B, S, Hq, Hkv, D) || n_chunks < B) return AA_EINVAL;
+  if (D != 64 && D != 128) return AA_EUNSUPPORTED;
+  if (!flags_ok(flags)) return AA_EINVAL;
+  if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
+  if (!aligned(cu, 4) || !aligned(chunk_doc, 4)) return AA_EINVAL;
+  return AA_OK;
+}
+
+aa_status anchor_attn_fwd_chunks(const void* q, const void* k, const void* v,
+                                 const int32_t* cu_chunks, const int32_t* chunk_doc, int n_chunks,
+                                 double rope_base, int causal, int flags, int B, int S, int Hq,
+                                 int Hkv, int D, float softmax_scale, void* o, float* lse,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return AA_EINVAL;
+  const aa_status e = chunk_args_ok(cu_chunks, chunk_doc, n_chunks, flags, B, S, Hq, Hkv, D, rope_base);
+  if (e != AA_OK) return e;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, kAlign))
+    return AA_EINVAL;
+  const Layout L = layout(B, S, Hq, Hkv, D, false);
+  const ChunkLayout C = chunk_layout(L.total, B, S, Hq, Hkv, D, n_chunks, false);
+  if (ws_bytes < C.total) return AA_EWORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)D);
+  char* ws = (char*)workspace;
+  aa_status s = prologue_chunks(L, C, ws, q, k, v, cu_chunks, chunk_doc, n_chunks, rope_base,
+                                causal, flags, B, S, Hq, Hkv, D, false, stream);
+  if (s != AA_OK) return s;
+  TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
+  const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
+  const int32_t* src = (const int32_t*)(ws + C.src);
+  AA_LAUNCH(AA_K_FWD, stream,
+            launch_fwd((const bf16*)(ws + L.qrot), (const bf16*)(ws + L.krot),
+                       (const bf16*)(ws + C.vperm), tt, plan_bufs(L.pq, ws),
+                       (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D, scale, anchor,
+                       (bf16*)(ws + C.operm), (float*)(ws + C.lseperm), stream));
+  AA_LAUNCH(AA_K_GATHER, stream,
+            launch_move_rows((const bf16*)(ws + C.operm), src, B, S, Hq, D, true, (bf16*)o, stream));
+  AA_LAUNCH(AA_K_GATHER, stream,
+            launch_move_lse((const float*)(ws + C.lseperm), src, B, Hq, S, true, lse, stream));
+  return AA_OK;
+}
+
+aa_status anchor_attn_bwd_chunks(const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, const void* dout, const int32_t* cu_chunks,
+                                 const int32_t* chunk_doc, int n_chunks, double rope_base,
+                                 int causal, int flags, int B, int S, int Hq, int Hkv, int D,
+                                 float softmax_scale, void* dq, void* dk, void* dv,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return AA_EINVAL;
+  const aa_status e = chunk_args_ok(cu_chunks, chunk_doc, n_chunks, flags, B, S, Hq, Hkv, D, rope_base);
+  if (e != AA_OK) return e;
+  const void* ptrs16[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : ptrs16)
+    if (!aligned(p, 16)) return AA_EINVAL;
+  if (!aligned(lse, 4) || !aligned(workspace, kAlign)) return AA_EINVAL;
+  const Layout L = layout(B, S, Hq, Hkv, D, true);
+  const ChunkLayout C = chunk_layout(L.total, B, S, Hq, Hkv, D, n_chunks, true);
+  if (ws_bytes < C.total) return AA_EWORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)D);
+  char* ws = (char*)workspace;
+  aa_status s = prologue_chunks(L, C, ws, q, k, v, cu_chunks, chunk_doc, n_chunks, rope_base,
+                                causal, flags, B, S, Hq, Hkv, D, true, stream);
+  if (s != AA_OK) return s;
+  const int32_t* src = (const int32_t*)(ws + C.src);
+  AA_LAUNCH(AA_K_GATHER, stream,
+            launch_move_rows((const bf16*)o, src, B, S, Hq, D, false, (bf16*)(ws + C.operm), stream));
+  AA_LAUNCH(AA_K_GATHER, stream,
+            launch_move_rows((const bf16*)dout, src, B, S, Hq, D, false, (bf16*)(ws + C.doperm),
+                             stream));
+  AA_LAUNCH(AA_K_GATHER, stream,
+            launch_move_lse(lse, src, B, Hq, S, false, (float*)(ws + C.lseperm), stream));
+  BwdArgs a;
+  a.qr = (const bf16*)(ws + L.qrot);
+  a.kr = (const bf16*)(ws + L.krot);
+  a.v = (const bf16*)(ws + C.vperm);
+  a.o = (const bf16*)(ws + C.operm);
+  a.dout = (const bf16*)(ws + C.doperm);
+  a.lse = (const float*)(ws + C.lseperm);
+  a.table = (const float*)(ws + L.table);
+  a.tt = TokenTables{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
+  a.status = (const int32_t*)(ws + L.status);
+  a.dvec = (float*)(ws + L.dvec);
+  a.ds0 = (float*)(ws + L.ds0);
+  a.part_dk = (float*)(ws + L.pdk);
+  a.part_dv = (float*)(ws + L.pdv);
+  a.qstats = (float*)(ws + L.qstats);
+  a.nblk = L.nblk;
+  a.dq = (bf16*)(ws + C.dqp);
+  a.dk = (bf16*)(ws + C.dkp);
+  a.dv = (bf16*)(ws + C.dvp);
+  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
+  a.scale = scale;
+  a.anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
+  AA_LAUNCH(AA_K_BWD_PRE, stream, launch_bwd_pre(a, stream));
+  AA_LAUNCH(AA_K_BWD_DKDV, stream, launch_bwd_dkdv(a, plan_bufs(L.pk, ws), stream));
+  AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
+  if (a.anchor) AA_LAUNCH(AA_K_BWD_ANCHOR, stream, launch_bwd_anchor(a, stream));
+  AA_LAUNCH(AA_K_GATHER, stream,
+            launch_move_rows(a.dq, src, B, S, Hq, D, true, (bf16*)dq, stream));
+  AA_LAUNCH(AA_K_GATHER, stream,
+            launch_move_rows(a.dk, src, B, S, Hkv, D, true, (bf16*)dk, stream));
+  AA_LAUNCH(AA_K_GATHER, stream,
+            launch_move_rows(a.dv, src, B, S, Hkv, D, true, (bf16*)dv, stream));
+  return AA_OK;
+}
+
+aa_status anchor_attn_chunk_layout(const int32_t* cu_chunks, const int32_t* chunk_doc, int n_chunks,
+                                   int B, int S, int causal, int flags, int32_t* src, int32_t* pos,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!src || !pos || !workspace) return AA_EINVAL;
+  const aa_status e = chunk_args_ok(cu_chunks, chunk_doc, n_chunks, flags, B, S, 1, 1, 64, 1.0);
+  if (e != AA_OK) return e;
+  if (!aligned(src, 4) || !aligned(pos, 4) || !aligned(workspace, kAlign)) return AA_EINVAL;
+  const size_t need = anchor_attn_chunks_workspace_size(B, S, 1, 1, 64, n_chunks, 0);
+  if (ws_bytes < need) return AA_EWORKSPACE;
+  char* ws = (char*)workspace;
+  const Layout L = layout(B, S, 1, 1, 64, false);
+  const ChunkLayout C = chunk_layout(L.total, B, S, 1, 1, 64, n_chunks, false);
+  int32_t* status = (int32_t*)(ws + L.status);
+  TokenTables tt{pos, (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
+  ChunkBufs cb = chunk_bufs(C, ws);
+  cb.src = src;
+  hipLaunchKernelGGL(k_zero_status, dim3(1), dim3(64), 0, stream, status);
+  AA_HIP(hipGetLastError());
+  AA_HIP(launch_chunk_layout(cu_chunks, chunk_doc, n_chunks, B, S, causal,
+                             (flags & AA_FLAG_CONTINUOUS_POS) ? 1 : 0,
+                             (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1, cb, tt, status, stream));
+  return AA_OK;
+}
+
 aa_status anchor_attn_position_ids(const int32_t* cu_doc_lens, int n_seg, int B, int S, int flags,
                                    int32_t* pos, void* workspace, size_t ws_bytes,
                                    hipStream_t stream) {
@@ -406,7 +623,7 @@ aa_status anchor_attn_rope(const void* x, const int32_t* pos, int B, int S, int 
   if (!aligned(x, 16) || !aligned(x_rot, 16) || !aligned(table, 16) || !aligned(pos, 4))
     return AA_EINVAL;
   AA_HIP(launch_rope_table(S, D, make_theta(D, rope_base), table, stream));
-  AA_HIP(launch_rope_apply((const bf16*)x, pos, table, S, B, S, H, D, (bf16*)x_rot, stream));
+  AA_HIP(launch_rope_apply((const bf16*)x, nullptr, pos, table, S, B, S, H, D, (bf16*)x_rot, stream));
   return AA_OK;
 }
 

@@ -31,10 +31,11 @@ __global__ void k_rope_table(int S, int half, RopeTheta th, float* __restrict__ 
 }
 
 // One thread per 8 consecutive features (4 pairs) of one (token, head).
-// Positions are clamped into the table's npos rows.
-__global__ void k_rope_apply(const bf16* __restrict__ x, const int32_t* __restrict__ pos,
-                             const float* __restrict__ table, long long n_chunks, int npos, int H,
-                             int D, bf16* __restrict__ y) {
+// Positions are clamped into the table's npos rows.  With src, output token
+// p takes its input from token src[p] (a gather fused into the rotation).
+__global__ void k_rope_apply(const bf16* __restrict__ x, const int32_t* __restrict__ src,
+                             const int32_t* __restrict__ pos, const float* __restrict__ table,
+                             long long n_chunks, int npos, int H, int D, bf16* __restrict__ y) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_chunks) return;
   const int chunks_per_tok = H * D / 8;
@@ -42,7 +43,8 @@ __global__ void k_rope_apply(const bf16* __restrict__ x, const int32_t* __restri
   const int within = (int)(i % chunks_per_tok);
   const int d0 = (within % (D / 8)) * 8;
   const int p = min(max(pos[tok], 0), npos - 1);  // table rows exist for 0 <= pos < npos
-  const bf16x8 xv = *(const bf16x8*)(x + i * 8);
+  const long long in = src ? (long long)src[tok] * chunks_per_tok + within : i;
+  const bf16x8 xv = *(const bf16x8*)(x + in * 8);
   const f32x4* tb = (const f32x4*)(table + ((size_t)p * (D / 2) + d0 / 2) * 2);
   const f32x4 cs01 = tb[0];   // cos0 sin0 cos1 sin1
   const f32x4 cs23 = tb[1];
@@ -66,12 +68,13 @@ hipError_t launch_rope_table(int S, int D, const RopeTheta& th, float* table, hi
   return hipGetLastError();
 }
 
-hipError_t launch_rope_apply(const bf16* x, const int32_t* pos, const float* table, int npos, int B,
-                             int S, int H, int D, bf16* x_rot, hipStream_t st) {
+hipError_t launch_rope_apply(const bf16* x, const int32_t* src, const int32_t* pos,
+                             const float* table, int npos, int B, int S, int H, int D, bf16* x_rot,
+                             hipStream_t st) {
   const long long n = (long long)B * S * H * D / 8;
   const int threads = 256;
   hipLaunchKernelGGL(k_rope_apply, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0,
-                     st, x, pos, table, n, npos, H, D, x_rot);
+                     st, x, src, pos, table, n, npos, H, D, x_rot);
   return hipGetLastError();
 }
 

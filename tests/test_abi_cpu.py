@@ -87,5 +87,20 @@ def test_argument_errors_before_launch(lib):
     assert rc == api.AA_EINVAL
     rc = lib.anchor_attn_position_ids(fake, 4, 1, 256, 4, fake, fake, 1 << 40, None)
     assert rc == api.AA_EINVAL
+    # interleaved-chunk entry points: null chunk arrays, unknown flags, too few chunks
+    rc = lib.anchor_attn_fwd_chunks(fake, fake, fake, None, fake, 4, 1e4, 1, 0, 1, 256, 4, 2, 128,
+                                    0.0, fake, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    rc = lib.anchor_attn_fwd_chunks(fake, fake, fake, fake, fake, 4, 1e4, 1, 8, 1, 256, 4, 2, 128,
+                                    0.0, fake, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    rc = lib.anchor_attn_bwd_chunks(fake, fake, fake, fake, fake, fake, fake, fake, 1, 1e4, 1, 0, 2,
+                                    256, 4, 2, 128, 0.0, fake, fake, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    assert lib.anchor_attn_chunks_workspace_size(1, 256, 4, 2, 96, 4, 0) == 0
+    assert lib.anchor_attn_chunks_workspace_size(1, 256, 4, 2, 128, 4, 1) > \
+        lib.anchor_attn_workspace_size(1, 256, 4, 2, 128, 1)
+    rc = lib.anchor_attn_chunk_layout(fake, fake, 4, 1, 256, 1, 0, fake, fake, fake, 16, None)
+    assert rc == api.AA_EWORKSPACE
     rc = lib.anchor_attn_rope(fake, fake, 1, 256, 2, 80, 1e4, fake, fake, None)
     assert rc == api.AA_EUNSUPPORTED
