@@ -140,6 +140,9 @@ def main() -> int:
     ap.add_argument("--workload", default="64k",
                     help="tiny | 8k | 64k | 128k_gqa | short_docs (default: 64k, the headline)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--no-fwd-workspace", action="store_true",
+                    help="self-contained backward: rebuild positions, plan and rotated q, k "
+                         "instead of reusing the forward's workspace")
     ap.add_argument("--mode", default="anchor", choices=sorted(MODES),
                     help="anchor (default, the method) | anchor_continuous | intra_doc_reset | "
                          "intra_doc_continuous | full_causal | interleaved: the pages' other "
@@ -185,6 +188,14 @@ def main() -> int:
     marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(args.steps)]
 
+    # By default the step runs as the autograd function does: one workspace
+    # sized for the backward, which reuses the forward's positions, plan and
+    # rotated q, k (AA_FLAG_FWD_WORKSPACE).  Every step still computes them once.
+    reuse = chunk_doc is None and not args.no_fwd_workspace
+    if reuse:
+        ws_f = ws_b
+    bflags = flags | (api.FLAG_FWD_WORKSPACE if reuse else 0)
+
     def step(mark=None):
         if chunk_doc is not None:
             o, lse = api.anchor_attn_fwd_chunks(qc, kc, vc, cu, chunk_doc, w.rope_base, True, None,
@@ -198,7 +209,7 @@ def main() -> int:
                                        None, ws_b, flags=flags)
         elif w.backward:
             api.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base, True, None, ws_b,
-                                flags=flags)
+                                flags=bflags)
         if mark is not None:
             mark[1].record()
 
@@ -247,7 +258,8 @@ def main() -> int:
         "config": {"workload": w.name if args.mode == "anchor" else f"{w.name}_{args.mode}",
                    "mode": args.mode, "batch": w.B, "seq_len": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "rope_base": w.rope_base, "documents_per_row": len(doc_rows[0]),
-                   "backward": w.backward, "unmasked_pairs_per_head": fl["pairs_per_head"]},
+                   "backward": w.backward, "unmasked_pairs_per_head": fl["pairs_per_head"],
+                   "bwd_reuses_forward_workspace": reuse},
         "tokens_per_s": tokens / (ms * 1e-3),
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms if w.backward else None,

@@ -92,6 +92,17 @@ enum {
  * Unknown bits are rejected with AA_EINVAL. */
 #define AA_FLAG_CONTINUOUS_POS 1
 #define AA_FLAG_NO_ANCHOR 2
+/*   AA_FLAG_FWD_WORKSPACE  (anchor_attn_bwd_ex) the workspace still holds what
+ *       anchor_attn_fwd_ex left in it for the same q, k, cu_doc_lens,
+ *       rope_base, causal, other flags and shape: it was sized for the
+ *       backward (anchor_attn_workspace_size(..., for_bwd = 1)) and given to
+ *       the forward, and nothing wrote to it in between.  The backward then
+ *       reuses the forward's position IDs, query-major plan, RoPE table and
+ *       rotated q, k instead of rebuilding them (the forward's workspace
+ *       layout is a prefix of the backward's).  anchor_attn_fwd_ex ignores
+ *       it; the other entry points reject it.  If the promise does not hold
+ *       the results are wrong; nothing detects it. */
+#define AA_FLAG_FWD_WORKSPACE 4
 
 /* Human-readable text for a status code (static storage). */
 const char* anchor_attn_strerror(aa_status s);

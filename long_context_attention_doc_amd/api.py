@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libanchor_attn.so")
 AA_OK, AA_EINVAL, AA_EDOCS, AA_EUNSUPPORTED, AA_EWORKSPACE, AA_EHIP = range(6)
 # Options (anchor_attn.h): continuous position IDs; rows without a shared anchor.
 FLAG_CONTINUOUS_POS, FLAG_NO_ANCHOR = 1, 2
+# anchor_attn_bwd: the workspace still holds the forward's state (see anchor_attn.h)
+FLAG_FWD_WORKSPACE = 4
 TILE_FULL, TILE_PARTIAL, TILE_ANCHOR = 1, 2, 3
 
 # Tile shapes the attention kernels run with (query tile x key tile).
@@ -348,8 +350,13 @@ def profile_end() -> dict:
 class _AnchorAttnFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, cu, rope_base, causal, softmax_scale, flags):
-        o, lse = anchor_attn_fwd(q, k, v, cu, rope_base, causal, softmax_scale, flags=flags)
+        # one workspace sized for the backward: the backward reuses the
+        # forward's positions, plan and rotated q, k left in it
+        B, S, Hq, D = q.shape
+        ws = _workspace(workspace_size(B, S, Hq, k.shape[2], D, True), q.device)
+        o, lse = anchor_attn_fwd(q, k, v, cu, rope_base, causal, softmax_scale, ws, flags=flags)
         ctx.save_for_backward(q, k, v, o, lse, cu)
+        ctx.ws = ws
         ctx.cfg = (rope_base, causal, softmax_scale, flags)
         return o
 
@@ -358,7 +365,8 @@ class _AnchorAttnFn(torch.autograd.Function):
         q, k, v, o, lse, cu = ctx.saved_tensors
         rope_base, causal, scale, flags = ctx.cfg
         dq, dk, dv = anchor_attn_bwd(q, k, v, o, lse, do.contiguous(), cu, rope_base, causal, scale,
-                                     flags=flags)
+                                     ctx.ws, flags=flags | FLAG_FWD_WORKSPACE)
+        ctx.ws = None
         return dq, dk, dv, None, None, None, None, None
 
 

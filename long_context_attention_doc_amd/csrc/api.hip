@@ -289,8 +289,8 @@ size_t anchor_attn_workspace_size(int B, int S, int Hq, int Hkv, int D, int for_
   return layout(B, S, Hq, Hkv, D, for_bwd != 0).total;
 }
 
-static bool flags_ok(int flags) {
-  return (flags & ~(AA_FLAG_CONTINUOUS_POS | AA_FLAG_NO_ANCHOR)) == 0;
+static bool flags_ok(int flags, int extra = 0) {
+  return (flags & ~(AA_FLAG_CONTINUOUS_POS | AA_FLAG_NO_ANCHOR | extra)) == 0;
 }
 
 static aa_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* cu_doc_lens,
@@ -298,7 +298,7 @@ static aa_status fwd_impl(const void* q, const void* k, const void* v, const int
                           int Hkv, int D, float softmax_scale, void* o, float* lse,
                           void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !cu_doc_lens || !o || !lse || !workspace) return AA_EINVAL;
-  if (!flags_ok(flags)) return AA_EINVAL;
+  if (!flags_ok(flags, AA_FLAG_FWD_WORKSPACE)) return AA_EINVAL;
   if (!shape_ok(B, S, Hq, Hkv, D) || n_seg < B) return AA_EINVAL;
   if (D != 64 && D != 128) return AA_EUNSUPPORTED;
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
@@ -328,7 +328,7 @@ static aa_status bwd_impl(const void* q, const void* k, const void* v, const voi
                           void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !dout || !cu_doc_lens || !dq || !dk || !dv || !workspace)
     return AA_EINVAL;
-  if (!flags_ok(flags)) return AA_EINVAL;
+  if (!flags_ok(flags, AA_FLAG_FWD_WORKSPACE)) return AA_EINVAL;
   if (!shape_ok(B, S, Hq, Hkv, D) || n_seg < B) return AA_EINVAL;
   if (D != 64 && D != 128) return AA_EUNSUPPORTED;
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
@@ -340,9 +340,19 @@ static aa_status bwd_impl(const void* q, const void* k, const void* v, const voi
   if (ws_bytes < L.total) return AA_EWORKSPACE;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)D);
   char* ws = (char*)workspace;
-  aa_status s = prologue(L, ws, q, k, cu_doc_lens, n_seg, rope_base, causal, flags, B, S, Hq,
-                         Hkv, D, true, stream);
-  if (s != AA_OK) return s;
+  if (flags & AA_FLAG_FWD_WORKSPACE) {
+    // the forward's status word, token tables, query-major plan, RoPE table
+    // and rotated q, k are still in place (the forward's layout is a prefix of
+    // this one); only the key-major plan is new
+    const TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
+    const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
+    AA_LAUNCH(AA_K_PLAN, stream,
+              launch_plan(tt.lo, tt.hi, B, S, anchor, plan_bufs(L.pk, ws), true, stream));
+  } else {
+    aa_status s = prologue(L, ws, q, k, cu_doc_lens, n_seg, rope_base, causal, flags, B, S, Hq,
+                           Hkv, D, true, stream);
+    if (s != AA_OK) return s;
+  }
   BwdArgs a;
   a.qr = (const bf16*)(ws + L.qrot);
   a.kr = (const bf16*)(ws + L.krot);

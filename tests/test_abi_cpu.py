@@ -79,8 +79,14 @@ def test_argument_errors_before_launch(lib):
     rc = lib.anchor_attn_tile_plan(fake, 4, 1, 256, 64, 64, 1, 4, fake, fake, fake, fake, fake, fake,
                                    fake, fake, 1 << 40, None)
     assert rc == api.AA_EINVAL
-    rc = lib.anchor_attn_fwd_ex(fake, fake, fake, fake, 4, 1e4, 1, 4, 1, 256, 4, 2, 128, 0.0,
+    rc = lib.anchor_attn_fwd_ex(fake, fake, fake, fake, 4, 1e4, 1, 8, 1, 256, 4, 2, 128, 0.0,
                                 fake, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    # the forward-workspace promise is only for the forward/backward pair
+    rc = lib.anchor_attn_position_ids(fake, 4, 1, 256, 4, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    rc = lib.anchor_attn_fwd_chunks(fake, fake, fake, fake, fake, 4, 1e4, 1, 4, 1, 256, 4, 2, 128,
+                                    0.0, fake, fake, fake, 1 << 40, None)
     assert rc == api.AA_EINVAL
     rc = lib.anchor_attn_bwd_ex(fake, fake, fake, fake, fake, fake, fake, 4, 1e4, 1, 8, 1, 256, 4, 2,
                                 128, 0.0, fake, fake, fake, fake, 1 << 40, None)

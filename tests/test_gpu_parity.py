@@ -122,6 +122,24 @@ def test_determinism(gpu_lib):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("flags", [0, 2], ids=["anchor", "no_anchor"])
+def test_backward_reusing_the_forward_workspace(gpu_lib, flags):
+    """AA_FLAG_FWD_WORKSPACE: the backward on the forward's workspace gives
+    bit-identical gradients to a self-contained backward."""
+    B, S, Hq, Hkv, D = 2, 1000, 4, 2, 128
+    rng = np.random.default_rng(31)
+    rows = [W.random_partition(rng, S if flags == 0 else S + 1, 20) for _ in range(B)]
+    cu = W.cu_doc_lens_from_lengths(rows, S) if flags == 0 else W.cu_doc_lens_no_anchor(rows, S)
+    q, k, v, do = (t.cuda() for t in _inputs(B, S, Hq, Hkv, D, 55))
+    ws = torch.empty(gpu_lib.workspace_size(B, S, Hq, Hkv, D, True), dtype=torch.uint8, device="cuda")
+    o, lse = gpu_lib.anchor_attn_fwd(q, k, v, cu, 5e6, workspace=ws, flags=flags)
+    g_reuse = gpu_lib.anchor_attn_bwd(q, k, v, o, lse, do, cu, 5e6, workspace=ws,
+                                      flags=flags | gpu_lib.FLAG_FWD_WORKSPACE)
+    g_self = gpu_lib.anchor_attn_bwd(q, k, v, o, lse, do, cu, 5e6, flags=flags)
+    for a, b in zip(g_reuse, g_self):
+        assert torch.equal(a, b)
+
+
 def test_autograd_function(gpu_lib):
     B, S, Hq, Hkv, D = 1, 400, 2, 2, 64
     cu = W.cu_doc_lens_from_lengths([[199, 200]], S)
