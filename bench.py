@@ -185,8 +185,7 @@ def main() -> int:
 
     # Events between the forward and the backward call of every step split
     # the step time; they are on the same stream as the calls.
-    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(args.steps)]
+    marks = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
 
     # By default the step runs as the autograd function does: one workspace
     # sized for the backward, which reuses the forward's positions, plan and
@@ -197,6 +196,8 @@ def main() -> int:
     bflags = flags | (api.FLAG_FWD_WORKSPACE if reuse else 0)
 
     def step(mark=None):
+        if mark is not None:
+            mark[2].record()
         if chunk_doc is not None:
             o, lse = api.anchor_attn_fwd_chunks(qc, kc, vc, cu, chunk_doc, w.rope_base, True, None,
                                                 ws_f, flags=flags)
@@ -225,8 +226,10 @@ def main() -> int:
     torch.cuda.synchronize()
     prof = api.profile_end()
     ms = e0.elapsed_time(e1) / args.steps
-    bwd_ms = sum(a.elapsed_time(b) for a, b in marks) / args.steps
+    bwd_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / args.steps
     fwd_ms = ms - bwd_ms
+    per_step = sorted(c.elapsed_time(b) for a, b, c in marks)     # start of step -> end of backward
+    median_ms = per_step[len(per_step) // 2]
 
     fl = flops_fwd_bwd(doc_rows, w.Hq, w.D, anchor=anchor)
     total_flops = fl["total"] if w.backward else fl["fwd"]
@@ -253,7 +256,7 @@ def main() -> int:
                    if args.mode == "anchor" else
                    f"{args.mode} baseline fwd+bwd unmasked TFLOP/s (same kernels; also tokens/s)"),
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": ms, "ms_per_step_median": median_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name if args.mode == "anchor" else f"{w.name}_{args.mode}",
                    "mode": args.mode, "batch": w.B, "seq_len": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv,
