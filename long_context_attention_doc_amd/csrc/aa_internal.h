@@ -67,6 +67,8 @@ struct PlanBufs {
   uint8_t* qkind;      // [cap]
   int32_t* qpack;      // [cap] qidx | qkind << 24, may be null
   int32_t* n_live;     // [1]
+  int32_t* order;      // [B*nq + 1] work order of the query tiles, then its flags (kOrder*);
+                       // null where no attention kernel runs on the plan
 };
 
 // ---------------------------------------------------------------- launchers
@@ -114,7 +116,8 @@ struct BwdArgs {
 constexpr int kPreRows = 64;    // rows per block of the backward preprocess
 
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st);
-hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, hipStream_t st);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, const PlanBufs& pq,
+                           hipStream_t st);
 hipError_t launch_bwd_dq(const BwdArgs& a, const PlanBufs& pq, hipStream_t st);
 hipError_t launch_bwd_anchor(const BwdArgs& a, hipStream_t st);
 
@@ -291,6 +294,40 @@ __host__ __device__ inline int padded_grid(int total) { return xcd_per(total) * 
 __device__ __forceinline__ int xcd_work_item(int linear, int total) {
   const int w = (linear % kXcds) * xcd_per(total) + linear / kXcds;
   return w < total ? w : -1;
+}
+
+// Work order of a launch over H heads x T tiles.  The plan builder writes,
+// for its T = B * nq query tiles, order[0 .. T) (the tiles in launch order)
+// and order[T] (these flags):
+//  kOrderLpt         the tiles go by descending live-tile count, ties by index
+//                    (longest processing time first); else natural order.
+//                    Chosen when the largest count exceeds 1.5x the mean.
+//  kOrderInterleave  an XCD's slice of work items (H / 8 whole heads when H is
+//                    a multiple of 8) is walked rank-major across its heads,
+//                    so the first tiles of all its heads start together; else
+//                    head after head.  Chosen when a head has at most
+//                    kInterleaveMaxTiles tiles (about two rounds of an XCD's
+//                    concurrent workgroups, where walking head after head
+//                    starts the last head's long tiles late) or when the work
+//                    is even (the heads' tiles of one token range then run
+//                    together and their K/V rows are adjacent in HBM).  With
+//                    many tiles per head and uneven work, head after head
+//                    keeps one head's concurrent tiles on shared K/V in L2.
+constexpr int kOrderLpt = 1, kOrderInterleave = 2;
+constexpr int kInterleaveMaxTiles = 128;
+
+// Work item w -> (head, rank of its tile in the order).
+__device__ __forceinline__ void head_and_rank(int w, int T, int H, int flags, int& head,
+                                              int& rank) {
+  if ((flags & kOrderInterleave) && H % kXcds == 0) {
+    const int G = H / kXcds, slice = G * T;
+    const int x = w / slice, u = w - x * slice;
+    head = x * G + u % G;
+    rank = u / G;
+    return;
+  }
+  head = w / T;
+  rank = w - head * T;
 }
 
 // Packed plan entries: tile index in the low 24 bits, kind in the high 8.

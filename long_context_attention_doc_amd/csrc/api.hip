@@ -17,7 +17,8 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct PlanLayout {
   int BM, BN, nq, nk;
   size_t cap;
-  size_t kinds, kinds_t, cntq, cntk, qptr, kidx, kkind, kpack, kptr, qidx, qkind, qpack, n_live, end;
+  size_t kinds, kinds_t, cntq, cntk, qptr, kidx, kkind, kpack, kptr, qidx, qkind, qpack, n_live, order;
+  size_t end;
 };
 
 PlanLayout plan_layout(int B, int S, int BM, int BN, size_t base) {
@@ -41,6 +42,7 @@ PlanLayout plan_layout(int B, int S, int BM, int BN, size_t base) {
   p.qkind = o;  o = up(o + p.cap);
   p.qpack = o;  o = up(o + p.cap * 4);
   p.n_live = o; o = up(o + 4);
+  p.order = o;  o = up(o + ((size_t)B * p.nq + 1) * 4);
   p.end = o;
   return p;
 }
@@ -61,6 +63,7 @@ PlanBufs plan_bufs(const PlanLayout& l, char* ws) {
   b.qkind = (uint8_t*)(ws + l.qkind);
   b.qpack = (int32_t*)(ws + l.qpack);
   b.n_live = (int32_t*)(ws + l.n_live);
+  b.order = (int32_t*)(ws + l.order);
   return b;
 }
 
@@ -376,7 +379,8 @@ static aa_status bwd_impl(const void* q, const void* k, const void* v, const voi
   a.scale = scale;
   a.anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   AA_LAUNCH(AA_K_BWD_PRE, stream, launch_bwd_pre(a, stream));
-  AA_LAUNCH(AA_K_BWD_DKDV, stream, launch_bwd_dkdv(a, plan_bufs(L.pk, ws), stream));
+  AA_LAUNCH(AA_K_BWD_DKDV, stream,
+            launch_bwd_dkdv(a, plan_bufs(L.pk, ws), plan_bufs(L.pq, ws), stream));
   AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
   // without an anchor, key 0 is an ordinary key and dk/dv of it are complete
   if (a.anchor) AA_LAUNCH(AA_K_BWD_ANCHOR, stream, launch_bwd_anchor(a, stream));
@@ -522,7 +526,8 @@ aa_status anchor_attn_bwd_chunks(const void* q, const void* k, const void* v, co
   a.scale = scale;
   a.anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   AA_LAUNCH(AA_K_BWD_PRE, stream, launch_bwd_pre(a, stream));
-  AA_LAUNCH(AA_K_BWD_DKDV, stream, launch_bwd_dkdv(a, plan_bufs(L.pk, ws), stream));
+  AA_LAUNCH(AA_K_BWD_DKDV, stream,
+            launch_bwd_dkdv(a, plan_bufs(L.pk, ws), plan_bufs(L.pq, ws), stream));
   AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
   if (a.anchor) AA_LAUNCH(AA_K_BWD_ANCHOR, stream, launch_bwd_anchor(a, stream));
   AA_LAUNCH(AA_K_GATHER, stream,
@@ -615,7 +620,7 @@ aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, in
   // the caller's output arrays replace the workspace copies
   pb.qptr = qptr; pb.kidx = kidx; pb.kkind = kkind;
   pb.kptr = kptr; pb.qidx = qidx; pb.qkind = qkind; pb.n_live = n_live;
-  pb.kpack = nullptr; pb.qpack = nullptr;
+  pb.kpack = nullptr; pb.qpack = nullptr; pb.order = nullptr;
   hipLaunchKernelGGL(k_zero_status, dim3(1), dim3(64), 0, stream, status);
   AA_HIP(hipGetLastError());
   const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;

@@ -137,7 +137,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     const bf16* __restrict__ dout, const float* __restrict__ qstats,
     const float* __restrict__ table, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ kptr, const int32_t* __restrict__ qpack,
-    const int32_t* __restrict__ status, int S, int Hq, int Hkv,
+    const int32_t* __restrict__ order_flags, const int32_t* __restrict__ status, int S, int Hq,
+    int Hkv,
     int nk, int nblk, int n_items, float scale, int anchor, bf16* __restrict__ dk,
     bf16* __restrict__ dv) {
   constexpr int BM = kDkvBM, BN = kDkvBN;    // plan tiles: 64 queries x 128 keys
@@ -153,8 +154,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
 
   const int item = xcd_work_item(blockIdx.x, n_items);   // (hkv, b, kt), kt fastest
   if (item < 0) return;
-  const int ktile = item % (n_items / Hkv);                // b * nk + kt
-  const int hkv = item / (n_items / Hkv);
+  int hkv, ktile;   // ktile = b * nk + kt, in natural order: within a document the
+                    // key tiles already go from the most query tiles to the fewest
+  head_and_rank(item, n_items / Hkv, Hkv, *order_flags, hkv, ktile);
   const int b = ktile / nk, kt = ktile % nk;
   const int group = Hq / Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const float* __restrict__ ds0, const float* __restrict__ table,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ lo,
     const int32_t* __restrict__ hi, const int32_t* __restrict__ qptr,
-    const int32_t* __restrict__ kpack,
+    const int32_t* __restrict__ kpack, const int32_t* __restrict__ order,
     const int32_t* __restrict__ status, int S, int Hq, int Hkv, int nq, int n_items, float scale,
     int anchor,
     bf16* __restrict__ dq) {
@@ -337,8 +339,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
 
   const int item = xcd_work_item(blockIdx.x, n_items);   // (hq, b, qt), qt fastest
   if (item < 0) return;
-  const int tile = item % (n_items / Hq);
-  const int hq = item / (n_items / Hq);
+  const int tiles_per_head = n_items / Hq;
+  int hq, rank;
+  head_and_rank(item, tiles_per_head, Hq, order[tiles_per_head], hq, rank);
+  const int tile = order[rank];   // b * nq + qt
   const int b = tile / nq, qt = tile % nq;
   const int hkv = hq / (Hq / Hkv);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -519,16 +523,18 @@ hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, hipStream_t st) {
+hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, const PlanBufs& pq,
+                           hipStream_t st) {
   const int n_items = a.B * pk.nk * a.Hkv;
+  const int32_t* flags = pq.order + (size_t)a.B * pq.nq;   // the query-major plan's order flags
   const dim3 grid(padded_grid(n_items));
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_dkdv<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout,
-                       a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, a.status, a.S,
+                       a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, flags, a.status, a.S,
                        a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, a.dk, a.dv);
   else
     hipLaunchKernelGGL(k_bwd_dkdv<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout,
-                       a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, a.status, a.S,
+                       a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, flags, a.status, a.S,
                        a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, a.dk, a.dv);
   return hipGetLastError();
 }
@@ -539,11 +545,11 @@ hipError_t launch_bwd_dq(const BwdArgs& a, const PlanBufs& pq, hipStream_t st) {
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
-                       a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.dq);
+                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.dq);
   else
     hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
-                       a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.dq);
+                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.dq);
   return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
     const int32_t* __restrict__ qptr, const int32_t* __restrict__ kpack,
-    const int32_t* __restrict__ status, int S, int Hq, int Hkv,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
     int nq, int n_items, float scale_log2, int anchor, bf16* __restrict__ o,
     float* __restrict__ lse) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
@@ -59,8 +59,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
 
   const int item = xcd_work_item(blockIdx.x, n_items);   // (hq, b, qt), qt fastest
   if (item < 0) return;
-  const int tile = item % (n_items / Hq);   // b * nq + qt
-  const int hq = item / (n_items / Hq);
+  const int tiles_per_head = n_items / Hq;
+  int hq, rank;
+  head_and_rank(item, tiles_per_head, Hq, order[tiles_per_head], hq, rank);
+  const int tile = order[rank];   // b * nq + qt
   const int b = tile / nq, qt = tile % nq;
   const int hkv = hq / (Hq / Hkv);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -259,10 +261,10 @@ hipError_t launch_fwd(const bf16* qr, const bf16* kr, const bf16* v, TokenTables
   const dim3 grid(padded_grid(n_items));
   if (D == 128) {
     hipLaunchKernelGGL(k_fwd<128>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
-                       pb.kpack, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, anchor, o, lse);
+                       pb.kpack, pb.order, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, anchor, o, lse);
   } else {
     hipLaunchKernelGGL(k_fwd<64>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
-                       pb.kpack, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, anchor, o, lse);
+                       pb.kpack, pb.order, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, anchor, o, lse);
   }
   return hipGetLastError();
 }

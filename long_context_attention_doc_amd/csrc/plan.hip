@@ -211,6 +211,57 @@ __global__ void k_row_compact(const uint8_t* __restrict__ m, int rows, int n,
   }
 }
 
+// Work order of the n query tiles of a plan (the flags are described with
+// kOrderLpt): order[0 .. n) and order[n].  Every workgroup holds all counts in
+// LDS and derives the same flags; thread i writes tile i at its rank, the
+// number of tiles that go before it.  Plans with more than kMaxLptTiles tiles
+// keep the natural order, head after head.
+constexpr int kMaxLptTiles = 16384;
+__global__ __launch_bounds__(256) void k_tile_order(const int32_t* __restrict__ cnt, int n,
+                                                   int32_t* __restrict__ order) {
+  __shared__ int w[kMaxLptTiles];
+  __shared__ int wmax[4], wsum[4];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (n > kMaxLptTiles) {
+    if (i < n) order[i] = i;
+    if (i == 0) order[n] = 0;
+    return;
+  }
+  int mx = 0, sm = 0;   // counts are at most nk and n * nk < 2^29 here
+  for (int j = threadIdx.x; j < n; j += 256) {
+    const int c = cnt[j];
+    w[j] = c;
+    mx = max(mx, c);
+    sm += c;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    mx = max(mx, __shfl_xor(mx, off));
+    sm += __shfl_xor(sm, off);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    wmax[threadIdx.x >> 6] = mx;
+    wsum[threadIdx.x >> 6] = sm;
+  }
+  __syncthreads();
+  mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const long long total = (long long)wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  const bool lpt = 2LL * mx * n > 3LL * total;
+  const bool interleave = n <= kInterleaveMaxTiles || !lpt;
+  if (i == 0) order[n] = (lpt ? kOrderLpt : 0) | (interleave ? kOrderInterleave : 0);
+  if (i >= n) return;
+  if (!lpt) {
+    order[i] = i;
+    return;
+  }
+  const int wi = w[i];
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const int wj = w[j];
+    rank += (wj > wi) || (wj == wi && j < i);
+  }
+  order[rank] = i;
+}
+
 hipError_t launch_positions(const int32_t* cu, int n_seg, int B, int S, int causal, int mode,
                             int anchor, TokenTables tt, int32_t* status, hipStream_t st) {
   const long long total = (long long)B * S;
@@ -230,6 +281,9 @@ hipError_t launch_plan(const int32_t* lo, const int32_t* hi, int B, int S, int a
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pb.cntq, B * nq, pb.qptr, pb.n_live);
   hipLaunchKernelGGL(k_row_compact, dim3((B * nq + 3) / 4), dim3(256), 0, st, pb.kinds, B * nq, nk,
                      pb.qptr, pb.kidx, pb.kkind, pb.kpack);
+  if (pb.order)
+    hipLaunchKernelGGL(k_tile_order, dim3((B * nq + 255) / 256), dim3(256), 0, st, pb.cntq, B * nq,
+                       pb.order);
   if (key_major) {
     hipLaunchKernelGGL(k_transpose_kinds, dim3((nk + 63) / 64, (nq + 63) / 64, B), dim3(64, 4), 0,
                        st, pb.kinds, nq, nk, pb.kinds_t);
