@@ -229,7 +229,7 @@ struct DirectTile {
   static constexpr int NCH = D / 8;
   static constexpr int ITERS = ROWS * NCH / NTHREADS;
   static_assert(ROWS * NCH % NTHREADS == 0, "tile must split evenly over the waves");
-  uint32_t off[ITERS];
+  uint32_t off[ITERS];   // byte offset of this lane's 16 bytes from the tile's first row
   __device__ __forceinline__ static void locate(int u, int& row, int& chunk) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int pc_idx = (wave * ITERS + u) * 64 + lane;
@@ -241,13 +241,15 @@ struct DirectTile {
     for (int u = 0; u < ITERS; ++u) {
       int row, chunk;
       locate(u, row, chunk);
-      off[u] = (uint32_t)(row * row_stride + chunk * 8);
+      off[u] = (uint32_t)((row * row_stride + chunk * 8) * sizeof(bf16));
     }
   }
+  // The tile base is uniform and the offsets are 32-bit, so every load takes
+  // the scalar-base + vector-offset form with its LDS address in M0.
   __device__ __forceinline__ void load(bf16* lds_tile, const bf16* gbase, size_t row_stride,
                                        int row0, int row_max) const {
-    const int wave = threadIdx.x >> 6;
-    const bf16* tbase = gbase + (size_t)row0 * row_stride;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const char* tbase = (const char*)(gbase + (size_t)row0 * row_stride);
     if (row0 + ROWS - 1 <= row_max) {
 #pragma unroll
       for (int u = 0; u < ITERS; ++u)
@@ -260,9 +262,9 @@ struct DirectTile {
         int row, chunk;
         locate(u, row, chunk);
         const int r = min(row0 + row, row_max) - row0;
-        __builtin_amdgcn_global_load_lds((const void*)(tbase + (size_t)r * row_stride + chunk * 8),
-                                         (lds_void*)(lds_tile + (wave * ITERS + u) * 64 * 8), 16, 0,
-                                         0);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(tbase + (uint32_t)((r * row_stride + chunk * 8) * sizeof(bf16))),
+            (lds_void*)(lds_tile + (wave * ITERS + u) * 64 * 8), 16, 0, 0);
       }
     }
   }
