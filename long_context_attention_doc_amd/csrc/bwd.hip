@@ -46,8 +46,11 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
   constexpr int RPP = 256 / LPR;            // rows per pass of the workgroup
   __shared__ float red_k[RPP][D + 4];
   __shared__ float red_v[RPP][D + 4];
-  const int blk = blockIdx.x % nblk, b = blockIdx.x / nblk;
-  const int hq = blockIdx.y;
+  // heads fastest: neighbouring workgroups read neighbouring D-wide pieces
+  // of the same token rows
+  const int hq = blockIdx.x % Hq;
+  const int rb = blockIdx.x / Hq;
+  const int blk = rb % nblk, b = rb / nblk;
   const int hkv = hq / (Hq / Hkv);
   const int tid = threadIdx.x;
   const int slot = tid / LPR, f0 = (tid % LPR) * 8;
@@ -511,7 +514,9 @@ __global__ __launch_bounds__(1024) void k_bwd_anchor(
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st) {
-  const dim3 grid(a.B * a.nblk, a.Hq);
+  const long long blocks = (long long)a.Hq * a.B * a.nblk;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks);
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_pre<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.dout,
                        a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.dvec, a.ds0,
