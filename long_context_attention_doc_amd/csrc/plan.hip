@@ -281,7 +281,7 @@ hipError_t launch_plan(const int32_t* lo, const int32_t* hi, int B, int S, int a
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pb.cntq, B * nq, pb.qptr, pb.n_live);
   hipLaunchKernelGGL(k_row_compact, dim3((B * nq + 3) / 4), dim3(256), 0, st, pb.kinds, B * nq, nk,
                      pb.qptr, pb.kidx, pb.kkind, pb.kpack);
-  if (pb.order)
+  if (pb.order && !key_major)   // the key-major launches read the query-major plan's flags
     hipLaunchKernelGGL(k_tile_order, dim3((B * nq + 255) / 256), dim3(256), 0, st, pb.cntq, B * nq,
                        pb.order);
   if (key_major) {
