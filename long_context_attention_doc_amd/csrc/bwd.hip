@@ -411,6 +411,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     // columns = this wave's queries), dS^T, then dQ^T += K^T dS^T.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      // a block none of the wave's queries may see contributes exactly zero
+      const int k0 = kt * BN + 32 * kb;
+      if (need_mask && !__builtin_amdgcn_ballot_w64(qlo <= k0 + 31 && qhi >= k0)) continue;
       f32x16 st, dpt;
 #pragma unroll
       for (int j = 0; j < 16; ++j) { st[j] = 0.f; dpt[j] = 0.f; }

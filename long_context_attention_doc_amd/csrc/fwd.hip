@@ -150,16 +150,31 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     const bf16* Kc = Ks[BUF];
     const bf16* Vc = Vs[BUF];
 
+    // A 32-key block that none of the wave's queries may see (a document
+    // edge or the causal diagonal inside a partial tile) gets -inf scores
+    // and no products: its weights are exactly zero.
+    bool live[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int k0 = kt * BN + 32 * kb;
+      live[kb] = !need_mask || __builtin_amdgcn_ballot_w64(qlo <= k0 + 31 && qhi >= k0) != 0;
+    }
+
     // S^T = K Q^T for this wave's 32 queries and the BN keys of the tile.
     f32x16 st[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      if (live[kb]) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) st[kb][j] = 0.f;
+        for (int j = 0; j < 16; ++j) st[kb][j] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        st[kb] = mfma32(*(const bf16x8*)(Kc + T::chunk_off(kb * 32 + col, 2 * kk + h)), qf[kk],
-                        st[kb]);
+        for (int kk = 0; kk < NKK; ++kk)
+          st[kb] = mfma32(*(const bf16x8*)(Kc + T::chunk_off(kb * 32 + col, 2 * kk + h)), qf[kk],
+                          st[kb]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st[kb][j] = -INFINITY;
+      }
     }
     if (need_mask) {
       // keys outside [qlo, qhi] (row-local) are masked
@@ -220,12 +235,16 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
       l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 6, 7), ones, l, false);
     }
 
-    // O^T += V^T P^T.
+    // O^T += V^T P^T over the live key blocks.
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int kb = 0; kb < NKB; ++kb)
+      if (live[kb]) {
 #pragma unroll
-      for (int c = 0; c < BN / 16; ++c)
-        acc[db] = mfma32(tr_operand<D>(Vc, 16 * c, 32 * db), pb[c], acc[db]);
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int c = 2 * kb; c < 2 * kb + 2; ++c)
+            acc[db] = mfma32(tr_operand<D>(Vc, 16 * c, 32 * db), pb[c], acc[db]);
+      }
   };
   for (int i = 0; i < n_tiles; i += 2) {
     step(std::integral_constant<int, 0>{}, i);

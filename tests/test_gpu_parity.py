@@ -281,3 +281,45 @@ def test_full_size_sampled_modes(gpu_lib, mode):
     e_dv = rel_frob(f64(dv).reshape(B * S, Hkv, D)[keys][:, heads], dv_r[:, heads])
     say(f"[full-modes] {mode} dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
     assert max(e_dq, e_dk, e_dv) <= G_TOL
+
+
+def test_many_query_tiles_natural_order(gpu_lib):
+    """More query tiles than the work-order kernel ranks (130 rows x 128
+    tiles = 16,640 > 16,384): the launches fall back to the natural order,
+    head after head; sampled outputs against the oracle."""
+    B, S, Hq, Hkv, D, base = 130, 16384, 2, 1, 64, 5e5
+    rows_docs = [W.sample_doc_lengths(S, 1024, 1.0, 64, S - 1, 300 + b) for b in range(B)]
+    cu = W.cu_doc_lens_from_lengths(rows_docs, S)
+    say(f"[many-tiles] B={B} S={S} Hq={Hq} Hkv={Hkv} D={D}: generating inputs")
+    q, k, v, do = W.make_tensors(B, S, Hq, Hkv, D, 4321)
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    say("[many-tiles] fwd+bwd on GPU")
+    o, lse = gpu_lib.anchor_attn_fwd(qc, kc, vc, cu, base)
+    dq, dk, dv = gpu_lib.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, base)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    heads = [0, 1]          # the whole kv group
+    rows = np.unique(np.concatenate([[0, S, (B - 1) * S, B * S - 1],
+                                     rng.integers(0, B * S, 40), cu[1:-1][rng.integers(0, len(cu) - 2, 16)]]))
+    say(f"[many-tiles] oracle forward on {len(rows)} rows")
+    o_ref, lse_ref, _, _ = oracle.forward(q, k, v, cu, base, heads=heads, rows=rows)
+    ridx = torch.as_tensor(rows, device=o.device)
+    o_g = f64(o.reshape(B * S, Hq, D)[ridx][:, heads])
+    lse_g = f64(lse).transpose(1, 0, 2).reshape(Hq, B * S)[heads][:, rows]
+    say(f"[many-tiles] O err {o_err(o_g, o_ref):.2e} lse err {np.abs(lse_g - lse_ref).max():.2e}")
+    assert o_err(o_g, o_ref) <= O_TOL
+    assert np.abs(lse_g - lse_ref).max() <= LSE_TOL
+    # keys of short documents (every query that sees them is cheap to sum),
+    # and the anchors of the first and last rows
+    short = [(int(s_), int(e_)) for s_, e_ in zip(cu[:-1], cu[1:]) if 1 < e_ - s_ <= 400]
+    keys = np.unique(np.array([0, (B - 1) * S] + [x for s_, e_ in short[:12] for x in (s_, e_ - 1)]))
+    qrows = rows[:32]
+    say(f"[many-tiles] oracle backward on {len(qrows)} rows, {len(keys)} keys")
+    dq_r, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, base, heads=heads, q_rows=qrows, k_cols=keys)
+    qidx = torch.as_tensor(qrows, device=o.device)
+    kidx = torch.as_tensor(keys, device=o.device)
+    e_dq = rel_frob(f64(dq.reshape(B * S, Hq, D)[qidx][:, heads]), dq_r)
+    e_dk = rel_frob(f64(dk.reshape(B * S, Hkv, D)[kidx][:, [0]]), dk_r[:, [0]])
+    e_dv = rel_frob(f64(dv.reshape(B * S, Hkv, D)[kidx][:, [0]]), dv_r[:, [0]])
+    say(f"[many-tiles] dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
+    assert max(e_dq, e_dk, e_dv) <= G_TOL
