@@ -86,9 +86,13 @@ hipError_t launch_move_lse(const float* x, const int32_t* src, int B, int H, int
                            float* y, hipStream_t st);
 hipError_t launch_rope_apply(const bf16* x, const int32_t* src, const int32_t* pos, const float* table, int npos, int B, int S,
                              int H, int D, bf16* x_rot, hipStream_t st);
-hipError_t launch_fwd(const bf16* qr, const bf16* kr, const bf16* v, TokenTables tt,
-                      const PlanBufs& pb, const int32_t* status, int B, int S, int Hq, int Hkv,
-                      int D, float scale, int anchor, bf16* o, float* lse, hipStream_t st);
+// The forward.  With q_raw non-null it rotates Q itself as it loads it (from
+// q_raw, positions tt.pos and the RoPE table of npos rows) and writes the
+// rotated q to qr for the backward; otherwise it reads qr, rotated before.
+hipError_t launch_fwd(const bf16* q_raw, const float* table, int npos, bf16* qr, const bf16* kr,
+                      const bf16* v, TokenTables tt, const PlanBufs& pb, const int32_t* status,
+                      int B, int S, int Hq, int Hkv, int D, float scale, int anchor, bf16* o,
+                      float* lse, hipStream_t st);
 
 struct BwdArgs {
   const bf16* qr;      // rotated q [B,S,Hq,D]
@@ -135,6 +139,27 @@ __device__ __forceinline__ float partner(float x) {
                                                   false);
   // lanes 0-31 receive x[l+32] in r[1]; lanes 32-63 receive x[l-32] in r[0]
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// RoPE (Eq. 6 of arXiv 2411.13476 as given on the paper-graph architecture
+// page, section 3.4) of 8 consecutive features x[d0 .. d0+8), four adjacent
+// pairs, of a token at table row p: tb = table + (p * (D/2) + d0/2) * 2 holds
+// {cos, sin} of the four pair angles.  Float32 rotation, bf16 result (RNE).
+// The RoPE pass and the forward's Q loads share this one definition, so a
+// rotated vector is the same bits wherever it is formed.
+__device__ __forceinline__ bf16x8 rope_rotate8(const bf16x8 xv, const float* tb) {
+  const f32x4 cs01 = ((const f32x4*)tb)[0];   // cos0 sin0 cos1 sin1
+  const f32x4 cs23 = ((const f32x4*)tb)[1];
+  bf16x8 out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float c = q < 2 ? cs01[2 * (q & 1)] : cs23[2 * (q & 1)];
+    const float s = q < 2 ? cs01[2 * (q & 1) + 1] : cs23[2 * (q & 1) + 1];
+    const float x0 = (float)xv[2 * q], x1 = (float)xv[2 * q + 1];
+    out[2 * q] = (bf16)__builtin_fmaf(x0, c, -x1 * s);
+    out[2 * q + 1] = (bf16)__builtin_fmaf(x0, s, x1 * c);
+  }
+  return out;
 }
 
 // ---------------------------------------------------------------- LDS tiles

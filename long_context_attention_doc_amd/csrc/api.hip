@@ -202,7 +202,7 @@ hipError_t launch_zero_status(int32_t* status, hipStream_t st) {
 // the forward and the backward.
 aa_status prologue(const Layout& L, char* ws, const void* q, const void* k,
                    const int32_t* cu, int n_seg, double rope_base, int causal, int flags, int B,
-                   int S, int Hq, int Hkv, int D, bool bwd, hipStream_t st) {
+                   int S, int Hq, int Hkv, int D, bool bwd, hipStream_t st, bool rotate_q = true) {
   int32_t* status = (int32_t*)(ws + L.status);
   TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
   const int mode = (flags & AA_FLAG_CONTINUOUS_POS) ? 1 : 0;
@@ -220,9 +220,10 @@ aa_status prologue(const Layout& L, char* ws, const void* q, const void* k,
   // reset IDs (its tokens count 1 .. S), so the table has S + 1 rows.
   AA_LAUNCH(AA_K_ROPE_TABLE, st,
             launch_rope_table(S + 1, D, make_theta(D, rope_base), table, st));
-  AA_LAUNCH(AA_K_ROPE, st,
-            launch_rope_apply((const bf16*)q, nullptr, tt.pos, table, S + 1, B, S, Hq, D,
-                              (bf16*)(ws + L.qrot), st));
+  if (rotate_q)
+    AA_LAUNCH(AA_K_ROPE, st,
+              launch_rope_apply((const bf16*)q, nullptr, tt.pos, table, S + 1, B, S, Hq, D,
+                                (bf16*)(ws + L.qrot), st));
   AA_LAUNCH(AA_K_ROPE, st,
             launch_rope_apply((const bf16*)k, nullptr, tt.pos, table, S + 1, B, S, Hkv, D,
                               (bf16*)(ws + L.krot), st));
@@ -312,15 +313,18 @@ static aa_status fwd_impl(const void* q, const void* k, const void* v, const int
   if (ws_bytes < L.total) return AA_EWORKSPACE;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)D);
   char* ws = (char*)workspace;
+  // the forward rotates Q as it loads it (and leaves the rotated q in the
+  // workspace for the backward); the RoPE pass rotates K only
   aa_status s = prologue(L, ws, q, k, cu_doc_lens, n_seg, rope_base, causal, flags, B, S, Hq,
-                         Hkv, D, false, stream);
+                         Hkv, D, false, stream, /*rotate_q=*/false);
   if (s != AA_OK) return s;
   TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
   const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   AA_LAUNCH(AA_K_FWD, stream,
-            launch_fwd((const bf16*)(ws + L.qrot), (const bf16*)(ws + L.krot), (const bf16*)v, tt,
-                       plan_bufs(L.pq, ws), (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D,
-                       scale, anchor, (bf16*)o, lse, stream));
+            launch_fwd((const bf16*)q, (const float*)(ws + L.table), S + 1, (bf16*)(ws + L.qrot),
+                       (const bf16*)(ws + L.krot), (const bf16*)v, tt, plan_bufs(L.pq, ws),
+                       (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D, scale, anchor, (bf16*)o,
+                       lse, stream));
   return AA_OK;
 }
 
@@ -463,7 +467,7 @@ aa_status anchor_attn_fwd_chunks(const void* q, const void* k, const void* v,
   const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   const int32_t* src = (const int32_t*)(ws + C.src);
   AA_LAUNCH(AA_K_FWD, stream,
-            launch_fwd((const bf16*)(ws + L.qrot), (const bf16*)(ws + L.krot),
+            launch_fwd(nullptr, nullptr, 0, (bf16*)(ws + L.qrot), (const bf16*)(ws + L.krot),
                        (const bf16*)(ws + C.vperm), tt, plan_bufs(L.pq, ws),
                        (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D, scale, anchor,
                        (bf16*)(ws + C.operm), (float*)(ws + C.lseperm), stream));

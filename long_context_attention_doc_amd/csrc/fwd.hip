@@ -16,7 +16,11 @@
 // lane's 32x32 accumulator column is one query: the softmax row statistics
 // are then per lane, and the two lanes holding the same query (lane l and
 // l + 32) combine with one v_permlane32_swap.
-//   * Q^T (B operand) stays in registers for the whole key loop.
+//   * Q^T (B operand) stays in registers for the whole key loop.  The RoPE
+//     rotation of Q happens in its load (ROTATE_Q): the rotated rows are
+//     formed once per work item and also written out for the backward.  K
+//     is streamed (every query tile reads it again), so it is rotated once
+//     by the RoPE pass before this kernel.
 //   * K and V tiles go straight from global memory into a ring of LDS
 //     buffers (global_load_lds) in a row-major layout with an XOR swizzle; K
 //     is read row-wise (A operand of S^T), V with transposing LDS reads
@@ -39,9 +43,10 @@
 
 namespace aa {
 
-template <int D>
+template <int D, bool ROTATE_Q>
 __global__ __launch_bounds__(256, 2) void k_fwd(
-    const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
+    const bf16* __restrict__ q_raw, const float* __restrict__ table, const int32_t* __restrict__ pos,
+    int npos, bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
     const int32_t* __restrict__ qptr, const int32_t* __restrict__ kpack,
     const int32_t* __restrict__ order, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
@@ -74,12 +79,27 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   if (!qvalid) { qlo = 1; qhi = 0; }
   const bool bad = status[0] != kStatusOk;
 
-  // Q^T operand: lane holds query `col`, features 16*kk + 8*h + i.
+  // Q^T operand: lane holds query `col`, features 16*kk + 8*h + i.  With
+  // ROTATE_Q the RoPE stage happens here: Q stays in registers for the
+  // whole key loop, so it is rotated once, and the rotated rows are written
+  // out for the backward.
   bf16x8 qf[NKK];
   {
-    const bf16* qp = qr + (tok * Hq + hq) * D + 8 * h;
+    const size_t qoff = (tok * Hq + hq) * D + 8 * h;
+    if constexpr (ROTATE_Q) {
+      const int p = min(max(pos[tok], 0), npos - 1);
+      const float* tb = table + (size_t)p * D + 8 * h;     // row p, pair (8h)/2, {cos, sin}
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk);
+      for (int kk = 0; kk < NKK; ++kk)
+        qf[kk] = rope_rotate8(*(const bf16x8*)(q_raw + qoff + 16 * kk), tb + 16 * kk);
+      if (qvalid) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) *(bf16x8*)(qr + qoff + 16 * kk) = qf[kk];
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const bf16x8*)(qr + qoff + 16 * kk);
+    }
   }
 
   // Anchor column: s_i0 = q'_i . k'_0 (k'_0 = k_0, its position is 0).  Rows
@@ -272,19 +292,25 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   }
 }
 
-hipError_t launch_fwd(const bf16* qr, const bf16* kr, const bf16* v, TokenTables tt,
-                      const PlanBufs& pb, const int32_t* status, int B, int S, int Hq, int Hkv,
-                      int D, float scale, int anchor, bf16* o, float* lse, hipStream_t st) {
+hipError_t launch_fwd(const bf16* q_raw, const float* table, int npos, bf16* qr, const bf16* kr,
+                      const bf16* v, TokenTables tt, const PlanBufs& pb, const int32_t* status,
+                      int B, int S, int Hq, int Hkv, int D, float scale, int anchor, bf16* o,
+                      float* lse, hipStream_t st) {
   const float scale_log2 = scale * 1.44269504088896340736f;
   const int n_items = B * pb.nq * Hq;
   const dim3 grid(padded_grid(n_items));
+#define AA_LAUNCH_FWD(DD, RQ)                                                                    \
+  hipLaunchKernelGGL((k_fwd<DD, RQ>), grid, dim3(256), 0, st, q_raw, table, tt.pos, npos, qr, kr, \
+                     v, tt.lo, tt.hi, pb.qptr, pb.kpack, pb.order, status, S, Hq, Hkv, pb.nq,     \
+                     n_items, scale_log2, anchor, o, lse)
   if (D == 128) {
-    hipLaunchKernelGGL(k_fwd<128>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
-                       pb.kpack, pb.order, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, anchor, o, lse);
+    if (q_raw) AA_LAUNCH_FWD(128, true);
+    else AA_LAUNCH_FWD(128, false);
   } else {
-    hipLaunchKernelGGL(k_fwd<64>, grid, dim3(256), 0, st, qr, kr, v, tt.lo, tt.hi, pb.qptr,
-                       pb.kpack, pb.order, status, S, Hq, Hkv, pb.nq, n_items, scale_log2, anchor, o, lse);
+    if (q_raw) AA_LAUNCH_FWD(64, true);
+    else AA_LAUNCH_FWD(64, false);
   }
+#undef AA_LAUNCH_FWD
   return hipGetLastError();
 }
 

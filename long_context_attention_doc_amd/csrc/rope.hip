@@ -45,19 +45,7 @@ __global__ void k_rope_apply(const bf16* __restrict__ x, const int32_t* __restri
   const int p = min(max(pos[tok], 0), npos - 1);  // table rows exist for 0 <= pos < npos
   const long long in = src ? (long long)src[tok] * chunks_per_tok + within : i;
   const bf16x8 xv = *(const bf16x8*)(x + in * 8);
-  const f32x4* tb = (const f32x4*)(table + ((size_t)p * (D / 2) + d0 / 2) * 2);
-  const f32x4 cs01 = tb[0];   // cos0 sin0 cos1 sin1
-  const f32x4 cs23 = tb[1];
-  bf16x8 out;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float c = q < 2 ? cs01[2 * (q & 1)] : cs23[2 * (q & 1)];
-    const float s = q < 2 ? cs01[2 * (q & 1) + 1] : cs23[2 * (q & 1) + 1];
-    const float x0 = (float)xv[2 * q], x1 = (float)xv[2 * q + 1];
-    out[2 * q] = (bf16)__builtin_fmaf(x0, c, -x1 * s);
-    out[2 * q + 1] = (bf16)__builtin_fmaf(x0, s, x1 * c);
-  }
-  *(bf16x8*)(y + i * 8) = out;
+  *(bf16x8*)(y + i * 8) = rope_rotate8(xv, table + ((size_t)p * (D / 2) + d0 / 2) * 2);
 }
 
 hipError_t launch_rope_table(int S, int D, const RopeTheta& th, float* table, hipStream_t st) {
