@@ -170,7 +170,8 @@ aa_status anchor_attn_bwd_ex(const void* q, const void* k, const void* v, const 
  * workspace size comes from anchor_attn_chunks_workspace_size (for_bwd 0/1).
  * The library runs the block-sparse kernels on every row permuted so that
  * each document is contiguous (the order inside a document is kept, so the
- * mask is unchanged) and scatters the results back. */
+ * mask is unchanged); the kernels write O, LSE, dq, dk, dv straight to the
+ * caller's token order. */
 size_t anchor_attn_chunks_workspace_size(int B, int S, int Hq, int Hkv, int D, int n_chunks,
                                          int for_bwd);
 aa_status anchor_attn_fwd_chunks(const void* q, const void* k, const void* v,

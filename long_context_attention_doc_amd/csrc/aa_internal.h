@@ -80,19 +80,20 @@ hipError_t launch_rope_table(int S, int D, const RopeTheta& th, float* table, hi
 hipError_t launch_chunk_layout(const int32_t* cu, const int32_t* chunk_doc, int n_chunks, int B,
                                int S, int causal, int mode, int anchor, ChunkBufs cb,
                                TokenTables tt, int32_t* status, hipStream_t st);
-hipError_t launch_move_rows(const bf16* x, const int32_t* src, int B, int S, int H, int D,
-                            bool scatter, bf16* y, hipStream_t st);
-hipError_t launch_move_lse(const float* x, const int32_t* src, int B, int H, int S, bool scatter,
-                           float* y, hipStream_t st);
+// y[p] = x[src[p]] for rows of H*D elements (one token's heads).
+hipError_t launch_gather_rows(const bf16* x, const int32_t* src, int B, int S, int H, int D,
+                              bf16* y, hipStream_t st);
 hipError_t launch_rope_apply(const bf16* x, const int32_t* src, const int32_t* pos, const float* table, int npos, int B, int S,
                              int H, int D, bf16* x_rot, hipStream_t st);
 // The forward.  With q_raw non-null it rotates Q itself as it loads it (from
 // q_raw, positions tt.pos and the RoPE table of npos rows) and writes the
 // rotated q to qr for the backward; otherwise it reads qr, rotated before.
+// With tok_map non-null (rows permuted so that documents are contiguous) the
+// output of position p goes to token tok_map[p] of o and lse.
 hipError_t launch_fwd(const bf16* q_raw, const float* table, int npos, bf16* qr, const bf16* kr,
                       const bf16* v, TokenTables tt, const PlanBufs& pb, const int32_t* status,
                       int B, int S, int Hq, int Hkv, int D, float scale, int anchor, bf16* o,
-                      float* lse, hipStream_t st);
+                      float* lse, const int32_t* tok_map, hipStream_t st);
 
 struct BwdArgs {
   const bf16* qr;      // rotated q [B,S,Hq,D]
@@ -116,6 +117,10 @@ struct BwdArgs {
   int B, S, Hq, Hkv, D;
   float scale;
   int anchor;          // 0: rows without a shared anchor (intra-document attention)
+  // Rows permuted so that documents are contiguous: position p (over B*S) is
+  // token tok_map[p] of the caller's o, lse, dq, dk, dv; qr, kr, v, dout and
+  // the token tables are in permuted order.  Null: no permutation.
+  const int32_t* tok_map = nullptr;
 };
 constexpr int kPreRows = 64;    // rows per block of the backward preprocess
 

@@ -109,7 +109,7 @@ Layout layout(int B, int S, int Hq, int Hkv, int D, bool bwd) {
 
 // Extra workspace of the interleaved-chunk entry points, after the Layout.
 struct ChunkLayout {
-  size_t new_start, doc_start, doc_end, row_ok, src, vperm, operm, doperm, lseperm, dqp, dkp, dvp;
+  size_t new_start, doc_start, doc_end, row_ok, src, vperm, doperm;
   size_t total;
 };
 
@@ -123,15 +123,10 @@ ChunkLayout chunk_layout(size_t base, int B, int S, int Hq, int Hkv, int D, int 
   C.doc_end = o;   o = up(o + (size_t)n_chunks * 4);
   C.row_ok = o;    o = up(o + (size_t)B * 4);
   C.src = o;       o = up(o + T * 4);
-  C.vperm = o;     o = up(o + T * Hkv * D * 2);
-  C.operm = o;     o = up(o + T * Hq * D * 2);
-  C.lseperm = o;   o = up(o + (size_t)B * Hq * S * 4);
-  C.doperm = C.dqp = C.dkp = C.dvp = 0;
-  if (bwd) {
+  C.vperm = o;     o = up(o + T * Hkv * D * 2);   // V and dO stream through LDS tiles in
+  C.doperm = 0;                                    // permuted order; everything else is
+  if (bwd) {                                       // read or written at tok_map[p]
     C.doperm = o;  o = up(o + T * Hq * D * 2);
-    C.dqp = o;     o = up(o + T * Hq * D * 2);
-    C.dkp = o;     o = up(o + T * Hkv * D * 2);
-    C.dvp = o;     o = up(o + T * Hkv * D * 2);
   }
   C.total = o;
   return C;
@@ -262,7 +257,7 @@ aa_status prologue_chunks(const Layout& L, const ChunkLayout& C, char* ws, const
             launch_rope_apply((const bf16*)k, cb.src, tt.pos, table, S + 1, B, S, Hkv, D,
                               (bf16*)(ws + L.krot), st));
   AA_LAUNCH(AA_K_GATHER, st,
-            launch_move_rows((const bf16*)v, cb.src, B, S, Hkv, D, false, (bf16*)(ws + C.vperm),
+            launch_gather_rows((const bf16*)v, cb.src, B, S, Hkv, D, (bf16*)(ws + C.vperm),
                              st));
   return AA_OK;
 }
@@ -324,7 +319,7 @@ static aa_status fwd_impl(const void* q, const void* k, const void* v, const int
             launch_fwd((const bf16*)q, (const float*)(ws + L.table), S + 1, (bf16*)(ws + L.qrot),
                        (const bf16*)(ws + L.krot), (const bf16*)v, tt, plan_bufs(L.pq, ws),
                        (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D, scale, anchor, (bf16*)o,
-                       lse, stream));
+                       lse, nullptr, stream));
   return AA_OK;
 }
 
@@ -470,11 +465,7 @@ aa_status anchor_attn_fwd_chunks(const void* q, const void* k, const void* v,
             launch_fwd(nullptr, nullptr, 0, (bf16*)(ws + L.qrot), (const bf16*)(ws + L.krot),
                        (const bf16*)(ws + C.vperm), tt, plan_bufs(L.pq, ws),
                        (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D, scale, anchor,
-                       (bf16*)(ws + C.operm), (float*)(ws + C.lseperm), stream));
-  AA_LAUNCH(AA_K_GATHER, stream,
-            launch_move_rows((const bf16*)(ws + C.operm), src, B, S, Hq, D, true, (bf16*)o, stream));
-  AA_LAUNCH(AA_K_GATHER, stream,
-            launch_move_lse((const float*)(ws + C.lseperm), src, B, Hq, S, true, lse, stream));
+                       (bf16*)o, lse, src, stream));
   return AA_OK;
 }
 
@@ -501,19 +492,15 @@ aa_status anchor_attn_bwd_chunks(const void* q, const void* k, const void* v, co
   if (s != AA_OK) return s;
   const int32_t* src = (const int32_t*)(ws + C.src);
   AA_LAUNCH(AA_K_GATHER, stream,
-            launch_move_rows((const bf16*)o, src, B, S, Hq, D, false, (bf16*)(ws + C.operm), stream));
-  AA_LAUNCH(AA_K_GATHER, stream,
-            launch_move_rows((const bf16*)dout, src, B, S, Hq, D, false, (bf16*)(ws + C.doperm),
+            launch_gather_rows((const bf16*)dout, src, B, S, Hq, D, (bf16*)(ws + C.doperm),
                              stream));
-  AA_LAUNCH(AA_K_GATHER, stream,
-            launch_move_lse(lse, src, B, Hq, S, false, (float*)(ws + C.lseperm), stream));
   BwdArgs a;
   a.qr = (const bf16*)(ws + L.qrot);
   a.kr = (const bf16*)(ws + L.krot);
   a.v = (const bf16*)(ws + C.vperm);
-  a.o = (const bf16*)(ws + C.operm);
+  a.o = (const bf16*)o;
   a.dout = (const bf16*)(ws + C.doperm);
-  a.lse = (const float*)(ws + C.lseperm);
+  a.lse = lse;
   a.table = (const float*)(ws + L.table);
   a.tt = TokenTables{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
   a.status = (const int32_t*)(ws + L.status);
@@ -523,9 +510,10 @@ aa_status anchor_attn_bwd_chunks(const void* q, const void* k, const void* v, co
   a.part_dv = (float*)(ws + L.pdv);
   a.qstats = (float*)(ws + L.qstats);
   a.nblk = L.nblk;
-  a.dq = (bf16*)(ws + C.dqp);
-  a.dk = (bf16*)(ws + C.dkp);
-  a.dv = (bf16*)(ws + C.dvp);
+  a.dq = (bf16*)dq;
+  a.dk = (bf16*)dk;
+  a.dv = (bf16*)dv;
+  a.tok_map = src;
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
   a.scale = scale;
   a.anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
@@ -534,12 +522,6 @@ aa_status anchor_attn_bwd_chunks(const void* q, const void* k, const void* v, co
             launch_bwd_dkdv(a, plan_bufs(L.pk, ws), plan_bufs(L.pq, ws), stream));
   AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
   if (a.anchor) AA_LAUNCH(AA_K_BWD_ANCHOR, stream, launch_bwd_anchor(a, stream));
-  AA_LAUNCH(AA_K_GATHER, stream,
-            launch_move_rows(a.dq, src, B, S, Hq, D, true, (bf16*)dq, stream));
-  AA_LAUNCH(AA_K_GATHER, stream,
-            launch_move_rows(a.dk, src, B, S, Hkv, D, true, (bf16*)dk, stream));
-  AA_LAUNCH(AA_K_GATHER, stream,
-            launch_move_rows(a.dv, src, B, S, Hkv, D, true, (bf16*)dv, stream));
   return AA_OK;
 }
 

@@ -41,7 +41,8 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
     const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi, int S, int Hq, int Hkv,
     int nblk, float scale, int anchor, float* __restrict__ dvec, float* __restrict__ ds0,
-    float* __restrict__ part_dk, float* __restrict__ part_dv, float* __restrict__ qstats) {
+    float* __restrict__ part_dk, float* __restrict__ part_dv, float* __restrict__ qstats,
+    const int32_t* __restrict__ tok_map) {
   constexpr int LPR = D / 8;                // lanes per row
   constexpr int RPP = 256 / LPR;            // rows per pass of the workgroup
   __shared__ float red_k[RPP][D + 4];
@@ -67,9 +68,10 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
     const int row = blk * kPreRows + r0 + slot;
     const bool valid = row < S;
     const size_t tok = tok0 + (valid ? row : S - 1);
+    const size_t otok = tok_map ? (size_t)tok_map[tok] : tok;   // the caller's O and LSE row
     const size_t off = (tok * Hq + hq) * D + f0;
     const bf16x8 qv = *(const bf16x8*)(qr + off);
-    const bf16x8 ov = *(const bf16x8*)(o + off);
+    const bf16x8 ov = *(const bf16x8*)(o + (otok * Hq + hq) * D + f0);
     const bf16x8 dv = *(const bf16x8*)(dout + off);
     float d_o = 0.f, s0 = 0.f, dp0 = 0.f;
 #pragma unroll
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
       s0 += __shfl_xor(s0, off2);
       dp0 += __shfl_xor(dp0, off2);
     }
-    const float L = lse[((size_t)b * Hq + hq) * S + (valid ? row : S - 1)];
+    const float L = lse[((size_t)b * Hq + hq) * S + (otok - tok0)];
     // without an anchor there is no anchor column: its weight and dS are zero
     float p0 = valid && anchor ? __builtin_amdgcn_exp2f((s0 * scale - L) * kLog2e) : 0.f;
     const float dsv = p0 * (dp0 - d_o);
@@ -142,7 +144,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     const int32_t* __restrict__ kptr, const int32_t* __restrict__ qpack,
     const int32_t* __restrict__ order_flags, const int32_t* __restrict__ status, int S, int Hq,
     int Hkv,
-    int nk, int nblk, int n_items, float scale, int anchor, bf16* __restrict__ dk,
+    int nk, int nblk, int n_items, float scale, int anchor, const int32_t* __restrict__ tok_map,
+    bf16* __restrict__ dk,
     bf16* __restrict__ dv) {
   constexpr int BM = kDkvBM, BN = kDkvBN;    // plan tiles: 64 queries x 128 keys
   constexpr int BH = BM / 2;                 // queries per step
@@ -289,8 +292,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   if (kvalid) {
     const int pk = pos[ktok];
     const float* tb = table + (size_t)pk * D;      // (D/2) pairs of {cos, sin}
-    bf16* dkp = dk + (ktok * Hkv + hkv) * D;
-    bf16* dvp = dv + (ktok * Hkv + hkv) * D;
+    const size_t otok = tok_map ? (size_t)tok_map[ktok] : ktok;   // the caller's dk, dv row
+    bf16* dkp = dk + (otok * Hkv + hkv) * D;
+    bf16* dvp = dv + (otok * Hkv + hkv) * D;
 #pragma unroll
     for (int dblk = 0; dblk < NDB; ++dblk)
 #pragma unroll
@@ -328,8 +332,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const int32_t* __restrict__ hi, const int32_t* __restrict__ qptr,
     const int32_t* __restrict__ kpack, const int32_t* __restrict__ order,
     const int32_t* __restrict__ status, int S, int Hq, int Hkv, int nq, int n_items, float scale,
-    int anchor,
-    bf16* __restrict__ dq) {
+    int anchor, const int32_t* __restrict__ tok_map, bf16* __restrict__ dq) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
@@ -359,7 +362,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   const bool bad = status[0] != kStatusOk;
   const float scale_log2 = scale * kLog2e;
   const size_t rowstat = ((size_t)b * Hq + hq) * S + (qvalid ? qrow : S - 1);
-  const float nlse2 = -lse[rowstat] * kLog2e;
+  const size_t otok = tok_map ? (size_t)tok_map[tok] : tok;   // the caller's LSE and dq row
+  const float nlse2 = -lse[((size_t)b * Hq + hq) * S + (otok - tok0)] * kLog2e;
   const float dvi = dvec[rowstat];
 
   bf16x8 qf[NKK], gf[NKK];
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const bf16* k0 = kr + (tok0 * Hkv + hkv) * D;
     const int pq = pos[tok];
     const float* tb = table + (size_t)pq * D;
-    bf16* dqp = dq + (tok * Hq + hq) * D;
+    bf16* dqp = dq + (otok * Hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -486,7 +490,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
 __global__ __launch_bounds__(1024) void k_bwd_anchor(
     const float* __restrict__ part_dk, const float* __restrict__ part_dv,
     const int32_t* __restrict__ status, int S, int Hq, int Hkv, int D, int nblk, float scale,
-    bf16* __restrict__ dk, bf16* __restrict__ dv) {
+    const int32_t* __restrict__ tok_map, bf16* __restrict__ dk, bf16* __restrict__ dv) {
   __shared__ float red[2][1024];
   const int b = blockIdx.x / Hkv, hkv = blockIdx.x % Hkv;
   const int group = Hq / Hkv;
@@ -509,7 +513,8 @@ __global__ __launch_bounds__(1024) void k_bwd_anchor(
       sk += red[0][q * D + d];
       sv += red[1][q * D + d];
     }
-    const size_t off = ((size_t)b * S * Hkv + hkv) * D + d;
+    const size_t atok = tok_map ? (size_t)tok_map[(size_t)b * S] : (size_t)b * S;
+    const size_t off = (atok * Hkv + hkv) * D + d;
     dk[off] = (bf16)(bad ? NAN : sk * scale);
     dv[off] = (bf16)(bad ? NAN : sv);
   }
@@ -523,11 +528,11 @@ hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st) {
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_pre<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.dout,
                        a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.dvec, a.ds0,
-                       a.part_dk, a.part_dv, a.qstats);
+                       a.part_dk, a.part_dv, a.qstats, a.tok_map);
   else
     hipLaunchKernelGGL(k_bwd_pre<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.dout,
                        a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.dvec, a.ds0,
-                       a.part_dk, a.part_dv, a.qstats);
+                       a.part_dk, a.part_dv, a.qstats, a.tok_map);
   return hipGetLastError();
 }
 
@@ -539,11 +544,11 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, const PlanBufs&
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_dkdv<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout,
                        a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, flags, a.status, a.S,
-                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, a.dk, a.dv);
+                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, a.tok_map, a.dk, a.dv);
   else
     hipLaunchKernelGGL(k_bwd_dkdv<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout,
                        a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, flags, a.status, a.S,
-                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, a.dk, a.dv);
+                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, a.tok_map, a.dk, a.dv);
   return hipGetLastError();
 }
 
@@ -553,17 +558,19 @@ hipError_t launch_bwd_dq(const BwdArgs& a, const PlanBufs& pq, hipStream_t st) {
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
-                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.dq);
+                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.tok_map,
+                       a.dq);
   else
     hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
-                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.dq);
+                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.tok_map,
+                       a.dq);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_anchor(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_bwd_anchor, dim3(a.B * a.Hkv), dim3(1024), 0, st, a.part_dk, a.part_dv,
-                     a.status, a.S, a.Hq, a.Hkv, a.D, a.nblk, a.scale, a.dk, a.dv);
+                     a.status, a.S, a.Hq, a.Hkv, a.D, a.nblk, a.scale, a.tok_map, a.dk, a.dv);
   return hipGetLastError();
 }
 

@@ -10,8 +10,10 @@
 // documents by ascending id.  The permutation keeps the order inside every
 // document, so "same document and not after the query" is the same relation
 // before and after it, and the block-sparse kernels run unchanged on the
-// permuted row.  Q and K are gathered by the RoPE pass itself, V, O, dO and
-// LSE by the gathers below, and the results are scattered back.
+// permuted row.  Q and K are gathered by the RoPE pass itself and V and dO
+// (streamed through LDS tiles) by the gather below; every other access to a
+// caller's tensor (O and LSE written by the forward and read by the backward,
+// dq, dk, dv) goes through the permutation inside the kernels.
 //
 // k_chunk_layout sorts the chunks of a row by (document id, chunk index) in
 // LDS and assigns every chunk its place in the permuted row; k_chunk_tokens
@@ -246,29 +248,6 @@ __global__ void k_gather_rows(const bf16* __restrict__ x, const int32_t* __restr
   *(bf16x8*)(y + i * 8) = *(const bf16x8*)(x + ((long long)src[p] * row_vecs + w) * 8);
 }
 
-// y[src[p]] = x[p].
-__global__ void k_scatter_rows(const bf16* __restrict__ x, const int32_t* __restrict__ src,
-                               long long n_vec, int row_vecs, bf16* __restrict__ y) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_vec) return;
-  const long long p = i / row_vecs;
-  const int w = (int)(i % row_vecs);
-  *(bf16x8*)(y + ((long long)src[p] * row_vecs + w) * 8) = *(const bf16x8*)(x + i * 8);
-}
-
-// LSE [B, H, S]: gather (y[b,h,p] = x[b,h,src(p)]) or scatter (y[b,h,src(p)] = x[b,h,p]).
-__global__ void k_move_lse(const float* __restrict__ x, const int32_t* __restrict__ src, int B,
-                           int H, int S, int scatter, float* __restrict__ y) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)B * H * S) return;
-  const long long row = i / S;                   // b * H + h
-  const int pl = (int)(i % S);
-  const long long b = row / H;
-  const int tl = (int)(src[b * S + pl] - b * S);
-  if (scatter) y[row * S + tl] = x[i];
-  else y[i] = x[row * S + tl];
-}
-
 hipError_t launch_chunk_layout(const int32_t* cu, const int32_t* chunk_doc, int n_chunks, int B,
                                int S, int causal, int mode, int anchor, ChunkBufs cb,
                                TokenTables tt, int32_t* status, hipStream_t st) {
@@ -282,23 +261,12 @@ hipError_t launch_chunk_layout(const int32_t* cu, const int32_t* chunk_doc, int 
   return hipGetLastError();
 }
 
-hipError_t launch_move_rows(const bf16* x, const int32_t* src, int B, int S, int H, int D,
-                            bool scatter, bf16* y, hipStream_t st) {
+hipError_t launch_gather_rows(const bf16* x, const int32_t* src, int B, int S, int H, int D,
+                              bf16* y, hipStream_t st) {
   const int row_vecs = H * D / 8;
   const long long n = (long long)B * S * row_vecs;
-  const dim3 grid((unsigned)((n + 255) / 256));
-  if (scatter)
-    hipLaunchKernelGGL(k_scatter_rows, grid, dim3(256), 0, st, x, src, n, row_vecs, y);
-  else
-    hipLaunchKernelGGL(k_gather_rows, grid, dim3(256), 0, st, x, src, n, row_vecs, y);
-  return hipGetLastError();
-}
-
-hipError_t launch_move_lse(const float* x, const int32_t* src, int B, int H, int S, bool scatter,
-                           float* y, hipStream_t st) {
-  const long long n = (long long)B * H * S;
-  hipLaunchKernelGGL(k_move_lse, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, src, B, H,
-                     S, scatter ? 1 : 0, y);
+  hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, src, n,
+                     row_vecs, y);
   return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     const int32_t* __restrict__ qptr, const int32_t* __restrict__ kpack,
     const int32_t* __restrict__ order, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
     int nq, int n_items, float scale_log2, int anchor, bf16* __restrict__ o,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, const int32_t* __restrict__ tok_map) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int NKK = D / 16;    // 16-wide reduction steps over d
   constexpr int NDB = D / 32;    // 32-row blocks of d in O^T
@@ -275,7 +275,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   const float lt = l + partner(l);
   const float inv = 1.f / lt;
   if (qvalid) {
-    bf16* op = o + (tok * Hq + hq) * D;
+    const size_t otok = tok_map ? (size_t)tok_map[tok] : tok;   // where this query's output goes
+    bf16* op = o + (otok * Hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
       }
     if (h == 0) {
       const float val = (m + __log2f(lt)) * 0.69314718055994530942f;
-      lse[((size_t)b * Hq + hq) * S + qrow] = bad ? NAN : val;
+      lse[((size_t)b * Hq + hq) * S + (otok - tok0)] = bad ? NAN : val;
     }
   }
 }
@@ -295,14 +296,14 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
 hipError_t launch_fwd(const bf16* q_raw, const float* table, int npos, bf16* qr, const bf16* kr,
                       const bf16* v, TokenTables tt, const PlanBufs& pb, const int32_t* status,
                       int B, int S, int Hq, int Hkv, int D, float scale, int anchor, bf16* o,
-                      float* lse, hipStream_t st) {
+                      float* lse, const int32_t* tok_map, hipStream_t st) {
   const float scale_log2 = scale * 1.44269504088896340736f;
   const int n_items = B * pb.nq * Hq;
   const dim3 grid(padded_grid(n_items));
 #define AA_LAUNCH_FWD(DD, RQ)                                                                    \
   hipLaunchKernelGGL((k_fwd<DD, RQ>), grid, dim3(256), 0, st, q_raw, table, tt.pos, npos, qr, kr, \
                      v, tt.lo, tt.hi, pb.qptr, pb.kpack, pb.order, status, S, Hq, Hkv, pb.nq,     \
-                     n_items, scale_log2, anchor, o, lse)
+                     n_items, scale_log2, anchor, o, lse, tok_map)
   if (D == 128) {
     if (q_raw) AA_LAUNCH_FWD(128, true);
     else AA_LAUNCH_FWD(128, false);
