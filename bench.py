@@ -143,6 +143,8 @@ def main() -> int:
     ap.add_argument("--no-fwd-workspace", action="store_true",
                     help="self-contained backward: rebuild positions, plan and rotated q, k "
                          "instead of reusing the forward's workspace")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra timing of the step captured in a HIP graph and replayed")
     ap.add_argument("--mode", default="anchor", choices=sorted(MODES),
                     help="anchor (default, the method) | anchor_continuous | intra_doc_reset | "
                          "intra_doc_continuous | full_causal | interleaved: the pages' other "
@@ -231,6 +233,31 @@ def main() -> int:
     per_step = sorted(c.elapsed_time(b) for a, b, c in marks)     # start of step -> end of backward
     median_ms = per_step[len(per_step) // 2]
 
+    # The same step captured once in a HIP graph and replayed: the kernels and
+    # their work are identical, the host launch gaps between them are gone.
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        del graph
+
     fl = flops_fwd_bwd(doc_rows, w.Hq, w.D, anchor=anchor)
     total_flops = fl["total"] if w.backward else fl["fwd"]
     tflops = total_flops / (ms * 1e-3) / 1e12
@@ -263,6 +290,8 @@ def main() -> int:
                    "head_dim": w.D, "rope_base": w.rope_base, "documents_per_row": len(doc_rows[0]),
                    "backward": w.backward, "unmasked_pairs_per_head": fl["pairs_per_head"],
                    "bwd_reuses_forward_workspace": reuse},
+        "graph_ms_per_step": graph_ms,
+        "graph_tflops": (total_flops / (graph_ms * 1e-3) / 1e12) if graph_ms else None,
         "tokens_per_s": tokens / (ms * 1e-3),
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms if w.backward else None,
