@@ -103,6 +103,12 @@ enum {
  *       it; the other entry points reject it.  If the promise does not hold
  *       the results are wrong; nothing detects it. */
 #define AA_FLAG_FWD_WORKSPACE 4
+/*   AA_FLAG_O_FP32  (anchor_attn_fwd_ex, anchor_attn_bwd_ex,
+ *       anchor_attn_fwd_chunks, anchor_attn_bwd_chunks) O is float32
+ *       [B,S,Hq,D] instead of bf16: the forward writes the normalised output
+ *       without the bf16 rounding, and the backward reads O in that dtype
+ *       (16-byte aligned in both cases).  The other entry points reject it. */
+#define AA_FLAG_O_FP32 8
 
 /* Human-readable text for a status code (static storage). */
 const char* anchor_attn_strerror(aa_status s);

@@ -20,6 +20,8 @@ AA_OK, AA_EINVAL, AA_EDOCS, AA_EUNSUPPORTED, AA_EWORKSPACE, AA_EHIP = range(6)
 FLAG_CONTINUOUS_POS, FLAG_NO_ANCHOR = 1, 2
 # anchor_attn_bwd: the workspace still holds the forward's state (see anchor_attn.h)
 FLAG_FWD_WORKSPACE = 4
+# O in float32 instead of bf16 (forward output and backward input)
+FLAG_O_FP32 = 8
 TILE_FULL, TILE_PARTIAL, TILE_ANCHOR = 1, 2, 3
 
 # Tile shapes the attention kernels run with (query tile x key tile).
@@ -109,6 +111,13 @@ def _dev_cu(cu, device) -> torch.Tensor:
     return cu.to(device=device, dtype=torch.int32).contiguous()
 
 
+def _need_o(o: torch.Tensor, flags: int) -> None:
+    want = torch.float32 if flags & FLAG_O_FP32 else torch.bfloat16
+    if o.dtype != want or o.dim() != 4 or not o.is_cuda or not o.is_contiguous():
+        raise ValueError(f"o must be a contiguous {want} CUDA tensor with 4 dims "
+                         "(float32 exactly when FLAG_O_FP32 is set)")
+
+
 def _need_bf16(name: str, t: torch.Tensor, ndim: int = 4) -> None:
     if t.dtype != torch.bfloat16 or t.dim() != ndim or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor with {ndim} dims")
@@ -133,8 +142,9 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 def anchor_attn_fwd(q, k, v, cu_doc_lens, rope_base: float, causal: bool = True,
                     softmax_scale: float | None = None, workspace: torch.Tensor | None = None,
                     flags: int = 0):
-    """Forward pass; returns (o [B,S,Hq,D] bf16, lse [B,Hq,S] fp32).  flags: OR of
-    FLAG_CONTINUOUS_POS / FLAG_NO_ANCHOR (0 = the method, anchor_attn_fwd)."""
+    """Forward pass; returns (o [B,S,Hq,D] bf16, or float32 with FLAG_O_FP32; lse [B,Hq,S]
+    fp32).  flags: OR of FLAG_CONTINUOUS_POS / FLAG_NO_ANCHOR / FLAG_O_FP32 (0 = the
+    method with a bf16 output, anchor_attn_fwd)."""
     lib = load()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _need_bf16(n, t)
@@ -146,7 +156,7 @@ def anchor_attn_fwd(q, k, v, cu_doc_lens, rope_base: float, causal: bool = True,
     ws_n = workspace_size(B, S, Hq, Hkv, D, False)
     if workspace is None or workspace.numel() < ws_n:
         workspace = _workspace(ws_n, q.device)
-    o = torch.empty_like(q)
+    o = torch.empty_like(q, dtype=torch.float32 if flags & FLAG_O_FP32 else torch.bfloat16)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     if flags:
         _check(lib.anchor_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), cu.numel() - 1,
@@ -167,8 +177,9 @@ def anchor_attn_bwd(q, k, v, o, lse, dout, cu_doc_lens, rope_base: float, causal
                     flags: int = 0):
     """Backward pass; returns (dq, dk, dv) bf16.  flags as for anchor_attn_fwd."""
     lib = load()
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+    for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need_bf16(n, t)
+    _need_o(o, flags)
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     if lse.dtype != torch.float32 or lse.shape != (B, Hq, S) or not lse.is_contiguous():
@@ -220,7 +231,7 @@ def anchor_attn_fwd_chunks(q, k, v, cu_chunks, chunk_doc, rope_base: float, caus
     ws_n = chunks_workspace_size(B, S, Hq, Hkv, D, cd.numel(), False)
     if workspace is None or workspace.numel() < ws_n:
         workspace = _workspace(ws_n, q.device)
-    o = torch.empty_like(q)
+    o = torch.empty_like(q, dtype=torch.float32 if flags & FLAG_O_FP32 else torch.bfloat16)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     _check(lib.anchor_attn_fwd_chunks(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), _ptr(cd), cd.numel(),
                                       float(rope_base), int(bool(causal)), int(flags), B, S, Hq, Hkv,
@@ -235,8 +246,9 @@ def anchor_attn_bwd_chunks(q, k, v, o, lse, dout, cu_chunks, chunk_doc, rope_bas
                            workspace: torch.Tensor | None = None, flags: int = 0):
     """Backward pass over interleaved document chunks; returns (dq, dk, dv)."""
     lib = load()
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+    for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need_bf16(n, t)
+    _need_o(o, flags)
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     if lse.dtype != torch.float32 or lse.shape != (B, Hq, S) or not lse.is_contiguous():
@@ -364,8 +376,9 @@ class _AnchorAttnFn(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, o, lse, cu = ctx.saved_tensors
         rope_base, causal, scale, flags = ctx.cfg
-        dq, dk, dv = anchor_attn_bwd(q, k, v, o, lse, do.contiguous(), cu, rope_base, causal, scale,
-                                     ctx.ws, flags=flags | FLAG_FWD_WORKSPACE)
+        # dO is taken in bf16 (an fp32 O's gradient arrives in fp32)
+        dq, dk, dv = anchor_attn_bwd(q, k, v, o, lse, do.to(torch.bfloat16).contiguous(), cu,
+                                     rope_base, causal, scale, ctx.ws, flags=flags | FLAG_FWD_WORKSPACE)
         ctx.ws = None
         return dq, dk, dv, None, None, None, None, None
 

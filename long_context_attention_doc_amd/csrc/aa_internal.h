@@ -90,16 +90,17 @@ hipError_t launch_rope_apply(const bf16* x, const int32_t* src, const int32_t* p
 // rotated q to qr for the backward; otherwise it reads qr, rotated before.
 // With tok_map non-null (rows permuted so that documents are contiguous) the
 // output of position p goes to token tok_map[p] of o and lse.
+// o is bf16, or float32 with o_f32.
 hipError_t launch_fwd(const bf16* q_raw, const float* table, int npos, bf16* qr, const bf16* kr,
                       const bf16* v, TokenTables tt, const PlanBufs& pb, const int32_t* status,
-                      int B, int S, int Hq, int Hkv, int D, float scale, int anchor, bf16* o,
-                      float* lse, const int32_t* tok_map, hipStream_t st);
+                      int B, int S, int Hq, int Hkv, int D, float scale, int anchor, void* o,
+                      int o_f32, float* lse, const int32_t* tok_map, hipStream_t st);
 
 struct BwdArgs {
   const bf16* qr;      // rotated q [B,S,Hq,D]
   const bf16* kr;      // rotated k [B,S,Hkv,D]
   const bf16* v;
-  const bf16* o;
+  const void* o;       // bf16, or float32 with o_f32
   const bf16* dout;
   const float* lse;    // [B,Hq,S]
   const float* table;  // RoPE cos/sin table [S][D/2][2]
@@ -121,6 +122,7 @@ struct BwdArgs {
   // token tok_map[p] of the caller's o, lse, dq, dk, dv; qr, kr, v, dout and
   // the token tables are in permuted order.  Null: no permutation.
   const int32_t* tok_map = nullptr;
+  int o_f32 = 0;
 };
 constexpr int kPreRows = 64;    // rows per block of the backward preprocess
 

@@ -297,7 +297,7 @@ static aa_status fwd_impl(const void* q, const void* k, const void* v, const int
                           int Hkv, int D, float softmax_scale, void* o, float* lse,
                           void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !cu_doc_lens || !o || !lse || !workspace) return AA_EINVAL;
-  if (!flags_ok(flags, AA_FLAG_FWD_WORKSPACE)) return AA_EINVAL;
+  if (!flags_ok(flags, AA_FLAG_FWD_WORKSPACE | AA_FLAG_O_FP32)) return AA_EINVAL;
   if (!shape_ok(B, S, Hq, Hkv, D) || n_seg < B) return AA_EINVAL;
   if (D != 64 && D != 128) return AA_EUNSUPPORTED;
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
@@ -318,8 +318,8 @@ static aa_status fwd_impl(const void* q, const void* k, const void* v, const int
   AA_LAUNCH(AA_K_FWD, stream,
             launch_fwd((const bf16*)q, (const float*)(ws + L.table), S + 1, (bf16*)(ws + L.qrot),
                        (const bf16*)(ws + L.krot), (const bf16*)v, tt, plan_bufs(L.pq, ws),
-                       (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D, scale, anchor, (bf16*)o,
-                       lse, nullptr, stream));
+                       (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D, scale, anchor, o,
+                       (flags & AA_FLAG_O_FP32) ? 1 : 0, lse, nullptr, stream));
   return AA_OK;
 }
 
@@ -330,7 +330,7 @@ static aa_status bwd_impl(const void* q, const void* k, const void* v, const voi
                           void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !dout || !cu_doc_lens || !dq || !dk || !dv || !workspace)
     return AA_EINVAL;
-  if (!flags_ok(flags, AA_FLAG_FWD_WORKSPACE)) return AA_EINVAL;
+  if (!flags_ok(flags, AA_FLAG_FWD_WORKSPACE | AA_FLAG_O_FP32)) return AA_EINVAL;
   if (!shape_ok(B, S, Hq, Hkv, D) || n_seg < B) return AA_EINVAL;
   if (D != 64 && D != 128) return AA_EUNSUPPORTED;
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
@@ -359,7 +359,8 @@ static aa_status bwd_impl(const void* q, const void* k, const void* v, const voi
   a.qr = (const bf16*)(ws + L.qrot);
   a.kr = (const bf16*)(ws + L.krot);
   a.v = (const bf16*)v;
-  a.o = (const bf16*)o;
+  a.o = o;
+  a.o_f32 = (flags & AA_FLAG_O_FP32) ? 1 : 0;
   a.dout = (const bf16*)dout;
   a.lse = lse;
   a.table = (const float*)(ws + L.table);
@@ -429,11 +430,12 @@ size_t anchor_attn_chunks_workspace_size(int B, int S, int Hq, int Hkv, int D, i
 }
 
 static aa_status chunk_args_ok(const int32_t* cu, const int32_t* chunk_doc, int n_chunks, int flags,
-                               int B, int S, int Hq, int Hkv, int D, double rope_base) {
+                               int B, int S, int Hq, int Hkv, int D, double rope_base,
+                               int extra_flags = 0) {
   if (!cu || !chunk_doc) return AA_EINVAL;
   if (!shape_ok(B, S, Hq, Hkv, D) || n_chunks < B) return AA_EINVAL;
   if (D != 64 && D != 128) return AA_EUNSUPPORTED;
-  if (!flags_ok(flags)) return AA_EINVAL;
+  if (!flags_ok(flags, extra_flags)) return AA_EINVAL;
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
   if (!aligned(cu, 4) || !aligned(chunk_doc, 4)) return AA_EINVAL;
   return AA_OK;
@@ -445,7 +447,8 @@ aa_status anchor_attn_fwd_chunks(const void* q, const void* k, const void* v,
                                  int Hkv, int D, float softmax_scale, void* o, float* lse,
                                  void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !workspace) return AA_EINVAL;
-  const aa_status e = chunk_args_ok(cu_chunks, chunk_doc, n_chunks, flags, B, S, Hq, Hkv, D, rope_base);
+  const aa_status e = chunk_args_ok(cu_chunks, chunk_doc, n_chunks, flags, B, S, Hq, Hkv, D, rope_base,
+                                    AA_FLAG_O_FP32);
   if (e != AA_OK) return e;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(lse, 4) || !aligned(workspace, kAlign))
@@ -464,8 +467,8 @@ aa_status anchor_attn_fwd_chunks(const void* q, const void* k, const void* v,
   AA_LAUNCH(AA_K_FWD, stream,
             launch_fwd(nullptr, nullptr, 0, (bf16*)(ws + L.qrot), (const bf16*)(ws + L.krot),
                        (const bf16*)(ws + C.vperm), tt, plan_bufs(L.pq, ws),
-                       (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D, scale, anchor,
-                       (bf16*)o, lse, src, stream));
+                       (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D, scale, anchor, o,
+                       (flags & AA_FLAG_O_FP32) ? 1 : 0, lse, src, stream));
   return AA_OK;
 }
 
@@ -476,7 +479,8 @@ aa_status anchor_attn_bwd_chunks(const void* q, const void* k, const void* v, co
                                  float softmax_scale, void* dq, void* dk, void* dv,
                                  void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return AA_EINVAL;
-  const aa_status e = chunk_args_ok(cu_chunks, chunk_doc, n_chunks, flags, B, S, Hq, Hkv, D, rope_base);
+  const aa_status e = chunk_args_ok(cu_chunks, chunk_doc, n_chunks, flags, B, S, Hq, Hkv, D, rope_base,
+                                    AA_FLAG_O_FP32);
   if (e != AA_OK) return e;
   const void* ptrs16[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : ptrs16)
@@ -498,7 +502,8 @@ aa_status anchor_attn_bwd_chunks(const void* q, const void* k, const void* v, co
   a.qr = (const bf16*)(ws + L.qrot);
   a.kr = (const bf16*)(ws + L.krot);
   a.v = (const bf16*)(ws + C.vperm);
-  a.o = (const bf16*)o;
+  a.o = o;
+  a.o_f32 = (flags & AA_FLAG_O_FP32) ? 1 : 0;
   a.dout = (const bf16*)(ws + C.doperm);
   a.lse = lse;
   a.table = (const float*)(ws + L.table);

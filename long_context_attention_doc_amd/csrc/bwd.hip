@@ -38,7 +38,8 @@ constexpr float kLog2e = 1.44269504088896340736f;
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_pre(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
-    const bf16* __restrict__ o, const bf16* __restrict__ dout, const float* __restrict__ lse,
+    const void* __restrict__ o, int o_f32, const bf16* __restrict__ dout,
+    const float* __restrict__ lse,
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi, int S, int Hq, int Hkv,
     int nblk, float scale, int anchor, float* __restrict__ dvec, float* __restrict__ ds0,
     float* __restrict__ part_dk, float* __restrict__ part_dv, float* __restrict__ qstats,
@@ -71,13 +72,23 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
     const size_t otok = tok_map ? (size_t)tok_map[tok] : tok;   // the caller's O and LSE row
     const size_t off = (tok * Hq + hq) * D + f0;
     const bf16x8 qv = *(const bf16x8*)(qr + off);
-    const bf16x8 ov = *(const bf16x8*)(o + (otok * Hq + hq) * D + f0);
+    float of[8];
+    if (o_f32) {
+      const f32x4* op = (const f32x4*)((const float*)o + (otok * Hq + hq) * D + f0);
+      const f32x4 o0 = op[0], o1 = op[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { of[i] = o0[i]; of[4 + i] = o1[i]; }
+    } else {
+      const bf16x8 ov = *(const bf16x8*)((const bf16*)o + (otok * Hq + hq) * D + f0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) of[i] = (float)ov[i];
+    }
     const bf16x8 dv = *(const bf16x8*)(dout + off);
     float d_o = 0.f, s0 = 0.f, dp0 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float g = (float)dv[i];
-      d_o += g * (float)ov[i];
+      d_o += g * of[i];
       s0 += (float)qv[i] * k0[i];
       dp0 += g * v0[i];
     }
@@ -526,11 +537,11 @@ hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
   if (a.D == 128)
-    hipLaunchKernelGGL(k_bwd_pre<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.dout,
+    hipLaunchKernelGGL(k_bwd_pre<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.o_f32, a.dout,
                        a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.dvec, a.ds0,
                        a.part_dk, a.part_dv, a.qstats, a.tok_map);
   else
-    hipLaunchKernelGGL(k_bwd_pre<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.dout,
+    hipLaunchKernelGGL(k_bwd_pre<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.o_f32, a.dout,
                        a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.dvec, a.ds0,
                        a.part_dk, a.part_dv, a.qstats, a.tok_map);
   return hipGetLastError();

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
     const int32_t* __restrict__ qptr, const int32_t* __restrict__ kpack,
     const int32_t* __restrict__ order, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
-    int nq, int n_items, float scale_log2, int anchor, bf16* __restrict__ o,
+    int nq, int n_items, float scale_log2, int anchor, void* __restrict__ o, int o_f32,
     float* __restrict__ lse, const int32_t* __restrict__ tok_map) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int NKK = D / 16;    // 16-wide reduction steps over d
@@ -276,15 +276,23 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   const float inv = 1.f / lt;
   if (qvalid) {
     const size_t otok = tok_map ? (size_t)tok_map[tok] : tok;   // where this query's output goes
-    bf16* op = o + (otok * Hq + hq) * D;
+    const size_t orow = (otok * Hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4 w;
+        f32x4 w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = (bf16)(bad ? NAN : acc[db][4 * g + r] * inv);
-        *(bf16x4*)(op + 32 * db + 8 * g + 4 * h) = w;
+        for (int r = 0; r < 4; ++r) w[r] = bad ? NAN : acc[db][4 * g + r] * inv;
+        const int d0 = 32 * db + 8 * g + 4 * h;
+        if (o_f32) {
+          *(f32x4*)((float*)o + orow + d0) = w;
+        } else {
+          bf16x4 wb;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) wb[r] = (bf16)w[r];
+          *(bf16x4*)((bf16*)o + orow + d0) = wb;
+        }
       }
     if (h == 0) {
       const float val = (m + __log2f(lt)) * 0.69314718055994530942f;
@@ -295,15 +303,15 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
 
 hipError_t launch_fwd(const bf16* q_raw, const float* table, int npos, bf16* qr, const bf16* kr,
                       const bf16* v, TokenTables tt, const PlanBufs& pb, const int32_t* status,
-                      int B, int S, int Hq, int Hkv, int D, float scale, int anchor, bf16* o,
-                      float* lse, const int32_t* tok_map, hipStream_t st) {
+                      int B, int S, int Hq, int Hkv, int D, float scale, int anchor, void* o,
+                      int o_f32, float* lse, const int32_t* tok_map, hipStream_t st) {
   const float scale_log2 = scale * 1.44269504088896340736f;
   const int n_items = B * pb.nq * Hq;
   const dim3 grid(padded_grid(n_items));
 #define AA_LAUNCH_FWD(DD, RQ)                                                                    \
   hipLaunchKernelGGL((k_fwd<DD, RQ>), grid, dim3(256), 0, st, q_raw, table, tt.pos, npos, qr, kr, \
                      v, tt.lo, tt.hi, pb.qptr, pb.kpack, pb.order, status, S, Hq, Hkv, pb.nq,     \
-                     n_items, scale_log2, anchor, o, lse, tok_map)
+                     n_items, scale_log2, anchor, o, o_f32, lse, tok_map)
   if (D == 128) {
     if (q_raw) AA_LAUNCH_FWD(128, true);
     else AA_LAUNCH_FWD(128, false);

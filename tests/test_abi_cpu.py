@@ -75,11 +75,13 @@ def test_argument_errors_before_launch(lib):
     rc = lib.anchor_attn_tile_plan(fake, 4, 1, 256, 48, 64, 1, 0, fake, fake, fake, fake, fake, fake,
                                    fake, fake, 1 << 40, None)
     assert rc == api.AA_EUNSUPPORTED
-    # unknown option bits are rejected before anything is launched
+    # unknown option bits are rejected before anything is launched (a bit no
+    # option will take: a call that passed validation would launch kernels)
+    UNKNOWN = 1 << 20
     rc = lib.anchor_attn_tile_plan(fake, 4, 1, 256, 64, 64, 1, 4, fake, fake, fake, fake, fake, fake,
                                    fake, fake, 1 << 40, None)
     assert rc == api.AA_EINVAL
-    rc = lib.anchor_attn_fwd_ex(fake, fake, fake, fake, 4, 1e4, 1, 8, 1, 256, 4, 2, 128, 0.0,
+    rc = lib.anchor_attn_fwd_ex(fake, fake, fake, fake, 4, 1e4, 1, UNKNOWN, 1, 256, 4, 2, 128, 0.0,
                                 fake, fake, fake, 1 << 40, None)
     assert rc == api.AA_EINVAL
     # the forward-workspace promise is only for the forward/backward pair
@@ -88,16 +90,26 @@ def test_argument_errors_before_launch(lib):
     rc = lib.anchor_attn_fwd_chunks(fake, fake, fake, fake, fake, 4, 1e4, 1, 4, 1, 256, 4, 2, 128,
                                     0.0, fake, fake, fake, 1 << 40, None)
     assert rc == api.AA_EINVAL
-    rc = lib.anchor_attn_bwd_ex(fake, fake, fake, fake, fake, fake, fake, 4, 1e4, 1, 8, 1, 256, 4, 2,
+    rc = lib.anchor_attn_bwd_ex(fake, fake, fake, fake, fake, fake, fake, 4, 1e4, 1, UNKNOWN, 1, 256, 4, 2,
                                 128, 0.0, fake, fake, fake, fake, 1 << 40, None)
     assert rc == api.AA_EINVAL
     rc = lib.anchor_attn_position_ids(fake, 4, 1, 256, 4, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    # the float32-output option is for the attention entry points only
+    assert api.FLAG_O_FP32 == 8
+    rc = lib.anchor_attn_position_ids(fake, 4, 1, 256, api.FLAG_O_FP32, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    rc = lib.anchor_attn_tile_plan(fake, 4, 1, 256, 64, 64, 1, api.FLAG_O_FP32, fake, fake, fake, fake,
+                                   fake, fake, fake, fake, 1 << 40, None)
+    assert rc == api.AA_EINVAL
+    rc = lib.anchor_attn_chunk_layout(fake, fake, 4, 1, 256, 1, api.FLAG_O_FP32, fake, fake, fake,
+                                      1 << 40, None)
     assert rc == api.AA_EINVAL
     # interleaved-chunk entry points: null chunk arrays, unknown flags, too few chunks
     rc = lib.anchor_attn_fwd_chunks(fake, fake, fake, None, fake, 4, 1e4, 1, 0, 1, 256, 4, 2, 128,
                                     0.0, fake, fake, fake, 1 << 40, None)
     assert rc == api.AA_EINVAL
-    rc = lib.anchor_attn_fwd_chunks(fake, fake, fake, fake, fake, 4, 1e4, 1, 8, 1, 256, 4, 2, 128,
+    rc = lib.anchor_attn_fwd_chunks(fake, fake, fake, fake, fake, 4, 1e4, 1, UNKNOWN, 1, 256, 4, 2, 128,
                                     0.0, fake, fake, fake, 1 << 40, None)
     assert rc == api.AA_EINVAL
     rc = lib.anchor_attn_bwd_chunks(fake, fake, fake, fake, fake, fake, fake, fake, 1, 1e4, 1, 0, 2,

@@ -108,6 +108,39 @@ def test_fwd_bwd_modes_full_compare(gpu_lib, case):
     assert max(e) <= G_TOL, e
 
 
+@pytest.mark.parametrize("case", [
+    ("ragged_gqa_d128", 2, 1000, 4, 2, 128, None, 5e6, True),
+    ("heads16_d64", 1, 1500, 16, 4, 64, [[900, 20, 579]], 1e4, True),
+    ("noncausal", 1, 600, 2, 2, 128, [[100, 1, 250, 248]], 1e4, False),
+], ids=lambda c: c[0])
+def test_fp32_output(gpu_lib, case):
+    """FLAG_O_FP32: the forward writes O in float32 (the bf16 output is exactly
+    its round-to-nearest-even), the LSE is unchanged, and the backward takes
+    the float32 O; both against the oracle."""
+    name, B, S, Hq, Hkv, D, rows, base, causal = case
+    if rows is None:
+        rng = np.random.default_rng(2024)
+        rows = [W.random_partition(rng, S, 30) for _ in range(B)]
+    cu = W.cu_doc_lens_from_lengths(rows, S)
+    q, k, v, do = _inputs(B, S, Hq, Hkv, D, 1234)
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    f32 = gpu_lib.FLAG_O_FP32
+    o32, lse32 = gpu_lib.anchor_attn_fwd(qc, kc, vc, cu, base, causal, flags=f32)
+    o16, lse16 = gpu_lib.anchor_attn_fwd(qc, kc, vc, cu, base, causal)
+    assert o32.dtype == torch.float32 and o16.dtype == torch.bfloat16
+    assert torch.equal(o32.to(torch.bfloat16), o16) and torch.equal(lse32, lse16)
+    o_ref, lse_ref, _, _ = oracle.forward(q, k, v, cu, base, causal)
+    e32 = o_err(f64(o32).reshape(B * S, Hq, D), o_ref)
+    e16 = o_err(f64(o16).reshape(B * S, Hq, D), o_ref)
+    dq, dk, dv = gpu_lib.anchor_attn_bwd(qc, kc, vc, o32, lse32, doc, cu, base, causal, flags=f32)
+    dq_r, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, base, causal)
+    e = (rel_frob(f64(dq).reshape(B * S, Hq, D), dq_r), rel_frob(f64(dk).reshape(B * S, Hkv, D), dk_r),
+         rel_frob(f64(dv).reshape(B * S, Hkv, D), dv_r))
+    say(f"[fp32-o] {name} O err fp32 {e32:.2e} (bf16 output {e16:.2e}) dq {e[0]:.2e} dk {e[1]:.2e} "
+        f"dv {e[2]:.2e}")
+    assert e32 <= O_TOL and max(e) <= G_TOL
+
+
 def test_interleaved_heads_bit_identical(gpu_lib):
     """16 query heads over few tiles: the work order walks an XCD's slice rank-
     major across its two heads.  Each (head, tile) item is computed the same
