@@ -111,6 +111,29 @@ def _dev_cu(cu, device) -> torch.Tensor:
     return cu.to(device=device, dtype=torch.int32).contiguous()
 
 
+def _check_host_cu(cu, B: int, S: int, anchor: bool) -> None:
+    """The segment layout rules, checked on a host copy of cu_doc_lens before
+    anything is launched (the device checks them again): cu[0] = 0, strictly
+    increasing, cu[-1] = B*S, no segment crosses a row start, and with the
+    anchor every row starts with a one-token anchor segment."""
+    import numpy as np
+    a = np.asarray(cu.cpu() if isinstance(cu, torch.Tensor) else cu, dtype=np.int64).reshape(-1)
+    if a.size < 2 or a[0] != 0 or a[-1] != B * S:
+        raise ValueError(f"cu_doc_lens must run from 0 to B*S = {B * S}")
+    if np.any(np.diff(a) <= 0):
+        raise ValueError("cu_doc_lens must be strictly increasing (no empty segment)")
+    starts = np.arange(B, dtype=np.int64) * S
+    if not np.all(np.isin(starts, a)):
+        raise ValueError("a segment of cu_doc_lens crosses the start of a row")
+    if anchor and S > 1 and not np.all(np.isin(starts + 1, a)):
+        raise ValueError("every row must start with a one-token anchor segment")
+
+
+def _check_cu(cu, B: int, S: int, flags: int) -> None:
+    if not (isinstance(cu, torch.Tensor) and cu.is_cuda):
+        _check_host_cu(cu, B, S, not flags & FLAG_NO_ANCHOR)
+
+
 def _need_o(o: torch.Tensor, flags: int) -> None:
     want = torch.float32 if flags & FLAG_O_FP32 else torch.bfloat16
     if o.dtype != want or o.dim() != 4 or not o.is_cuda or not o.is_contiguous():
@@ -144,8 +167,10 @@ def anchor_attn_fwd(q, k, v, cu_doc_lens, rope_base: float, causal: bool = True,
                     flags: int = 0):
     """Forward pass; returns (o [B,S,Hq,D] bf16, or float32 with FLAG_O_FP32; lse [B,Hq,S]
     fp32).  flags: OR of FLAG_CONTINUOUS_POS / FLAG_NO_ANCHOR / FLAG_O_FP32 (0 = the
-    method with a bf16 output, anchor_attn_fwd)."""
+    method with a bf16 output, anchor_attn_fwd).  A host cu_doc_lens is validated here
+    before anything is launched."""
     lib = load()
+    _check_cu(cu_doc_lens, q.shape[0], q.shape[1], flags)
     for n, t in (("q", q), ("k", k), ("v", v)):
         _need_bf16(n, t)
     B, S, Hq, D = q.shape
@@ -177,6 +202,7 @@ def anchor_attn_bwd(q, k, v, o, lse, dout, cu_doc_lens, rope_base: float, causal
                     flags: int = 0):
     """Backward pass; returns (dq, dk, dv) bf16.  flags as for anchor_attn_fwd."""
     lib = load()
+    _check_cu(cu_doc_lens, q.shape[0], q.shape[1], flags)
     for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need_bf16(n, t)
     _need_o(o, flags)

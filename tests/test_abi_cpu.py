@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -122,3 +123,30 @@ def test_argument_errors_before_launch(lib):
     assert rc == api.AA_EWORKSPACE
     rc = lib.anchor_attn_rope(fake, fake, 1, 256, 2, 80, 1e4, fake, fake, None)
     assert rc == api.AA_EUNSUPPORTED
+
+
+def test_python_binding_checks_host_cu():
+    """The binding validates a host cu_doc_lens before any launch: layout
+    errors raise ValueError naming cu_doc_lens; a valid layout gets past the
+    check (and stops at the CPU tensors)."""
+    import torch
+    from long_context_attention_doc_amd import api
+    q = torch.zeros((2, 8, 2, 64), dtype=torch.bfloat16)
+    kv = torch.zeros((2, 8, 1, 64), dtype=torch.bfloat16)
+    bad = {
+        "not ending at B*S": [0, 1, 8, 9, 15],
+        "empty segment": [0, 1, 1, 8, 9, 16],
+        "crossing a row": [0, 1, 10, 16],
+        "no anchor segment": [0, 8, 9, 16],
+    }
+    for why, cu in bad.items():
+        with pytest.raises(ValueError, match="cu_doc_lens|anchor|row"):
+            api.anchor_attn_fwd(q, kv, kv, np.asarray(cu, dtype=np.int32), 1e4)
+    # without the anchor option a row may start with a document
+    with pytest.raises(ValueError, match="CUDA"):
+        api.anchor_attn_fwd(q, kv, kv, np.asarray([0, 8, 9, 16], dtype=np.int32), 1e4,
+                            flags=api.FLAG_NO_ANCHOR)
+    with pytest.raises(ValueError, match="CUDA"):
+        api.anchor_attn_fwd(q, kv, kv, np.asarray([0, 1, 5, 8, 9, 16], dtype=np.int32), 1e4)
+    with pytest.raises(ValueError, match="cu_doc_lens"):
+        api.anchor_attn_bwd(q, kv, kv, q, torch.zeros((2, 2, 8)), q, [0, 1, 8, 9, 15], 1e4)

@@ -167,5 +167,9 @@ def test_device_status_flags_bad_documents(gpu_lib):
     pos, ws = gpu_lib.anchor_attn_position_ids(bad, 1, S)
     assert gpu_lib.anchor_attn_device_status(ws) == gpu_lib.AA_EDOCS
     q = torch.randn((1, S, 2, 64)).to(torch.bfloat16).cuda()
-    o, lse = gpu_lib.anchor_attn_fwd(q, q, q, bad, 1e4)
+    # a host copy is refused by the binding before any launch ...
+    with pytest.raises(ValueError, match="anchor"):
+        gpu_lib.anchor_attn_fwd(q, q, q, bad, 1e4)
+    # ... a device copy reaches the kernels, which flag it and NaN-fill the outputs
+    o, lse = gpu_lib.anchor_attn_fwd(q, q, q, torch.from_numpy(bad).cuda(), 1e4)
     assert torch.isnan(o.float()).all() and torch.isnan(lse).all()
