@@ -114,6 +114,29 @@ def test_fwd_bwd_interleaved(gpu_lib, case):
     assert max(e) <= G_TOL, e
 
 
+def test_interleaved_fp32_output(gpu_lib):
+    """FLAG_O_FP32 through the chunk entry points: the float32 O goes through
+    the permutation to the caller's order (the bf16 O is exactly its rounding)
+    and the backward reads it through the permutation; against the oracle."""
+    name, seed, B, S, Hq, Hkv, D, anchor, fpos, causal, max_docs, max_chunks = _cases()[0]
+    cu, cd = _layout(100 + seed, B, S, anchor, max_docs, max_chunks)
+    q, k, v, do = W.make_tensors(B, S, Hq, Hkv, D, 900 + seed)
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    f32 = gpu_lib.FLAG_O_FP32
+    o16, lse16 = gpu_lib.anchor_attn_fwd_chunks(qc, kc, vc, cu, cd, 1e4, causal)
+    o32, lse32 = gpu_lib.anchor_attn_fwd_chunks(qc, kc, vc, cu, cd, 1e4, causal, flags=f32)
+    assert o32.dtype == torch.float32
+    assert torch.equal(o32.to(torch.bfloat16), o16) and torch.equal(lse32, lse16)
+    o_ref, _, _, _ = oracle.forward(q, k, v, cu, 1e4, causal, anchor=anchor, seg_doc=cd)
+    e_o = o_err(f64(o32).reshape(B * S, Hq, D), o_ref)
+    dq, dk, dv = gpu_lib.anchor_attn_bwd_chunks(qc, kc, vc, o32, lse32, doc, cu, cd, 1e4, causal, flags=f32)
+    dq_r, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, 1e4, causal, anchor=anchor, seg_doc=cd)
+    e = (rel_frob(f64(dq).reshape(B * S, Hq, D), dq_r), rel_frob(f64(dk).reshape(B * S, Hkv, D), dk_r),
+         rel_frob(f64(dv).reshape(B * S, Hkv, D), dv_r))
+    say(f"[chunks] fp32 O {e_o:.2e} dq {e[0]:.2e} dk {e[1]:.2e} dv {e[2]:.2e}")
+    assert e_o <= O_TOL and max(e) <= G_TOL, (e_o, e)
+
+
 def test_interleaved_64k_sampled(gpu_lib):
     """The 64K documents cut into up to 4 chunks each and interleaved; the
     benchmark's shapes; uniformly sampled rows, keys in short documents."""
