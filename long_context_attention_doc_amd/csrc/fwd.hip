@@ -58,7 +58,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   constexpr int NKB = BN / 32;   // 32-key blocks of a key tile
   using T = SwzTile<D>;
   constexpr int NBUF = kFwdStages;
-  constexpr int LPT = 2 * (BN * (D / 8) / 256);   // direct-load instructions per wave and tile
   __shared__ __align__(16) bf16 Ks[NBUF][BN * D];
   __shared__ __align__(16) bf16 Vs[NBUF][BN * D];
 

@@ -137,7 +137,7 @@ __global__ void k_scan(const int32_t* __restrict__ cnt, int n, int32_t* __restri
     buf[threadIdx.x] = x;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
-      const int y = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+      const int y = (int)threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
       __syncthreads();
       buf[threadIdx.x] += y;
       __syncthreads();
