@@ -138,7 +138,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="64k",
-                    help="tiny | 8k | 64k | 128k_gqa | short_docs (default: 64k, the headline)")
+                    help="tiny | 8k | 64k | 128k_gqa | short_docs | 64k_ulysses8 (one GPU's head share of 64K "
+                         "over 8 GPUs) (default: 64k, the headline)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--no-fwd-workspace", action="store_true",
                     help="self-contained backward: rebuild positions, plan and rotated q, k "

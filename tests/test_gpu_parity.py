@@ -235,7 +235,7 @@ def _sample_keys(w, rng, n, max_doc=2500):
     return np.array(sorted(keys[i] for i in pick))
 
 
-@pytest.mark.parametrize("wname", ["8k", "64k", "128k_gqa", "short_docs"])
+@pytest.mark.parametrize("wname", ["8k", "64k", "128k_gqa", "short_docs", "64k_ulysses8"])
 def test_full_size_sampled(gpu_lib, wname):
     """The benchmark's shapes and launch configuration; sampled outputs."""
     w = W.get(wname)

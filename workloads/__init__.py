@@ -167,6 +167,10 @@ def _mk_workloads() -> dict[str, Workload]:
         "128k_gqa", 1, 131072, 32, 8, 128, 5e5, True,
         (tuple(sample_doc_lengths(131072, 4096, 1.2, 64, 131071, 3)),), 1003,
         "GQA: batch 1, seq 131072, 32 query heads / 8 KV heads, head_dim 128, lognormal docs (median 4096, sigma 1.2)")
+    w["64k_ulysses8"] = Workload(
+        "64k_ulysses8", 1, 65536, 4, 4, 128, 5e6, True, w["64k"].doc_rows, 1005,
+        "one GPU's share of the 64K workload under head sharding over 8 GPUs (Ulysses): the same "
+        "documents, 4 of the 32 heads")
     short_row = tuple([256] * 127 + [32768 - 1 - 127 * 256])
     w["short_docs"] = Workload(
         "short_docs", 2, 32768, 32, 32, 128, 5e6, True, (short_row, short_row), 1004,
