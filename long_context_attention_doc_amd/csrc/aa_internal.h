@@ -350,18 +350,35 @@ __device__ __forceinline__ int xcd_work_item(int linear, int total) {
 constexpr int kOrderLpt = 1, kOrderInterleave = 2;
 constexpr int kInterleaveMaxTiles = 128;
 
-// Work item w -> (head, rank of its tile in the order).
-__device__ __forceinline__ void head_and_rank(int w, int T, int H, int flags, int& head,
-                                              int& rank) {
-  if ((flags & kOrderInterleave) && H % kXcds == 0) {
+// Workgroup -> (head, rank of its tile in the order), or false for a padding
+// workgroup.  When H is a multiple of the XCD count each XCD walks whole
+// heads (xcd_work_item), as described with kOrderInterleave.  Otherwise an
+// XCD's slice would hold part of a head, and in longest-first order the
+// first slice would get that head's long tiles and the next one its short
+// tiles; there the workgroups take the items rank-major across heads in
+// plain launch order, so that the dispatcher's round-robin deals every
+// rank's tiles evenly over the XCDs.
+__device__ __forceinline__ bool work_head_rank(int T, int H, int flags, int& head, int& rank) {
+  const int n_items = T * H;
+  if (H % kXcds != 0) {
+    const int w = blockIdx.x;
+    if (w >= n_items) return false;
+    head = w % H;
+    rank = w / H;
+    return true;
+  }
+  const int w = xcd_work_item(blockIdx.x, n_items);
+  if (w < 0) return false;
+  if (flags & kOrderInterleave) {
     const int G = H / kXcds, slice = G * T;
     const int x = w / slice, u = w - x * slice;
     head = x * G + u % G;
     rank = u / G;
-    return;
+    return true;
   }
   head = w / T;
   rank = w - head * T;
+  return true;
 }
 
 // Packed plan entries: tile index in the low 24 bits, kind in the high 8.

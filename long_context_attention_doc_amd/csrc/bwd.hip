@@ -169,11 +169,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   __shared__ __align__(16) float s_st[2][4][BM];     // LSE*log2(e), Dv, lo, hi (int bits)
   __shared__ __align__(16) bf16 Ks[BN * D];          // this workgroup's keys (rotated)
 
-  const int item = xcd_work_item(blockIdx.x, n_items);   // (hkv, b, kt), kt fastest
-  if (item < 0) return;
   int hkv, ktile;   // ktile = b * nk + kt, in natural order: within a document the
                     // key tiles already go from the most query tiles to the fewest
-  head_and_rank(item, n_items / Hkv, Hkv, *order_flags, hkv, ktile);
+  if (!work_head_rank(n_items / Hkv, Hkv, *order_flags, hkv, ktile)) return;
   const int b = ktile / nk, kt = ktile % nk;
   const int group = Hq / Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -353,11 +351,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   __shared__ __align__(16) bf16 Ks[NBUF][BN * D];
   __shared__ __align__(16) bf16 Vs[NBUF][BN * D];
 
-  const int item = xcd_work_item(blockIdx.x, n_items);   // (hq, b, qt), qt fastest
-  if (item < 0) return;
   const int tiles_per_head = n_items / Hq;
   int hq, rank;
-  head_and_rank(item, tiles_per_head, Hq, order[tiles_per_head], hq, rank);
+  if (!work_head_rank(tiles_per_head, Hq, order[tiles_per_head], hq, rank)) return;
   const int tile = order[rank];   // b * nq + qt
   const int b = tile / nq, qt = tile % nq;
   const int hkv = hq / (Hq / Hkv);

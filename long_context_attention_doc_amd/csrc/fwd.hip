@@ -61,11 +61,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   __shared__ __align__(16) bf16 Ks[NBUF][BN * D];
   __shared__ __align__(16) bf16 Vs[NBUF][BN * D];
 
-  const int item = xcd_work_item(blockIdx.x, n_items);   // (hq, b, qt), qt fastest
-  if (item < 0) return;
   const int tiles_per_head = n_items / Hq;
   int hq, rank;
-  head_and_rank(item, tiles_per_head, Hq, order[tiles_per_head], hq, rank);
+  if (!work_head_rank(tiles_per_head, Hq, order[tiles_per_head], hq, rank)) return;
   const int tile = order[rank];   // b * nq + qt
   const int b = tile / nq, qt = tile % nq;
   const int hkv = hq / (Hq / Hkv);
