@@ -236,6 +236,20 @@ aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, in
                                 int32_t* n_live, void* workspace, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* Work order of the query tiles of a query-major plan: the order the
+ * attention kernels take them in (scheduling only; no result depends on
+ * it).  cnt: int32 [n], live key tiles per query tile (qptr differences);
+ * order: int32 [n + 1] receives the tiles in launch order, then the flags:
+ *   AA_ORDER_LPT        the largest count exceeds 1.5x the mean: tiles by
+ *                       descending count, ties by index (longest
+ *                       processing time first); otherwise order[i] = i;
+ *   AA_ORDER_INTERLEAVE n <= 128, or the natural order: the tiles of the
+ *                       heads of an XCD's slice are taken rank by rank.
+ * Plans of more than 16384 tiles keep the natural order with flags 0. */
+#define AA_ORDER_LPT 1
+#define AA_ORDER_INTERLEAVE 2
+aa_status anchor_attn_tile_order(const int32_t* cnt, int n, int32_t* order, hipStream_t stream);
+
 /* RoPE stage alone (Eq. 6; angle pos*theta_p formed and reduced in float64,
  * cos/sin rounded to float32, pair rotated in float32, result rounded to
  * bf16 to nearest even).  x, x_rot: [B,S,H,D] bf16; pos: int32 [B*S] with

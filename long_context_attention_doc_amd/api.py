@@ -35,7 +35,7 @@ EXPORTS = (
     "anchor_attn_chunk_layout",
     "anchor_attn_position_ids",
     "anchor_attn_plan_workspace_size", "anchor_attn_plan_capacity", "anchor_attn_tile_plan",
-    "anchor_attn_rope", "anchor_attn_device_status", "anchor_attn_profile_begin",
+    "anchor_attn_tile_order", "anchor_attn_rope", "anchor_attn_device_status", "anchor_attn_profile_begin",
     "anchor_attn_profile_end",
 )
 KERNEL_IDS = ("status", "positions", "plan", "rope_table", "rope", "fwd", "bwd_pre", "bwd_dkdv",
@@ -79,6 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "anchor_attn_plan_workspace_size": (Z, [I, I, I, I]),
         "anchor_attn_plan_capacity": (Z, [I, I, I, I]),
         "anchor_attn_tile_plan": (I, [P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P]),
+        "anchor_attn_tile_order": (I, [P, I, P, P]),
         "anchor_attn_rope": (I, [P, P, I, I, I, I, D, P, P, P]),
         "anchor_attn_device_status": (I, [P, P, P]),
         "anchor_attn_profile_begin": (I, [I]),
@@ -348,6 +349,22 @@ def anchor_attn_tile_plan(cu_doc_lens, B: int, S: int, BM: int, BN: int, causal:
                                      _stream(ws.device)), "anchor_attn_tile_plan")
     out["workspace"] = ws
     out["nq"], out["nk"] = nq, nk
+    return out
+
+
+ORDER_LPT, ORDER_INTERLEAVE = 1, 2
+
+
+def anchor_attn_tile_order(cnt: torch.Tensor) -> torch.Tensor:
+    """Work order of a query-major plan: cnt int32 [n] (live key tiles per query
+    tile) -> int32 [n + 1], the tiles in launch order and then the flags
+    (ORDER_LPT, ORDER_INTERLEAVE)."""
+    lib = load()
+    if cnt.dtype != torch.int32 or cnt.dim() != 1 or not cnt.is_cuda or not cnt.is_contiguous():
+        raise ValueError("cnt must be a contiguous int32 CUDA vector")
+    out = torch.empty(cnt.numel() + 1, dtype=torch.int32, device=cnt.device)
+    _check(lib.anchor_attn_tile_order(_ptr(cnt), cnt.numel(), _ptr(out), _stream(cnt.device)),
+           "anchor_attn_tile_order")
     return out
 
 

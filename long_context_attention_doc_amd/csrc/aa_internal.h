@@ -81,6 +81,7 @@ hipError_t launch_chunk_layout(const int32_t* cu, const int32_t* chunk_doc, int 
                                int S, int causal, int mode, int anchor, ChunkBufs cb,
                                TokenTables tt, int32_t* status, hipStream_t st);
 // y[p] = x[src[p]] for rows of H*D elements (one token's heads).
+hipError_t launch_tile_order(const int32_t* cnt, int n, int32_t* order, hipStream_t st);
 hipError_t launch_gather_rows(const bf16* x, const int32_t* src, int B, int S, int H, int D,
                               bf16* y, hipStream_t st);
 hipError_t launch_rope_apply(const bf16* x, const int32_t* src, const int32_t* pos, const float* table, int npos, int B, int S,
@@ -347,7 +348,7 @@ __device__ __forceinline__ int xcd_work_item(int linear, int total) {
 //                    together and their K/V rows are adjacent in HBM).  With
 //                    many tiles per head and uneven work, head after head
 //                    keeps one head's concurrent tiles on shared K/V in L2.
-constexpr int kOrderLpt = 1, kOrderInterleave = 2;
+constexpr int kOrderLpt = 1, kOrderInterleave = 2;   // AA_ORDER_LPT, AA_ORDER_INTERLEAVE
 constexpr int kInterleaveMaxTiles = 128;
 
 // Workgroup -> (head, rank of its tile in the order), or false for a padding

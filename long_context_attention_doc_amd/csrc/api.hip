@@ -620,6 +620,16 @@ aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, in
   return AA_OK;
 }
 
+static_assert(kOrderLpt == AA_ORDER_LPT && kOrderInterleave == AA_ORDER_INTERLEAVE,
+              "work-order flags of the header and the kernels");
+
+aa_status anchor_attn_tile_order(const int32_t* cnt, int n, int32_t* order, hipStream_t stream) {
+  if (!cnt || !order || n < 1 || n == 0x7fffffff) return AA_EINVAL;
+  if (!aligned(cnt, 4) || !aligned(order, 4)) return AA_EINVAL;
+  AA_HIP(launch_tile_order(cnt, n, order, stream));
+  return AA_OK;
+}
+
 aa_status anchor_attn_rope(const void* x, const int32_t* pos, int B, int S, int H, int D,
                            double rope_base, void* x_rot, float* table, hipStream_t stream) {
   if (!x || !pos || !x_rot || !table) return AA_EINVAL;

@@ -262,6 +262,12 @@ __global__ __launch_bounds__(256) void k_tile_order(const int32_t* __restrict__ 
   order[rank] = i;
 }
 
+hipError_t launch_tile_order(const int32_t* cnt, int n, int32_t* order, hipStream_t st) {
+  hipLaunchKernelGGL(k_tile_order, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cnt, n,
+                     order);
+  return hipGetLastError();
+}
+
 hipError_t launch_positions(const int32_t* cu, int n_seg, int B, int S, int causal, int mode,
                             int anchor, TokenTables tt, int32_t* status, hipStream_t st) {
   const long long total = (long long)B * S;

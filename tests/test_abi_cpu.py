@@ -96,6 +96,10 @@ def test_argument_errors_before_launch(lib):
     assert rc == api.AA_EINVAL
     rc = lib.anchor_attn_position_ids(fake, 4, 1, 256, 4, fake, fake, 1 << 40, None)
     assert rc == api.AA_EINVAL
+    # work order: null arrays or no tiles are rejected before any launch
+    assert lib.anchor_attn_tile_order(None, 4, fake, None) == api.AA_EINVAL
+    assert lib.anchor_attn_tile_order(fake, 0, fake, None) == api.AA_EINVAL
+    assert lib.anchor_attn_tile_order(fake, 4, None, None) == api.AA_EINVAL
     # the float32-output option is for the attention entry points only
     assert api.FLAG_O_FP32 == 8
     rc = lib.anchor_attn_position_ids(fake, 4, 1, 256, api.FLAG_O_FP32, fake, fake, 1 << 40, None)

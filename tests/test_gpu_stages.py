@@ -173,3 +173,49 @@ def test_device_status_flags_bad_documents(gpu_lib):
     # ... a device copy reaches the kernels, which flag it and NaN-fill the outputs
     o, lse = gpu_lib.anchor_attn_fwd(q, q, q, torch.from_numpy(bad).cuda(), 1e4)
     assert torch.isnan(o.float()).all() and torch.isnan(lse).all()
+
+
+def _expected_order(cnt):
+    """The work-order rule written out: longest processing time first (stable,
+    by descending count) when the largest count exceeds 1.5x the mean, else
+    the natural order; heads interleaved for at most 128 tiles or even work;
+    more than 16384 tiles keep the natural order with no flags."""
+    n = len(cnt)
+    if n > 16384:
+        return np.arange(n), 0
+    lpt = 2 * int(cnt.max()) * n > 3 * int(cnt.sum())
+    order = np.argsort(-cnt, kind="stable") if lpt else np.arange(n)
+    inter = n <= 128 or not lpt
+    return order, (1 if lpt else 0) | (2 if inter else 0)
+
+
+@pytest.mark.parametrize("case", ["skewed", "even", "ties", "one", "small_skewed", "beyond_limit"])
+def test_tile_order(gpu_lib, case):
+    """The work order is unique given the counts: bit-exact against the rule."""
+    rng = np.random.default_rng(sum(map(ord, case)))
+    cnt = {
+        "skewed": lambda: rng.integers(1, 400, 3000) ** 2 // 400 + 1,
+        "even": lambda: rng.integers(5, 7, 2048),
+        "ties": lambda: rng.integers(0, 4, 5000) * 50 + 1,
+        "one": lambda: np.array([7]),
+        "small_skewed": lambda: np.concatenate([np.full(60, 1), np.array([90, 3, 2])]),
+        "beyond_limit": lambda: rng.integers(1, 50, 16385),
+    }[case]().astype(np.int32)
+    got = gpu_lib.anchor_attn_tile_order(torch.from_numpy(cnt).cuda()).cpu().numpy()
+    order, flags = _expected_order(cnt)
+    say(f"[order] {case}: n={len(cnt)} flags={got[-1]}")
+    assert np.array_equal(got[:-1], order) and got[-1] == flags
+
+
+@pytest.mark.parametrize("wname", ["8k", "64k", "short_docs"])
+def test_tile_order_of_workload_plans(gpu_lib, wname):
+    """The order the kernels use for the benchmark workloads: from the live-tile
+    counts of the forward's query-major plan (128 x 64 tiles)."""
+    w = W.get(wname)
+    plan = gpu_lib.anchor_attn_tile_plan(w.cu_doc_lens, w.B, w.S, 128, 64)
+    qptr = plan["qptr"].cpu().numpy().astype(np.int64)
+    cnt = np.diff(qptr).astype(np.int32)
+    got = gpu_lib.anchor_attn_tile_order(torch.from_numpy(cnt).cuda()).cpu().numpy()
+    order, flags = _expected_order(cnt)
+    say(f"[order] {wname}: flags={got[-1]} (LPT {bool(got[-1] & 1)}, interleave {bool(got[-1] & 2)})")
+    assert np.array_equal(got[:-1], order) and got[-1] == flags
