@@ -76,6 +76,29 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   if (!qvalid) { qlo = 1; qhi = 0; }
   const bool bad = status[0] != kStatusOk;
 
+  const size_t tok0 = (size_t)b * S;
+  // K and V tiles are loaded straight into LDS, two buffers; the tile loop is
+  // unrolled by two so that every LDS address of a buffer is base + constant.
+  // The first tile is issued before the Q rows are loaded and rotated, so
+  // that its latency overlaps theirs (workgroups with few key tiles gain).
+  static_assert(NBUF == 2, "the unrolled tile loop assumes two buffers");
+  const size_t kv_row_stride = (size_t)Hkv * D;
+  const bf16* kbase = kr + tok0 * kv_row_stride + hkv * D;
+  const bf16* vbase = v + tok0 * kv_row_stride + hkv * D;
+  DirectTile<D, BN, 256> dl;
+  dl.init(kv_row_stride);
+  auto issue = [&](int buf, int kt) {
+    dl.load(Ks[buf], kbase, kv_row_stride, kt * BN, S - 1);
+    dl.load(Vs[buf], vbase, kv_row_stride, kt * BN, S - 1);
+  };
+
+  // Live key tiles e_first .. e_end-1 (only key tile 0 can be anchor-only).
+  int e_first = qptr[tile];
+  const int e_end = qptr[tile + 1];
+  if (e_first < e_end && packed_kind(kpack[e_first]) == kTileAnchor) ++e_first;
+  const int n_tiles = e_end - e_first;
+  if (n_tiles > 0) issue(0, packed_idx(kpack[e_first]));
+
   // Q^T operand: lane holds query `col`, features 16*kk + 8*h + i.  With
   // ROTATE_Q the RoPE stage happens here: Q stays in registers for the
   // whole key loop, so it is rotated once, and the rotated rows are written
@@ -101,7 +124,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
 
   // Anchor column: s_i0 = q'_i . k'_0 (k'_0 = k_0, its position is 0).  Rows
   // without an anchor start from an empty softmax instead.
-  const size_t tok0 = (size_t)b * S;
   float m, l;
   f32x16 acc[NDB];
   if (!anchor) {
@@ -133,26 +155,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
         for (int r = 0; r < 4; ++r) acc[db][4 * g + r] = (float)w[r];
       }
   }
-
-  // K and V tiles are loaded straight into LDS, two buffers; the tile loop is
-  // unrolled by two so that every LDS address of a buffer is base + constant.
-  static_assert(NBUF == 2, "the unrolled tile loop assumes two buffers");
-  const size_t kv_row_stride = (size_t)Hkv * D;
-  const bf16* kbase = kr + tok0 * kv_row_stride + hkv * D;
-  const bf16* vbase = v + tok0 * kv_row_stride + hkv * D;
-  DirectTile<D, BN, 256> dl;
-  dl.init(kv_row_stride);
-  auto issue = [&](int buf, int kt) {
-    dl.load(Ks[buf], kbase, kv_row_stride, kt * BN, S - 1);
-    dl.load(Vs[buf], vbase, kv_row_stride, kt * BN, S - 1);
-  };
-
-  // Live key tiles e_first .. e_end-1 (only key tile 0 can be anchor-only).
-  int e_first = qptr[tile];
-  const int e_end = qptr[tile + 1];
-  if (e_first < e_end && packed_kind(kpack[e_first]) == kTileAnchor) ++e_first;
-  const int n_tiles = e_end - e_first;
-  if (n_tiles > 0) issue(0, packed_idx(kpack[e_first]));
 
   auto step = [&](auto bufc, int i) {
     constexpr int BUF = decltype(bufc)::value;
