@@ -107,9 +107,7 @@ struct BwdArgs {
   const float* table;  // RoPE cos/sin table [S][D/2][2]
   TokenTables tt;
   const int32_t* status;
-  float* dvec;         // [B,Hq,S]   rowsum(dO * O)
-  float* ds0;          // [B,Hq,S]   dS of the anchor column
-  float* qstats;       // [B,Hq,nblk][4][kPreRows] per 64-query tile: LSE*log2(e), Dv, lo, hi
+  float* qstats;       // [B,Hq,nblk][4][kStatRows] per 64-query tile: LSE*log2(e), Dv, lo, hi
   float* part_dk;      // [B,Hq,nblk,D] per-row-block sums for the anchor key
   float* part_dv;      // [B,Hq,nblk,D]
   int nblk;
@@ -125,9 +123,8 @@ struct BwdArgs {
   const int32_t* tok_map = nullptr;
   int o_f32 = 0;
 };
-constexpr int kPreRows = 64;    // rows per block of the backward preprocess
+constexpr int kStatRows = 64;   // query rows per record block (= the dK/dV query tile)
 
-hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, const PlanBufs& pq,
                            hipStream_t st);
 hipError_t launch_bwd_dq(const BwdArgs& a, const PlanBufs& pq, hipStream_t st);
