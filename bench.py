@@ -2,8 +2,8 @@
 """Benchmark: AnchorAttention forward + backward on one MI355X.
 
 One step = one full pass of the hot path over one packed batch: position IDs,
-tile plans, RoPE, forward attention, backward preprocess, dK/dV, dQ and the
-anchor-key reduction (the library's anchor_attn_fwd + anchor_attn_bwd).
+tile plans, RoPE, forward attention, dQ (with the backward's per-row
+preprocessing), dK/dV and the anchor-key reduction (the library's anchor_attn_fwd + anchor_attn_bwd).
 
 Prints ONE JSON line.  `value` is fwd+bwd TFLOP/s counting only unmasked
 (query, key) pairs (14*D flops per pair and query head); inputs are resident
