@@ -223,7 +223,8 @@ def _sample_rows(w, rng, n):
 
 
 def _sample_keys(w, rng, n, max_doc=2500):
-    """Keys in documents short enough for the oracle to sum over, plus anchors."""
+    """Keys in documents short enough for the oracle to sum over (the anchor
+    key, which every query of the row sees, is checked at 8K on its own)."""
     cu = w.cu_doc_lens
     keys = set()
     for s, e in zip(cu[:-1], cu[1:]):
@@ -277,6 +278,31 @@ def test_full_size_sampled(gpu_lib, wname):
     e_dq = rel_frob(dq_g, dq_r)
     say(f"[full] {wname} dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
     assert max(e_dq, e_dk, e_dv) <= G_TOL
+
+
+def test_anchor_key_gradients_8k(gpu_lib):
+    """dk and dv of the anchor key at the 8K shape: every one of the 8,192
+    queries contributes, through the per-64-row partial sums and their
+    reduction; against the oracle summing over all rows, per head."""
+    w = W.get("8k")
+    B, S, Hq, Hkv, D = w.B, w.S, w.Hq, w.Hkv, w.D
+    say("[anchor-8k] generating inputs")
+    q, k, v, do = W.make_tensors(B, S, Hq, Hkv, D, w.tensor_seed)
+    cu = w.cu_doc_lens
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    say("[anchor-8k] fwd+bwd on GPU")
+    o, lse = gpu_lib.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base)
+    dq, dk, dv = gpu_lib.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base)
+    torch.cuda.synchronize()
+    heads = [0, Hq - 1]
+    say("[anchor-8k] oracle backward for the anchor key over every row")
+    _, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, w.rope_base, heads=heads, q_rows=[0],
+                                          k_cols=[0])
+    for h in heads:
+        e_dk = rel_frob(f64(dk).reshape(B * S, Hkv, D)[[0]][:, [h]], dk_r[:, [h]])
+        e_dv = rel_frob(f64(dv).reshape(B * S, Hkv, D)[[0]][:, [h]], dv_r[:, [h]])
+        say(f"[anchor-8k] head {h}: dk0 {e_dk:.2e} dv0 {e_dv:.2e}")
+        assert max(e_dk, e_dv) <= G_TOL
 
 
 @pytest.mark.parametrize("mode", ["intra_doc_reset", "full_causal", "anchor_continuous"])
