@@ -47,3 +47,37 @@ def algorithmic_bytes(B: int, S: int, Hq: int, Hkv: int, D: int, backward: bool 
     fwd = (xq + 2 * xk) + xq + lse + rope                       # Q K V in, O LSE out
     bwd = (xq + 2 * xk + xq + xq + lse) + (xq + 2 * xk) + rope  # Q K V O dO LSE in, dQ dK dV out
     return {"fwd": fwd, "bwd": bwd if backward else 0, "total": fwd + (bwd if backward else 0)}
+
+
+def kernel_algorithmic_bytes(kernel: str, B: int, S: int, Hq: int, Hkv: int, D: int) -> int:
+    """Minimum HBM traffic of one launch of an attention kernel: each operand
+    it needs read once, each result written once (bf16 tensors, float32 LSE).
+      fwd       reads q (unrotated), k', v; writes q' (for the backward), O, LSE
+      bwd_dkdv  reads q', k', v, dO; writes dK, dV
+      bwd_dq    reads q', k', v, dO, O, LSE; writes dQ
+    The per-row records and anchor partial sums are a few bytes per row and
+    are left out."""
+    xq = 2 * B * S * Hq * D
+    xk = 2 * B * S * Hkv * D
+    lse = 4 * B * Hq * S
+    table = {
+        "fwd": 3 * xq + 2 * xk + lse,
+        "bwd_dkdv": 2 * xq + 4 * xk,
+        "bwd_dq": 4 * xq + 2 * xk + lse,
+    }
+    return table[kernel]
+
+
+def roofline_point(flops: float, nbytes: float, seconds: float, peak_tflops: float,
+                   peak_gbs: float) -> dict:
+    """Where one launch sits on the roofline: bound by the matrix cores when
+    its flops per byte reach the ridge point peak_flops / peak_bandwidth,
+    else by HBM.  `achieved` and `peak` are in TFLOP/s or GB/s accordingly."""
+    intensity = flops / nbytes
+    ridge = peak_tflops * 1e12 / (peak_gbs * 1e9)
+    if intensity >= ridge:
+        achieved, peak, bound, unit = flops / seconds / 1e12, peak_tflops, "mfma", "TFLOP/s"
+    else:
+        achieved, peak, bound, unit = nbytes / seconds / 1e9, peak_gbs, "hbm", "GB/s"
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+            "flop_per_byte": intensity}

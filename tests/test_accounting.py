@@ -1,0 +1,50 @@
+"""Host-side work accounting of the benchmark: per-kernel algorithmic bytes
+and the roofline bound chosen from flops per byte (no GPU)."""
+import pytest
+
+import workloads as W
+from long_context_attention_doc_amd.accounting import (flops_fwd_bwd, kernel_algorithmic_bytes,
+                                                        roofline_point)
+
+PEAK_TF, PEAK_GBS = 2500.0, 8000.0
+FLOPS_PER_PAIR_D = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 6.0}
+
+
+def test_kernel_bytes_mha_and_gqa():
+    B, S, H, D = 2, 1024, 4, 128
+    x = 2 * B * S * H * D            # one [B,S,H,D] bf16 tensor
+    lse = 4 * B * H * S
+    assert kernel_algorithmic_bytes("fwd", B, S, H, H, D) == 5 * x + lse
+    assert kernel_algorithmic_bytes("bwd_dkdv", B, S, H, H, D) == 6 * x
+    assert kernel_algorithmic_bytes("bwd_dq", B, S, H, H, D) == 6 * x + lse
+    # GQA: key-side tensors are Hkv wide
+    xk = 2 * B * S * 1 * D
+    assert kernel_algorithmic_bytes("bwd_dkdv", B, S, H, 1, D) == 2 * x + 4 * xk
+    with pytest.raises(KeyError):
+        kernel_algorithmic_bytes("rope", B, S, H, H, D)
+
+
+def test_roofline_point_sides_of_the_ridge():
+    ridge = PEAK_TF * 1e12 / (PEAK_GBS * 1e9)          # 312.5 flop/B
+    assert ridge == pytest.approx(312.5)
+    hi = roofline_point(1e12, 1e12 / 1000.0, 1e-3, PEAK_TF, PEAK_GBS)
+    assert hi["bound"] == "mfma" and hi["unit"] == "TFLOP/s"
+    assert hi["achieved"] == pytest.approx(1000.0) and hi["frac"] == pytest.approx(0.4)
+    lo = roofline_point(1e9, 1e9, 1e-3, PEAK_TF, PEAK_GBS)
+    assert lo["bound"] == "hbm" and lo["unit"] == "GB/s"
+    assert lo["achieved"] == pytest.approx(1000.0) and lo["frac"] == pytest.approx(0.125)
+    edge = roofline_point(312.5e6, 1e6, 1.0, PEAK_TF, PEAK_GBS)
+    assert edge["bound"] == "mfma"
+
+
+@pytest.mark.parametrize("name,bound", [("8k", "mfma"), ("64k", "mfma"), ("128k_gqa", "mfma"),
+                                        ("64k_ulysses8", "mfma"), ("short_docs", "hbm")])
+def test_bench_workloads_bound(name, bound):
+    """The sparsity-stress workload's attention kernels sit below the ridge
+    point (too few pairs per byte moved); the long-context ones far above."""
+    w = W.get(name)
+    fl = flops_fwd_bwd([list(r) for r in w.doc_rows], w.Hq, w.D)
+    for kern, f in FLOPS_PER_PAIR_D.items():
+        flops = f * w.D * w.Hq * fl["pairs_per_head"]
+        nbytes = kernel_algorithmic_bytes(kern, w.B, w.S, w.Hq, w.Hkv, w.D)
+        assert roofline_point(flops, nbytes, 1.0, PEAK_TF, PEAK_GBS)["bound"] == bound
