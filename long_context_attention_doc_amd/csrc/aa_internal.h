@@ -152,9 +152,8 @@ __device__ __forceinline__ float partner(float x) {
 // {cos, sin} of the four pair angles.  Float32 rotation, bf16 result (RNE).
 // The RoPE pass and the forward's Q loads share this one definition, so a
 // rotated vector is the same bits wherever it is formed.
-__device__ __forceinline__ bf16x8 rope_rotate8(const bf16x8 xv, const float* tb) {
-  const f32x4 cs01 = ((const f32x4*)tb)[0];   // cos0 sin0 cos1 sin1
-  const f32x4 cs23 = ((const f32x4*)tb)[1];
+__device__ __forceinline__ bf16x8 rope_rotate8(const bf16x8 xv, const f32x4 cs01, const f32x4 cs23) {
+  // cs01 = cos0 sin0 cos1 sin1, cs23 = cos2 sin2 cos3 sin3
   bf16x8 out;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -165,6 +164,9 @@ __device__ __forceinline__ bf16x8 rope_rotate8(const bf16x8 xv, const float* tb)
     out[2 * q + 1] = (bf16)__builtin_fmaf(x0, s, x1 * c);
   }
   return out;
+}
+__device__ __forceinline__ bf16x8 rope_rotate8(const bf16x8 xv, const float* tb) {
+  return rope_rotate8(xv, ((const f32x4*)tb)[0], ((const f32x4*)tb)[1]);
 }
 
 // ---------------------------------------------------------------- LDS tiles

@@ -76,11 +76,21 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   if (!qvalid) { qlo = 1; qhi = 0; }
   const bool bad = status[0] != kStatusOk;
 
+  // Q^T operand: lane holds query `col`, features 16*kk + 8*h + i.  With
+  // ROTATE_Q the RoPE stage happens here: Q stays in registers for the
+  // whole key loop, so it is rotated once, and the rotated rows are written
+  // out for the backward.  The raw rows are loaded first, then the first K/V
+  // tile is issued, then the rows' cos/sin values (their address needs the
+  // position ID), so that the loads' latencies overlap (workgroups with few
+  // key tiles gain).
+  bf16x8 qf[NKK];
+  const size_t qoff = (tok * Hq + hq) * D + 8 * h;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const bf16x8*)((ROTATE_Q ? q_raw : qr) + qoff + 16 * kk);
+
   const size_t tok0 = (size_t)b * S;
   // K and V tiles are loaded straight into LDS, two buffers; the tile loop is
   // unrolled by two so that every LDS address of a buffer is base + constant.
-  // The first tile is issued before the Q rows are loaded and rotated, so
-  // that its latency overlaps theirs (workgroups with few key tiles gain).
   static_assert(NBUF == 2, "the unrolled tile loop assumes two buffers");
   const size_t kv_row_stride = (size_t)Hkv * D;
   const bf16* kbase = kr + tok0 * kv_row_stride + hkv * D;
@@ -99,26 +109,14 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   const int n_tiles = e_end - e_first;
   if (n_tiles > 0) issue(0, packed_idx(kpack[e_first]));
 
-  // Q^T operand: lane holds query `col`, features 16*kk + 8*h + i.  With
-  // ROTATE_Q the RoPE stage happens here: Q stays in registers for the
-  // whole key loop, so it is rotated once, and the rotated rows are written
-  // out for the backward.
-  bf16x8 qf[NKK];
-  {
-    const size_t qoff = (tok * Hq + hq) * D + 8 * h;
-    if constexpr (ROTATE_Q) {
-      const int p = min(max(pos[tok], 0), npos - 1);
-      const float* tb = table + (size_t)p * D + 8 * h;     // row p, pair (8h)/2, {cos, sin}
+  if constexpr (ROTATE_Q) {
+    const int p = min(max(pos[tok], 0), npos - 1);
+    const float* tb = table + (size_t)p * D + 8 * h;     // row p, pair (8h)/2, {cos, sin}
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        qf[kk] = rope_rotate8(*(const bf16x8*)(q_raw + qoff + 16 * kk), tb + 16 * kk);
-      if (qvalid) {
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = rope_rotate8(qf[kk], tb + 16 * kk);
+    if (qvalid) {
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) *(bf16x8*)(qr + qoff + 16 * kk) = qf[kk];
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) qf[kk] = *(const bf16x8*)(qr + qoff + 16 * kk);
+      for (int kk = 0; kk < NKK; ++kk) *(bf16x8*)(qr + qoff + 16 * kk) = qf[kk];
     }
   }
 
