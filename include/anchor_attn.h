@@ -271,9 +271,9 @@ aa_status anchor_attn_device_status(const void* workspace, hipStream_t stream, i
  * launches are recorded; later ones run untimed. */
 enum {
   AA_K_STATUS = 0, AA_K_POSITIONS = 1, AA_K_PLAN = 2, AA_K_ROPE_TABLE = 3, AA_K_ROPE = 4,
-  AA_K_FWD = 5, AA_K_BWD_DQ = 6, AA_K_BWD_DKDV = 7, AA_K_BWD_ANCHOR = 8,
-  AA_K_CHUNKS = 9, AA_K_GATHER = 10,
-  AA_K_COUNT = 11
+  AA_K_FWD = 5, AA_K_BWD_PRE = 6, AA_K_BWD_DKDV = 7, AA_K_BWD_DQ = 8, AA_K_BWD_ANCHOR = 9,
+  AA_K_CHUNKS = 10, AA_K_GATHER = 11,
+  AA_K_COUNT = 12
 };
 aa_status anchor_attn_profile_begin(int max_launches);
 aa_status anchor_attn_profile_end(double* ms, int32_t* count, int n);

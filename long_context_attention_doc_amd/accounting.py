@@ -50,20 +50,23 @@ def algorithmic_bytes(B: int, S: int, Hq: int, Hkv: int, D: int, backward: bool 
 
 
 def kernel_algorithmic_bytes(kernel: str, B: int, S: int, Hq: int, Hkv: int, D: int) -> int:
-    """Minimum HBM traffic of one launch of an attention kernel: each operand
-    it needs read once, each result written once (bf16 tensors, float32 LSE).
+    """Minimum HBM traffic of one launch of a kernel of the path: each operand
+    it needs read once, each result written once (bf16 tensors, float32 per-row
+    values [B,Hq,S]).
       fwd       reads q (unrotated), k', v; writes q' (for the backward), O, LSE
+      bwd_pre   reads q', O, dO, LSE; writes Dv and the anchor column's dS
       bwd_dkdv  reads q', k', v, dO; writes dK, dV
-      bwd_dq    reads q', k', v, dO, O, LSE; writes dQ
-    The per-row records and anchor partial sums are a few bytes per row and
-    are left out."""
+      bwd_dq    reads q', k', v, dO, LSE, Dv, the anchor column's dS; writes dQ
+    The per-tile query records and the anchor partial sums (a few bytes per
+    row) are left out."""
     xq = 2 * B * S * Hq * D
     xk = 2 * B * S * Hkv * D
-    lse = 4 * B * Hq * S
+    row = 4 * B * Hq * S          # one float32 value per row and query head
     table = {
-        "fwd": 3 * xq + 2 * xk + lse,
+        "fwd": 3 * xq + 2 * xk + row,
+        "bwd_pre": 3 * xq + 3 * row,
         "bwd_dkdv": 2 * xq + 4 * xk,
-        "bwd_dq": 4 * xq + 2 * xk + lse,
+        "bwd_dq": 3 * xq + 2 * xk + 3 * row,
     }
     return table[kernel]
 

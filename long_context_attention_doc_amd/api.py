@@ -38,8 +38,8 @@ EXPORTS = (
     "anchor_attn_tile_order", "anchor_attn_rope", "anchor_attn_device_status", "anchor_attn_profile_begin",
     "anchor_attn_profile_end",
 )
-KERNEL_IDS = ("status", "positions", "plan", "rope_table", "rope", "fwd", "bwd_dq", "bwd_dkdv",
-              "bwd_anchor", "chunks", "gather")
+KERNEL_IDS = ("status", "positions", "plan", "rope_table", "rope", "fwd", "bwd_pre", "bwd_dkdv",
+              "bwd_dq", "bwd_anchor", "chunks", "gather")
 
 _lib = None
 

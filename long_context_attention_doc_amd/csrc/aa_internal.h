@@ -107,7 +107,9 @@ struct BwdArgs {
   const float* table;  // RoPE cos/sin table [S][D/2][2]
   TokenTables tt;
   const int32_t* status;
-  float* qstats;       // [B,Hq,nblk][4][kStatRows] per 64-query tile: LSE*log2(e), Dv, lo, hi
+  float* dvec;         // [B,Hq,S]   rowsum(dO * O)
+  float* ds0;          // [B,Hq,S]   dS of the anchor column
+  float* qstats;       // [B,Hq,nblk][4][kPreRows] per 64-query tile: LSE*log2(e), Dv, lo, hi
   float* part_dk;      // [B,Hq,nblk,D] per-row-block sums for the anchor key
   float* part_dv;      // [B,Hq,nblk,D]
   int nblk;
@@ -123,8 +125,9 @@ struct BwdArgs {
   const int32_t* tok_map = nullptr;
   int o_f32 = 0;
 };
-constexpr int kStatRows = 64;   // query rows per record block (= the dK/dV query tile)
+constexpr int kPreRows = 64;    // rows per block of the backward preprocess
 
+hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, const PlanBufs& pq,
                            hipStream_t st);
 hipError_t launch_bwd_dq(const BwdArgs& a, const PlanBufs& pq, hipStream_t st);
@@ -152,8 +155,9 @@ __device__ __forceinline__ float partner(float x) {
 // {cos, sin} of the four pair angles.  Float32 rotation, bf16 result (RNE).
 // The RoPE pass and the forward's Q loads share this one definition, so a
 // rotated vector is the same bits wherever it is formed.
-__device__ __forceinline__ bf16x8 rope_rotate8(const bf16x8 xv, const f32x4 cs01, const f32x4 cs23) {
-  // cs01 = cos0 sin0 cos1 sin1, cs23 = cos2 sin2 cos3 sin3
+__device__ __forceinline__ bf16x8 rope_rotate8(const bf16x8 xv, const float* tb) {
+  const f32x4 cs01 = ((const f32x4*)tb)[0];   // cos0 sin0 cos1 sin1
+  const f32x4 cs23 = ((const f32x4*)tb)[1];
   bf16x8 out;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -164,9 +168,6 @@ __device__ __forceinline__ bf16x8 rope_rotate8(const bf16x8 xv, const f32x4 cs01
     out[2 * q + 1] = (bf16)__builtin_fmaf(x0, s, x1 * c);
   }
   return out;
-}
-__device__ __forceinline__ bf16x8 rope_rotate8(const bf16x8 xv, const float* tb) {
-  return rope_rotate8(xv, ((const f32x4*)tb)[0], ((const f32x4*)tb)[1]);
 }
 
 // ---------------------------------------------------------------- LDS tiles

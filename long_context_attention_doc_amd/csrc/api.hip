@@ -72,7 +72,7 @@ struct Layout {
   size_t status, pos, lo, hi, table, qrot, krot;
   PlanLayout pq;        // query-major plan of the forward and dq kernels
   PlanLayout pk;        // key-major plan of the dkdv kernel (backward only)
-  size_t pdk, pdv, qstats;
+  size_t dvec, ds0, pdk, pdv, qstats;
   int nblk;
   size_t total;
 };
@@ -90,16 +90,18 @@ Layout layout(int B, int S, int Hq, int Hkv, int D, bool bwd) {
   L.krot = o;   o = up(o + T * Hkv * D * 2);
   L.pq = plan_layout(B, S, kFwdBM, kFwdBN, o);
   o = L.pq.end;
-  L.nblk = (S + kStatRows - 1) / kStatRows;
+  L.nblk = (S + kPreRows - 1) / kPreRows;
   if (bwd) {
     L.pk = plan_layout(B, S, kDkvBM, kDkvBN, o);
     o = L.pk.end;
+    L.dvec = o; o = up(o + (size_t)B * Hq * S * 4);
+    L.ds0 = o;  o = up(o + (size_t)B * Hq * S * 4);
     L.pdk = o;  o = up(o + (size_t)B * Hq * L.nblk * D * 4);
     L.pdv = o;  o = up(o + (size_t)B * Hq * L.nblk * D * 4);
-    L.qstats = o; o = up(o + (size_t)B * Hq * L.nblk * 4 * kStatRows * 4);
+    L.qstats = o; o = up(o + (size_t)B * Hq * L.nblk * 4 * kPreRows * 4);
   } else {
     L.pk = L.pq;
-    L.pdk = L.pdv = L.qstats = 0;
+    L.dvec = L.ds0 = L.pdk = L.pdv = L.qstats = 0;
   }
   L.total = o;
   return L;
@@ -364,6 +366,8 @@ static aa_status bwd_impl(const void* q, const void* k, const void* v, const voi
   a.table = (const float*)(ws + L.table);
   a.tt = TokenTables{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
   a.status = (const int32_t*)(ws + L.status);
+  a.dvec = (float*)(ws + L.dvec);
+  a.ds0 = (float*)(ws + L.ds0);
   a.part_dk = (float*)(ws + L.pdk);
   a.part_dv = (float*)(ws + L.pdv);
   a.qstats = (float*)(ws + L.qstats);
@@ -374,10 +378,10 @@ static aa_status bwd_impl(const void* q, const void* k, const void* v, const voi
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
   a.scale = scale;
   a.anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
-  // dq first: it also writes the query records and anchor partial sums
-  AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
+  AA_LAUNCH(AA_K_BWD_PRE, stream, launch_bwd_pre(a, stream));
   AA_LAUNCH(AA_K_BWD_DKDV, stream,
             launch_bwd_dkdv(a, plan_bufs(L.pk, ws), plan_bufs(L.pq, ws), stream));
+  AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
   // without an anchor, key 0 is an ordinary key and dk/dv of it are complete
   if (a.anchor) AA_LAUNCH(AA_K_BWD_ANCHOR, stream, launch_bwd_anchor(a, stream));
   return AA_OK;
@@ -505,6 +509,8 @@ aa_status anchor_attn_bwd_chunks(const void* q, const void* k, const void* v, co
   a.table = (const float*)(ws + L.table);
   a.tt = TokenTables{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
   a.status = (const int32_t*)(ws + L.status);
+  a.dvec = (float*)(ws + L.dvec);
+  a.ds0 = (float*)(ws + L.ds0);
   a.part_dk = (float*)(ws + L.pdk);
   a.part_dv = (float*)(ws + L.pdv);
   a.qstats = (float*)(ws + L.qstats);
@@ -516,10 +522,10 @@ aa_status anchor_attn_bwd_chunks(const void* q, const void* k, const void* v, co
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
   a.scale = scale;
   a.anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
-  // dq first: it also writes the query records and anchor partial sums
-  AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
+  AA_LAUNCH(AA_K_BWD_PRE, stream, launch_bwd_pre(a, stream));
   AA_LAUNCH(AA_K_BWD_DKDV, stream,
             launch_bwd_dkdv(a, plan_bufs(L.pk, ws), plan_bufs(L.pq, ws), stream));
+  AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
   if (a.anchor) AA_LAUNCH(AA_K_BWD_ANCHOR, stream, launch_bwd_anchor(a, stream));
   return AA_OK;
 }

@@ -10,17 +10,15 @@
 //   dk_j  = R(pos_j)^T  scale sum_i dS_ij q'_i
 // Key gradients also sum over the query heads of a grouped-query group.
 //
-// Three kernels, all without atomics, launched in this order:
-//   dq     per (row b, query head, query tile of 128): the structure of the
-//          forward kernel, recomputing S and dP from LSE.  Its prologue
-//          also does the per-row preprocessing: Dv_i from the O row, the
-//          anchor column's P_i0 and dS_i0, and the per-tile query records
-//          the dkdv kernel reads; its epilogue adds the anchor column's term
-//          to dq, un-rotates, and writes per 64-row block the partial sums
-//          of dS_i0 q'_i and P_i0 dO_i;
+// Four kernels, all without atomics:
+//   pre    per query row: Dv_i, and the anchor column's P_i0 and dS_i0; per
+//          block of 64 rows, partial sums of dS_i0 q'_i and P_i0 dO_i;
 //   dkdv   per (row b, kv head, key tile of 128): K in LDS and V in
 //          registers for the whole kernel, the live query tiles of the
 //          key-major plan stream through LDS;
+//   dq     per (row b, query head, query tile of 128): the structure of the
+//          forward kernel, recomputing S and dP from LSE; adds the anchor
+//          column's term and un-rotates;
 //   anchor per (row b, kv head): reduces the partial sums into dk_0, dv_0.
 // A float32 atomic accumulation of dq across key tiles would move about
 // 34 GB at 64K tokens x 32 heads and is limited by the L2 atomic rate, so dq
@@ -32,6 +30,111 @@
 namespace aa {
 
 constexpr float kLog2e = 1.44269504088896340736f;
+
+// ---------------------------------------------------------------------------
+// pre: one workgroup per (row b, query head, block of kPreRows rows).
+// D/8 lanes share one row, 8 features each.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_pre(
+    const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
+    const void* __restrict__ o, int o_f32, const bf16* __restrict__ dout,
+    const float* __restrict__ lse,
+    const int32_t* __restrict__ lo, const int32_t* __restrict__ hi, int S, int Hq, int Hkv,
+    int nblk, float scale, int anchor, float* __restrict__ dvec, float* __restrict__ ds0,
+    float* __restrict__ part_dk, float* __restrict__ part_dv, float* __restrict__ qstats,
+    const int32_t* __restrict__ tok_map) {
+  constexpr int LPR = D / 8;                // lanes per row
+  constexpr int RPP = 256 / LPR;            // rows per pass of the workgroup
+  __shared__ float red_k[RPP][D + 4];
+  __shared__ float red_v[RPP][D + 4];
+  // heads fastest: neighbouring workgroups read neighbouring D-wide pieces
+  // of the same token rows
+  const int hq = blockIdx.x % Hq;
+  const int rb = blockIdx.x / Hq;
+  const int blk = rb % nblk, b = rb / nblk;
+  const int hkv = hq / (Hq / Hkv);
+  const int tid = threadIdx.x;
+  const int slot = tid / LPR, f0 = (tid % LPR) * 8;
+  const size_t tok0 = (size_t)b * S;
+  float k0[8], v0[8];
+  {
+    const bf16x8 kk = *(const bf16x8*)(kr + (tok0 * Hkv + hkv) * D + f0);
+    const bf16x8 vv = *(const bf16x8*)(v + (tok0 * Hkv + hkv) * D + f0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { k0[i] = (float)kk[i]; v0[i] = (float)vv[i]; }
+  }
+  float pk[8] = {0, 0, 0, 0, 0, 0, 0, 0}, pv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r0 = 0; r0 < kPreRows; r0 += RPP) {
+    const int row = blk * kPreRows + r0 + slot;
+    const bool valid = row < S;
+    const size_t tok = tok0 + (valid ? row : S - 1);
+    const size_t otok = tok_map ? (size_t)tok_map[tok] : tok;   // the caller's O and LSE row
+    const size_t off = (tok * Hq + hq) * D + f0;
+    const bf16x8 qv = *(const bf16x8*)(qr + off);
+    float of[8];
+    if (o_f32) {
+      const f32x4* op = (const f32x4*)((const float*)o + (otok * Hq + hq) * D + f0);
+      const f32x4 o0 = op[0], o1 = op[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { of[i] = o0[i]; of[4 + i] = o1[i]; }
+    } else {
+      const bf16x8 ov = *(const bf16x8*)((const bf16*)o + (otok * Hq + hq) * D + f0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) of[i] = (float)ov[i];
+    }
+    const bf16x8 dv = *(const bf16x8*)(dout + off);
+    float d_o = 0.f, s0 = 0.f, dp0 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float g = (float)dv[i];
+      d_o += g * of[i];
+      s0 += (float)qv[i] * k0[i];
+      dp0 += g * v0[i];
+    }
+#pragma unroll
+    for (int off2 = LPR / 2; off2 > 0; off2 >>= 1) {
+      d_o += __shfl_xor(d_o, off2);
+      s0 += __shfl_xor(s0, off2);
+      dp0 += __shfl_xor(dp0, off2);
+    }
+    const float L = lse[((size_t)b * Hq + hq) * S + (otok - tok0)];
+    // without an anchor there is no anchor column: its weight and dS are zero
+    float p0 = valid && anchor ? __builtin_amdgcn_exp2f((s0 * scale - L) * kLog2e) : 0.f;
+    const float dsv = p0 * (dp0 - d_o);
+    if (valid && (tid % LPR) == 0) {
+      dvec[((size_t)b * Hq + hq) * S + row] = d_o;
+      ds0[((size_t)b * Hq + hq) * S + row] = dsv;
+    }
+    if ((tid % LPR) == 0) {
+      // tile-aligned record for the dK/dV kernel; rows past S see nothing
+      float* rec = qstats + (((size_t)b * Hq + hq) * nblk + blk) * 4 * kPreRows;
+      const int rr = r0 + slot;
+      rec[rr] = valid ? L * kLog2e : 0.f;
+      rec[kPreRows + rr] = valid ? d_o : 0.f;
+      rec[2 * kPreRows + rr] = __int_as_float(valid ? lo[tok] : 1);
+      rec[3 * kPreRows + rr] = __int_as_float(valid ? hi[tok] : 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pk[i] += dsv * (float)qv[i];
+      pv[i] += p0 * (float)dv[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    red_k[slot][f0 + i] = pk[i];
+    red_v[slot][f0 + i] = pv[i];
+  }
+  __syncthreads();
+  for (int d = tid; d < D; d += 256) {
+    float sk = 0.f, sv = 0.f;
+    for (int r = 0; r < RPP; ++r) { sk += red_k[r][d]; sv += red_v[r][d]; }
+    const size_t pidx = (((size_t)b * Hq + hq) * nblk + blk) * D + d;
+    part_dk[pidx] = sk;
+    part_dv[pidx] = sv;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // dkdv: one workgroup of four waves per (row b, kv head, key tile of 128 keys),
@@ -56,7 +159,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     bf16* __restrict__ dk,
     bf16* __restrict__ dv) {
   constexpr int BM = kDkvBM, BN = kDkvBN;    // plan tiles: 64 queries x 128 keys
-  static_assert(BM == kStatRows, "one query record per plan tile");
   constexpr int BH = BM / 2;                 // queries per step
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
@@ -98,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     for (int j = 0; j < 16; ++j) { dka[db][j] = 0.f; dva[db][j] = 0.f; }
 
   // Q and dO half tiles go straight into LDS; wave 0 also fetches the tile's
-  // per-query record (LSE, Dv, visible-key interval) that the dq kernel wrote.
+  // per-query record (LSE, Dv, visible-key interval).
   const size_t q_row_stride = (size_t)Hq * D;
   auto issue = [&](int buf, int hq, int qt, int half) {
     const int row0 = qt * BM + half * BH;
@@ -229,25 +331,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
 // each wave owns 32 queries, as in the forward kernel.  K and V tiles go
 // straight into a ring of swizzled LDS buffers: row reads feed S^T = K Q^T
 // and dP^T = V dO^T, transposing reads feed K^T in dQ^T = K^T dS^T.
-//   * Prologue, per query row (the lane pair l, l+32 holds one row): Dv_i =
-//     dO_i . O_i, the anchor column's P_i0 = exp(s_i0 - LSE_i) and dS_i0 =
-//     P_i0 (dO_i . v_0 - Dv_i), and the row's entry in the query record of
-//     its 64-row block (LSE*log2(e), Dv, lo, hi) for the dkdv kernel.
-//   * Epilogue: after the key loop the K/V buffers hold, one 64-row block at
-//     a time, dS_i0 q'_i and P_i0 dO_i in float32; the workgroup sums each
-//     feature over the block's rows into the partial sums of the anchor key.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
-    const bf16* __restrict__ dout, const void* __restrict__ o, int o_f32,
-    const float* __restrict__ lse, const float* __restrict__ table,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dvec,
+    const float* __restrict__ ds0, const float* __restrict__ table,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ lo,
     const int32_t* __restrict__ hi, const int32_t* __restrict__ qptr,
     const int32_t* __restrict__ kpack, const int32_t* __restrict__ order,
-    const int32_t* __restrict__ status, int S, int Hq, int Hkv, int nq, int n_items, int nblk,
-    float scale, int anchor, const int32_t* __restrict__ tok_map, float* __restrict__ qstats,
-    float* __restrict__ part_dk, float* __restrict__ part_dv, bf16* __restrict__ dq) {
+    const int32_t* __restrict__ status, int S, int Hq, int Hkv, int nq, int n_items, float scale,
+    int anchor, const int32_t* __restrict__ tok_map, bf16* __restrict__ dq) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
@@ -256,7 +350,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   constexpr int NBUF = kFwdStages;
   __shared__ __align__(16) bf16 Ks[NBUF][BN * D];
   __shared__ __align__(16) bf16 Vs[NBUF][BN * D];
-  __shared__ __align__(16) float wts[2][BM];     // epilogue: dS_i0 and P_i0 per row
 
   const int tiles_per_head = n_items / Hq;
   int hq, rank;
@@ -274,9 +367,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   if (!qvalid) { qlo = 1; qhi = 0; }
   const bool bad = status[0] != kStatusOk;
   const float scale_log2 = scale * kLog2e;
-  const size_t otok = tok_map ? (size_t)tok_map[tok] : tok;   // the caller's O, LSE and dq row
-  const float lse_i = lse[((size_t)b * Hq + hq) * S + (otok - tok0)];
-  const float nlse2 = -lse_i * kLog2e;
+  const size_t rowstat = ((size_t)b * Hq + hq) * S + (qvalid ? qrow : S - 1);
+  const size_t otok = tok_map ? (size_t)tok_map[tok] : tok;   // the caller's LSE and dq row
+  const float nlse2 = -lse[((size_t)b * Hq + hq) * S + (otok - tok0)] * kLog2e;
+  const float dvi = dvec[rowstat];
 
   bf16x8 qf[NKK], gf[NKK];
   {
@@ -287,7 +381,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
       gf[kk] = *(const bf16x8*)(dout + off + 16 * kk);
     }
   }
-  // The first K/V tile is issued before the prologue waits for anything.
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
+
   static_assert(NBUF == 2, "the unrolled tile loop assumes two buffers");
   const size_t kv_row_stride = (size_t)Hkv * D;
   const bf16* kbase = kr + tok0 * kv_row_stride + hkv * D;
@@ -304,51 +403,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   if (e_first < e_end && packed_kind(kpack[e_first]) == kTileAnchor) ++e_first;
   const int n_tiles = e_end - e_first;
   if (n_tiles > 0) issue(0, packed_idx(kpack[e_first]));
-
-  // Dv_i = dO_i . O_i (each lane of the pair takes half of the features).
-  float dvi = 0.f;
-  {
-    const size_t ooff = (otok * Hq + hq) * D + 8 * h;
-    if (o_f32) {
-      const float* op = (const float*)o + ooff;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const f32x4 x0 = *(const f32x4*)(op + 16 * kk), x1 = *(const f32x4*)(op + 16 * kk + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dvi += (float)gf[kk][i] * x0[i];
-          dvi += (float)gf[kk][4 + i] * x1[i];
-        }
-      }
-    } else {
-      const bf16* op = (const bf16*)o + ooff;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 x = *(const bf16x8*)(op + 16 * kk);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dvi += (float)gf[kk][i] * (float)x[i];
-      }
-    }
-  }
-  dvi += partner(dvi);
-  // This row's entry of its block's query record; rows past S see nothing.
-  {
-    const int blk = qrow / kStatRows;
-    if (h == 0 && blk < nblk) {
-      float* rec = qstats + (((size_t)b * Hq + hq) * nblk + blk) * 4 * kStatRows;
-      const int rr = qrow % kStatRows;
-      rec[rr] = qvalid ? lse_i * kLog2e : 0.f;
-      rec[kStatRows + rr] = qvalid ? dvi : 0.f;
-      rec[2 * kStatRows + rr] = __int_as_float(qlo);
-      rec[3 * kStatRows + rr] = __int_as_float(qhi);
-    }
-  }
-  f32x16 acc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
-
   // tile loop unrolled by two: every LDS address of a buffer is base + constant
   auto step = [&](auto bufc, int i) {
     constexpr int BUF = decltype(bufc)::value;
@@ -405,88 +459,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     if (i + 1 < n_tiles) step(std::integral_constant<int, 1>{}, i + 1);
   }
 
-  // Anchor column: s_i0 = q'_i . k'_0, dP_i0 = dO_i . v_0 (needed only from
-  // here on).  Without an anchor there is no anchor column and both weights
-  // are zero.
-  float p0 = 0.f, a0 = 0.f;
-  if (anchor) {
-    const bf16* k0 = kr + (tok0 * Hkv + hkv) * D + 8 * h;
-    const bf16* v0 = v + (tok0 * Hkv + hkv) * D + 8 * h;
-    float s0 = 0.f, dp0 = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const bf16x8 kz = *(const bf16x8*)(k0 + 16 * kk);
-      const bf16x8 vz = *(const bf16x8*)(v0 + 16 * kk);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        s0 += (float)qf[kk][i] * (float)kz[i];
-        dp0 += (float)gf[kk][i] * (float)vz[i];
-      }
-    }
-    s0 += partner(s0);
-    dp0 += partner(dp0);
-    p0 = qvalid ? __builtin_amdgcn_exp2f((s0 * scale - lse_i) * kLog2e) : 0.f;
-    a0 = p0 * (dp0 - dvi);
-  }
-
-  // Anchor-key partial sums of this tile's two 64-row blocks, through LDS:
-  // the K ring takes the tile's q' rows and the V ring its dO rows (bf16,
-  // 16-byte units XOR-swizzled by row), wts the rows' dS_i0 and P_i0; then
-  // each wave sums one (block, quantity) pair, one row per step, each lane
-  // two neighbouring features.
-  if (anchor) {
-    static_assert(NBUF * BN == BM, "the K and V rings hold the tile's rows");
-    static_assert(BM == 2 * kStatRows, "two record blocks per query tile");
-    constexpr int NU = D / 8;                // 16-byte units per row
-    bf16* xq = &Ks[0][0];
-    bf16* xg = &Vs[0][0];
-    __syncthreads();                         // the key loop is done with the rings
-    {
-      const int r = wave * 32 + col;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const int su = (2 * kk + h) ^ (r % NU);
-        *(bf16x8*)(xq + r * D + 8 * su) = qf[kk];
-        *(bf16x8*)(xg + r * D + 8 * su) = gf[kk];
-      }
-      if (h == 0) {
-        wts[0][r] = a0;
-        wts[1][r] = p0;
-      }
-    }
-    __syncthreads();
-    if (tid < 2 * D) {
-      const int p = tid / D, c = (tid % D) / (D / 2), f = tid % (D / 2);
-      const int blk = 2 * qt + p;
-      const bf16* x = c == 0 ? xq : xg;
-      const float* w = &wts[c][p * kStatRows];
-      const int u = (2 * f) / 8, e = (2 * f) % 8;   // unit and element of features 2f, 2f+1
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int r0 = 0; r0 < kStatRows; r0 += 16) {
-        bf16x2 xv[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = p * kStatRows + r0 + i;
-          xv[i] = *(const bf16x2*)(x + r * D + 8 * (u ^ (r % NU)) + e);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float wr = w[r0 + i];
-          s0 = __builtin_fmaf(wr, (float)xv[i][0], s0);
-          s1 = __builtin_fmaf(wr, (float)xv[i][1], s1);
-        }
-      }
-      if (blk < nblk) {
-        float* dst = (c == 0 ? part_dk : part_dv) + (((size_t)b * Hq + hq) * nblk + blk) * D + 2 * f;
-        dst[0] = s0;
-        dst[1] = s1;
-      }
-    }
-  }
-
   // Epilogue: dq' = scale (acc + dS_i0 k'_0); dq = R(pos_i)^T dq'.
   if (qvalid) {
+    const float a0 = ds0[rowstat];
     const bf16* k0 = kr + (tok0 * Hkv + hkv) * D;
     const int pq = pos[tok];
     const float* tb = table + (size_t)pq * D;
@@ -552,6 +527,21 @@ __global__ __launch_bounds__(1024) void k_bwd_anchor(
 }
 
 // ---------------------------------------------------------------- launchers
+hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st) {
+  const long long blocks = (long long)a.Hq * a.B * a.nblk;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks);
+  if (a.D == 128)
+    hipLaunchKernelGGL(k_bwd_pre<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.o_f32, a.dout,
+                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.dvec, a.ds0,
+                       a.part_dk, a.part_dv, a.qstats, a.tok_map);
+  else
+    hipLaunchKernelGGL(k_bwd_pre<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.o_f32, a.dout,
+                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.dvec, a.ds0,
+                       a.part_dk, a.part_dv, a.qstats, a.tok_map);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, const PlanBufs& pq,
                            hipStream_t st) {
   const int n_items = a.B * pk.nk * a.Hkv;
@@ -571,18 +561,16 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, const PlanBufs&
 hipError_t launch_bwd_dq(const BwdArgs& a, const PlanBufs& pq, hipStream_t st) {
   const int n_items = a.B * pq.nq * a.Hq;
   const dim3 grid(padded_grid(n_items));
-  // every record block belongs to one query tile: nblk <= 2 * nq
-  if (a.nblk > 2 * pq.nq) return hipErrorInvalidValue;
   if (a.D == 128)
-    hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.o,
-                       a.o_f32, a.lse, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
-                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.nblk, a.scale,
-                       a.anchor, a.tok_map, a.qstats, a.part_dk, a.part_dv, a.dq);
+    hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
+                       a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
+                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.tok_map,
+                       a.dq);
   else
-    hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.o,
-                       a.o_f32, a.lse, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
-                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.nblk, a.scale,
-                       a.anchor, a.tok_map, a.qstats, a.part_dk, a.part_dv, a.dq);
+    hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
+                       a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
+                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.tok_map,
+                       a.dq);
   return hipGetLastError();
 }
 

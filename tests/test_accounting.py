@@ -15,8 +15,9 @@ def test_kernel_bytes_mha_and_gqa():
     x = 2 * B * S * H * D            # one [B,S,H,D] bf16 tensor
     lse = 4 * B * H * S
     assert kernel_algorithmic_bytes("fwd", B, S, H, H, D) == 5 * x + lse
+    assert kernel_algorithmic_bytes("bwd_pre", B, S, H, H, D) == 3 * x + 3 * lse
     assert kernel_algorithmic_bytes("bwd_dkdv", B, S, H, H, D) == 6 * x
-    assert kernel_algorithmic_bytes("bwd_dq", B, S, H, H, D) == 6 * x + lse
+    assert kernel_algorithmic_bytes("bwd_dq", B, S, H, H, D) == 5 * x + 3 * lse
     # GQA: key-side tensors are Hkv wide
     xk = 2 * B * S * 1 * D
     assert kernel_algorithmic_bytes("bwd_dkdv", B, S, H, 1, D) == 2 * x + 4 * xk
