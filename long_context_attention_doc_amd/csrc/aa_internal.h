@@ -282,21 +282,26 @@ struct DirectTile {
   __device__ __forceinline__ void load(bf16* lds_tile, const bf16* gbase, size_t row_stride,
                                        int row0, int row_max) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const char* tbase = (const char*)(gbase + (size_t)row0 * row_stride);
     if (row0 + ROWS - 1 <= row_max) {
+      const char* tbase = (const char*)(gbase + (size_t)row0 * row_stride);
 #pragma unroll
       for (int u = 0; u < ITERS; ++u)
         __builtin_amdgcn_global_load_lds((const void*)(tbase + off[u]),
                                          (lds_void*)(lds_tile + (wave * ITERS + u) * 64 * 8), 16, 0,
                                          0);
     } else {
+      // Rows past row_max read row_max.  The offsets are unsigned, so they are
+      // taken from min(row0, row_max): a tile may start past the last row
+      // (the second half of a last query tile), and every offset stays >= 0.
+      const int rb = min(row0, row_max);
+      const char* cbase = (const char*)(gbase + (size_t)rb * row_stride);
 #pragma unroll
       for (int u = 0; u < ITERS; ++u) {
         int row, chunk;
         locate(u, row, chunk);
-        const int r = min(row0 + row, row_max) - row0;
+        const int r = min(row0 + row, row_max) - rb;
         __builtin_amdgcn_global_load_lds(
-            (const void*)(tbase + (uint32_t)((r * row_stride + chunk * 8) * sizeof(bf16))),
+            (const void*)(cbase + (uint32_t)((r * row_stride + chunk * 8) * sizeof(bf16))),
             (lds_void*)(lds_tile + (wave * ITERS + u) * 64 * 8), 16, 0, 0);
       }
     }

@@ -164,9 +164,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   constexpr int NDB = D / 32;
   static_assert(BN == 4 * 32 && BH == 32, "four waves of 32 keys, 32-query steps");
   using T = SwzTile<D>;
+  // Two buffers of Q, dO and the query records, one LDS object each: the
+  // compiler can then tell that reads of one buffer do not alias the direct
+  // loads in flight into the other, and does not wait for those loads.
   __shared__ __align__(16) bf16 Qs[2][BH * D];
   __shared__ __align__(16) bf16 Gs[2][BH * D];
-  __shared__ __align__(16) float s_st[2][4][BM];     // LSE*log2(e), Dv, lo, hi (int bits)
+  __shared__ __align__(16) float s_st[2][4][BM];
   __shared__ __align__(16) bf16 Ks[BN * D];          // this workgroup's keys (rotated)
 
   int hkv, ktile;   // ktile = b * nk + kt, in natural order: within a document the
@@ -201,17 +204,22 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
 
   // Q and dO half tiles go straight into LDS; wave 0 also fetches the tile's
   // per-query record (LSE, Dv, visible-key interval).
+  // Q and dO share a row stride, so one set of precomputed lane offsets
+  // serves both.
   const size_t q_row_stride = (size_t)Hq * D;
+  DirectTile<D, BH, 256> dl;
+  dl.init(q_row_stride);
   auto issue = [&](int buf, int hq, int qt, int half) {
     const int row0 = qt * BM + half * BH;
-    tile_load_direct<D, BH, 256>(Qs[buf], qr + tok0 * q_row_stride + (size_t)hq * D, q_row_stride,
-                                 row0, S - 1);
-    tile_load_direct<D, BH, 256>(Gs[buf], dout + tok0 * q_row_stride + (size_t)hq * D,
-                                 q_row_stride, row0, S - 1);
+    dl.load(Qs[buf], qr + tok0 * q_row_stride + (size_t)hq * D, q_row_stride, row0, S - 1);
+    dl.load(Gs[buf], dout + tok0 * q_row_stride + (size_t)hq * D, q_row_stride, row0,
+            S - 1);
     if (wave == 0) {
-      const float* rec = qstats + (((size_t)b * Hq + hq) * nblk + qt) * 4 * BM;
-      __builtin_amdgcn_global_load_lds((const void*)(rec + 4 * lane), (lds_void*)(&s_st[buf][0][0]),
-                                       16, 0, 0);
+      // the record index is wave-uniform: keep its arithmetic scalar
+      const int ri = __builtin_amdgcn_readfirstlane((b * Hq + hq) * nblk + qt);
+      const float* rec = qstats + (size_t)ri * (4 * BM);
+      __builtin_amdgcn_global_load_lds((const void*)(rec + 4 * lane),
+                                       (lds_void*)(&s_st[buf][0][0]), 16, 0, 0);
     }
   };
 
@@ -236,18 +244,19 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   int e, hq, half = 0;
   first(e, hq);
   if (hq < h_end) issue(0, hq, packed_idx(qpack[e]), 0);
-  int cur = 0;
-  while (hq < h_end) {
+  // one step per half tile, unrolled by buffer
+  int BUF = 0;
+  auto step = [&](int) {
     const bool need_mask = packed_kind(qpack[e]) != kTileFull || (anchor && kt == 0);
     int e1 = e, h1 = hq, half1 = half ^ 1;
     if (half1 == 0) advance(e1, h1);
     const int qt1 = h1 < h_end ? packed_idx(qpack[e1]) : 0;
     wait_direct_loads();
-    __syncthreads();      // half tile in buffer `cur` visible; the other buffer free
-    if (h1 < h_end) issue(cur ^ 1, h1, qt1, half1);
-    const bf16* Qc = Qs[cur];
-    const bf16* Gc = Gs[cur];
-    const float* stc = &s_st[cur][0][0] + half * BH;
+    __syncthreads();      // half tile in buffer BUF visible; the other buffer free
+    if (h1 < h_end) issue(BUF ^ 1, h1, qt1, half1);
+    const bf16* Qc = Qs[BUF];
+    const bf16* Gc = Gs[BUF];
+    const float* stc = &s_st[BUF][0][0] + half * BH;
 
     // S = Q K^T, dP = dO V^T for the 32 queries: columns = this wave's keys.
     f32x16 sp, dp;
@@ -294,7 +303,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
         dka[dblk] = mfma32(tr_operand<D>(Qc, 16 * c, 32 * dblk), db_[c], dka[dblk]);
       }
     e = e1; hq = h1; half = half1;
-    cur ^= 1;
+  };
+  while (hq < h_end) {
+    step(0);
+    BUF ^= 1;
   }
 
   // Epilogue: dK = R(pos)^T (scale * dK'), dV as accumulated.
@@ -348,8 +360,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   constexpr int NKB = BN / 32;
   using T = SwzTile<D>;
   constexpr int NBUF = kFwdStages;
-  __shared__ __align__(16) bf16 Ks[NBUF][BN * D];
-  __shared__ __align__(16) bf16 Vs[NBUF][BN * D];
+  // One LDS object per buffer: the compiler can then tell that reads of
+  // one buffer do not alias the direct loads in flight into the other, and
+  // does not wait for those loads before the reads.
+  __shared__ __align__(16) bf16 Ks0[BN * D];
+  __shared__ __align__(16) bf16 Ks1[BN * D];
+  __shared__ __align__(16) bf16 Vs0[BN * D];
+  __shared__ __align__(16) bf16 Vs1[BN * D];
 
   const int tiles_per_head = n_items / Hq;
   int hq, rank;
@@ -394,8 +411,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   DirectTile<D, BN, 256> dl;
   dl.init(kv_row_stride);
   auto issue = [&](int buf, int kt) {
-    dl.load(Ks[buf], kbase, kv_row_stride, kt * BN, S - 1);
-    dl.load(Vs[buf], vbase, kv_row_stride, kt * BN, S - 1);
+    dl.load(buf ? Ks1 : Ks0, kbase, kv_row_stride, kt * BN, S - 1);
+    dl.load(buf ? Vs1 : Vs0, vbase, kv_row_stride, kt * BN, S - 1);
   };
 
   int e_first = qptr[tile];
@@ -414,8 +431,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     wait_direct_loads();
     __syncthreads();                 // tile i visible; the other buffer is free
     if (more) issue(BUF ^ 1, packed_idx(ent_next));
-    const bf16* Kc = Ks[BUF];
-    const bf16* Vc = Vs[BUF];
+    const bf16* Kc = BUF ? Ks1 : Ks0;
+    const bf16* Vc = BUF ? Vs1 : Vs0;
 
     // One 32-key block at a time: S^T = K Q^T, dP^T = V dO^T (rows = keys,
     // columns = this wave's queries), dS^T, then dQ^T += K^T dS^T.

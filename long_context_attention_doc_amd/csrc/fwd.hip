@@ -58,8 +58,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   constexpr int NKB = BN / 32;   // 32-key blocks of a key tile
   using T = SwzTile<D>;
   constexpr int NBUF = kFwdStages;
-  __shared__ __align__(16) bf16 Ks[NBUF][BN * D];
-  __shared__ __align__(16) bf16 Vs[NBUF][BN * D];
+  // One LDS object per buffer: the compiler can then tell that reads of
+  // one buffer do not alias the direct loads in flight into the other, and
+  // does not wait for those loads before the reads.
+  __shared__ __align__(16) bf16 Ks0[BN * D];
+  __shared__ __align__(16) bf16 Ks1[BN * D];
+  __shared__ __align__(16) bf16 Vs0[BN * D];
+  __shared__ __align__(16) bf16 Vs1[BN * D];
 
   const int tiles_per_head = n_items / Hq;
   int hq, rank;
@@ -98,8 +103,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   DirectTile<D, BN, 256> dl;
   dl.init(kv_row_stride);
   auto issue = [&](int buf, int kt) {
-    dl.load(Ks[buf], kbase, kv_row_stride, kt * BN, S - 1);
-    dl.load(Vs[buf], vbase, kv_row_stride, kt * BN, S - 1);
+    dl.load(buf ? Ks1 : Ks0, kbase, kv_row_stride, kt * BN, S - 1);
+    dl.load(buf ? Vs1 : Vs0, vbase, kv_row_stride, kt * BN, S - 1);
   };
 
   // Live key tiles e_first .. e_end-1 (only key tile 0 can be anchor-only).
@@ -164,8 +169,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     wait_direct_loads();
     __syncthreads();                 // tile i visible; the other buffer is free
     if (more) issue(BUF ^ 1, packed_idx(ent_next));
-    const bf16* Kc = Ks[BUF];
-    const bf16* Vc = Vs[BUF];
+    const bf16* Kc = BUF ? Ks1 : Ks0;
+    const bf16* Vc = BUF ? Vs1 : Vs0;
 
     // A 32-key block that none of the wave's queries may see (a document
     // edge or the causal diagonal inside a partial tile) gets -inf scores
