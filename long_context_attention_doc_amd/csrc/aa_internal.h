@@ -228,6 +228,12 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int r0, int f0) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// 32-bit LDS address of a __shared__ location, and back.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+__device__ __forceinline__ lds_void* lds_ptr(uint32_t a) { return (lds_void*)(uintptr_t)a; }
+
 // Direct global -> LDS copy (global_load_lds_dwordx4) of a [ROWS][D] tile
 // into the swizzled layout: lane L of a wave's instruction writes the 16
 // bytes at LDS chunk base + L, so each lane fetches the logical chunk that
@@ -275,6 +281,30 @@ struct DirectTile {
       int row, chunk;
       locate(u, row, chunk);
       off[u] = (uint32_t)((row * row_stride + chunk * 8) * sizeof(bf16));
+    }
+  }
+  // load() with the LDS tile given by its 32-bit address.
+  __device__ __forceinline__ void load_at(uint32_t lds_tile, const bf16* gbase, size_t row_stride,
+                                          int row0, int row_max) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row0 + ROWS - 1 <= row_max) {
+      const char* tbase = (const char*)(gbase + (size_t)row0 * row_stride);
+#pragma unroll
+      for (int u = 0; u < ITERS; ++u)
+        __builtin_amdgcn_global_load_lds((const void*)(tbase + off[u]),
+                                         lds_ptr(lds_tile + (wave * ITERS + u) * 64 * 16), 16, 0, 0);
+    } else {
+      const int rb = min(row0, row_max);
+      const char* cbase = (const char*)(gbase + (size_t)rb * row_stride);
+#pragma unroll
+      for (int u = 0; u < ITERS; ++u) {
+        int row, chunk;
+        locate(u, row, chunk);
+        const int r = min(row0 + row, row_max) - rb;
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(cbase + (uint32_t)((r * row_stride + chunk * 8) * sizeof(bf16))),
+            lds_ptr(lds_tile + (wave * ITERS + u) * 64 * 16), 16, 0, 0);
+      }
     }
   }
   // The tile base is uniform and the offsets are 32-bit, so every load takes

@@ -211,15 +211,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   dl.init(q_row_stride);
   auto issue = [&](int buf, int hq, int qt, int half) {
     const int row0 = qt * BM + half * BH;
-    dl.load(Qs[buf], qr + tok0 * q_row_stride + (size_t)hq * D, q_row_stride, row0, S - 1);
-    dl.load(Gs[buf], dout + tok0 * q_row_stride + (size_t)hq * D, q_row_stride, row0,
-            S - 1);
+    dl.load_at(lds_addr(Qs[0]) + buf * (BH * D * 2), qr + tok0 * q_row_stride + (size_t)hq * D,
+               q_row_stride, row0, S - 1);
+    dl.load_at(lds_addr(Gs[0]) + buf * (BH * D * 2), dout + tok0 * q_row_stride + (size_t)hq * D,
+               q_row_stride, row0, S - 1);
     if (wave == 0) {
       // the record index is wave-uniform: keep its arithmetic scalar
       const int ri = __builtin_amdgcn_readfirstlane((b * Hq + hq) * nblk + qt);
       const float* rec = qstats + (size_t)ri * (4 * BM);
       __builtin_amdgcn_global_load_lds((const void*)(rec + 4 * lane),
-                                       (lds_void*)(&s_st[buf][0][0]), 16, 0, 0);
+                                       lds_ptr(lds_addr(&s_st[0][0][0]) + buf * (4 * BM * 4)), 16, 0,
+                                       0);
     }
   };
 
@@ -280,12 +282,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[4 * g + r], scale_log2, -l4[r]));
       if (need_mask) {
-        const int4 lo4 = *(const int4*)(stc + 2 * BM + q0);
-        const int4 hi4 = *(const int4*)(stc + 3 * BM + q0);
-        pv[0] = (key >= lo4.x && key <= hi4.x) ? pv[0] : 0.f;
-        pv[1] = (key >= lo4.y && key <= hi4.y) ? pv[1] : 0.f;
-        pv[2] = (key >= lo4.z && key <= hi4.z) ? pv[2] : 0.f;
-        pv[3] = (key >= lo4.w && key <= hi4.w) ? pv[3] : 0.f;
+        const int4 lo4 = __builtin_bit_cast(int4, *(const f32x4*)(stc + 2 * BM + q0));
+        const int4 hi4 = __builtin_bit_cast(int4, *(const f32x4*)(stc + 3 * BM + q0));
+        pv[0] = ((key >= lo4.x) & (key <= hi4.x)) ? pv[0] : 0.f;
+        pv[1] = ((key >= lo4.y) & (key <= hi4.y)) ? pv[1] : 0.f;
+        pv[2] = ((key >= lo4.z) & (key <= hi4.z)) ? pv[2] : 0.f;
+        pv[3] = ((key >= lo4.w) & (key <= hi4.w)) ? pv[3] : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
