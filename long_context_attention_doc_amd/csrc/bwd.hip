@@ -170,7 +170,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   __shared__ __align__(16) bf16 Qs[2][BH * D];
   __shared__ __align__(16) bf16 Gs[2][BH * D];
   __shared__ __align__(16) float s_st[2][4][BM];
-  __shared__ __align__(16) bf16 Ks[BN * D];          // this workgroup's keys (rotated)
+  // This workgroup's keys (rotated), only ever read row-wise: rows padded by
+  // 16 bytes instead of swizzled, so that 16 consecutive rows at one 16-byte
+  // column still hit 16 distinct 4-bank groups and a lane's eight reads are
+  // one base address plus immediate offsets.
+  constexpr int KLD = D + 8;
+  __shared__ __align__(16) bf16 Ks[BN * KLD];
 
   int hkv, ktile;   // ktile = b * nk + kt, in natural order: within a document the
                     // key tiles already go from the most query tiles to the fewest
@@ -193,8 +198,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) vf[kk] = *(const bf16x8*)(vp + 16 * kk);
     const size_t kv_row_stride = (size_t)Hkv * D;
-    tile_load_direct<D, BN, 256>(Ks, kr + tok0 * kv_row_stride + hkv * D, kv_row_stride, kt * BN,
-                                 S - 1);
+    const bf16* kb0 = kr + tok0 * kv_row_stride + hkv * D;
+    constexpr int NCH = D / 8;
+#pragma unroll
+    for (int u = 0; u < BN * NCH / 256; ++u) {
+      const int idx = u * 256 + tid, r = idx / NCH, c = idx % NCH;
+      const int krow = min(kt * BN + r, S - 1);
+      *(bf16x8*)(Ks + r * KLD + c * 8) = *(const bf16x8*)(kb0 + (size_t)krow * kv_row_stride + c * 8);
+    }
   }
   f32x16 dka[NDB], dva[NDB];
 #pragma unroll
@@ -247,18 +258,23 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   first(e, hq);
   if (hq < h_end) issue(0, hq, packed_idx(qpack[e]), 0);
   // one step per half tile, unrolled by buffer
-  int BUF = 0;
-  auto step = [&](int) {
+  int kro = (32 * wave + col) * KLD + 8 * h;
+  int cur = 0;
+  while (hq < h_end) {
     const bool need_mask = packed_kind(qpack[e]) != kTileFull || (anchor && kt == 0);
     int e1 = e, h1 = hq, half1 = half ^ 1;
     if (half1 == 0) advance(e1, h1);
     const int qt1 = h1 < h_end ? packed_idx(qpack[e1]) : 0;
     wait_direct_loads();
-    __syncthreads();      // half tile in buffer BUF visible; the other buffer free
-    if (h1 < h_end) issue(BUF ^ 1, h1, qt1, half1);
-    const bf16* Qc = Qs[BUF];
-    const bf16* Gc = Gs[BUF];
-    const float* stc = &s_st[BUF][0][0] + half * BH;
+    __syncthreads();      // half tile in buffer `cur` visible; the other buffer free
+    if (h1 < h_end) issue(cur ^ 1, h1, qt1, half1);
+    // this lane's K row offset, re-declared live in every step so that the
+    // eight reads below stay one register plus immediate offsets (hoisted out
+    // of the loop they would take eight registers)
+    asm volatile("" : "+v"(kro));
+    const bf16* Qc = Qs[cur];
+    const bf16* Gc = Gs[cur];
+    const float* stc = &s_st[cur][0][0] + half * BH;
 
     // S = Q K^T, dP = dO V^T for the 32 queries: columns = this wave's keys.
     f32x16 sp, dp;
@@ -267,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int off = T::chunk_off(col, 2 * kk + h);
-      const bf16x8 kb = *(const bf16x8*)(Ks + T::chunk_off(32 * wave + col, 2 * kk + h));
+      const bf16x8 kb = *(const bf16x8*)(Ks + kro + 16 * kk);
       sp = mfma32(*(const bf16x8*)(Qc + off), kb, sp);
       dp = mfma32(*(const bf16x8*)(Gc + off), vf[kk], dp);
     }
@@ -305,10 +321,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
         dka[dblk] = mfma32(tr_operand<D>(Qc, 16 * c, 32 * dblk), db_[c], dka[dblk]);
       }
     e = e1; hq = h1; half = half1;
-  };
-  while (hq < h_end) {
-    step(0);
-    BUF ^= 1;
+    cur ^= 1;
   }
 
   // Epilogue: dK = R(pos)^T (scale * dK'), dV as accumulated.
