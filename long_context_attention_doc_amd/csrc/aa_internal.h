@@ -240,25 +240,6 @@ __device__ __forceinline__ lds_void* lds_ptr(uint32_t a) { return (lds_void*)(ui
 // the swizzle places there.  Global rows row0 .. row0+ROWS-1 are clamped to
 // row_max.  Every thread of the NTHREADS-thread workgroup calls it; the data
 // is visible after wait_direct_loads() and a workgroup barrier.
-template <int D, int ROWS, int NTHREADS>
-__device__ __forceinline__ void tile_load_direct(bf16* lds_tile, const bf16* gbase,
-                                                 size_t row_stride, int row0, int row_max) {
-  constexpr int NCH = D / 8;
-  constexpr int ITERS = ROWS * NCH / NTHREADS;
-  static_assert(ROWS * NCH % NTHREADS == 0, "tile must split evenly over the waves");
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int u = 0; u < ITERS; ++u) {
-    const int base = (wave * ITERS + u) * 64;     // first physical chunk of this instruction
-    const int pc_idx = base + lane;
-    const int row = pc_idx / NCH, pc = pc_idx % NCH;
-    const int c = (pc ^ SwzTile<D>::swz(row)) & (NCH - 1);
-    const bf16* src = gbase + (size_t)min(row0 + row, row_max) * row_stride + c * 8;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds_tile + base * 8), 16, 0, 0);
-  }
-}
-
-// The same copy with the per-lane part of the addresses computed once:
 // DirectTile<D, ROWS, NTHREADS>::init() precomputes each lane's element
 // offsets (row * row_stride + chunk * 8) inside a tile; load() adds the
 // tile's first row (a wave-uniform base) and only re-derives clamped offsets
@@ -283,7 +264,9 @@ struct DirectTile {
       off[u] = (uint32_t)((row * row_stride + chunk * 8) * sizeof(bf16));
     }
   }
-  // load() with the LDS tile given by its 32-bit address.
+  // load() with the LDS tile given by its 32-bit address.  The compiler then
+  // ties the copy to no __shared__ variable and inserts no wait for it before
+  // LDS reads; the caller's wait_direct_loads() and barrier order the data.
   __device__ __forceinline__ void load_at(uint32_t lds_tile, const bf16* gbase, size_t row_stride,
                                           int row0, int row_max) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
