@@ -36,8 +36,14 @@ KERNEL_SOURCE = {"fwd": "fwd.hip", "bwd_dkdv": "bwd.hip", "bwd_dq": "bwd.hip"}
 
 
 def _src_hash(kernel: str) -> str:
-    p = os.path.join(ROOT, "long_context_attention_doc_amd", "csrc", KERNEL_SOURCE[kernel])
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel's source file followed by its extra build flags (none
+    for most sources), so a counter summary goes stale when either changes."""
+    from long_context_attention_doc_amd.build import SOURCE_FLAGS
+    name = KERNEL_SOURCE[kernel]
+    p = os.path.join(ROOT, "long_context_attention_doc_amd", "csrc", name)
+    h = hashlib.sha256(open(p, "rb").read())
+    h.update(" ".join(SOURCE_FLAGS.get(name, [])).encode())
+    return h.hexdigest()[:16]
 
 
 def _traffic(kernel: str, workload: str):

@@ -24,13 +24,19 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source code generation options.  The backward kernels (two waves per
+# SIMD at the 256-register limit, latency-bound) run 1-6% faster with the
+# backend's iterative ILP scheduler; the forward is neutral to slower with it.
+SOURCE_FLAGS = {
+    "bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB) -> str:
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, *(extra or []), *sources(), "-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -40,6 +46,32 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB)
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs:
         print(msgs)
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB) -> str:
+    """Compile every source to an object (in parallel), then link the library."""
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    procs, objs = [], []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [HIPCC, *compile_flags, *SOURCE_FLAGS.get(os.path.basename(src), []), *(extra or []),
+               "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                            text=True)))
+        objs.append(obj)
+    for cmd, p in procs:
+        text = p.communicate()[0]
+        msgs = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l and l.strip())
+        if p.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({p.returncode}) on {cmd[-3]}:\n{msgs}")
+        if verbose and msgs:
+            print(msgs)
+    tmp = out + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     return out
 
