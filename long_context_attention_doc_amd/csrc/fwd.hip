@@ -173,8 +173,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     const bf16* Vc = BUF ? Vs1 : Vs0;
 
     // A 32-key block that none of the wave's queries may see (a document
-    // edge or the causal diagonal inside a partial tile) gets -inf scores
-    // and no products: its weights are exactly zero.
+    // edge or the causal diagonal inside a partial tile) has exactly zero
+    // weights: every stage below skips it (wave-uniform branches), so its
+    // score registers are never filled or read.
     bool live[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
     // S^T = K Q^T for this wave's 32 queries and the BN keys of the tile.
     f32x16 st[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb)
       if (live[kb]) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) st[kb][j] = 0.f;
@@ -193,37 +194,35 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
         for (int kk = 0; kk < NKK; ++kk)
           st[kb] = mfma32(*(const bf16x8*)(Kc + T::chunk_off(kb * 32 + col, 2 * kk + h)), qf[kk],
                           st[kb]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) st[kb][j] = -INFINITY;
       }
-    }
     if (need_mask) {
       // keys outside [qlo, qhi] (row-local) are masked
       const int a = qlo - kt * BN - 4 * h, z = qhi - kt * BN - 4 * h;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
+        if (live[kb]) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
-          st[kb][j] = (off >= a && off <= z) ? st[kb][j] : -INFINITY;
+          for (int j = 0; j < 16; ++j) {
+            const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
+            st[kb][j] = (off >= a && off <= z) ? st[kb][j] : -INFINITY;
+          }
         }
     }
-    // Tile maximum (raw scores; the scale is positive).  IEEE maximum needs
-    // no input canonicalisation and fuses into three-input maxima.
-    float mk[NKB];
+    // Tile maximum over the live blocks (raw scores; the scale is positive).
+    // IEEE maximum needs no input canonicalisation and fuses into
+    // three-input maxima.
+    float mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      mk[kb] = st[kb][0];
+    for (int kb = 0; kb < NKB; ++kb)
+      if (live[kb]) {
+        float mk = st[kb][0];
 #pragma unroll
-      for (int j = 1; j < 15; j += 2)
-        mk[kb] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mk[kb], st[kb][j]),
-                                               st[kb][j + 1]);
-      mk[kb] = __builtin_elementwise_maximum(mk[kb], st[kb][15]);
-    }
-    float mt = mk[0];
-#pragma unroll
-    for (int kb = 1; kb < NKB; ++kb) mt = __builtin_elementwise_maximum(mt, mk[kb]);
+        for (int j = 1; j < 15; j += 2)
+          mk = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mk, st[kb][j]),
+                                             st[kb][j + 1]);
+        mk = __builtin_elementwise_maximum(mk, st[kb][15]);
+        mt = __builtin_elementwise_maximum(mt, mk);
+      }
     mt = __builtin_elementwise_maximum(mt, partner(mt)) * scale_log2;
     const bool raise = mt > m;
     if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -237,35 +236,31 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
         for (int j = 0; j < 16; ++j) acc[db][j] *= factor;
     }
 
-    // P^T = exp2(s * scale_log2 - m) as bf16 B operands, one per 16-key step.
-    // The row sum adds the same bf16 weights that multiply V (pairwise dot
-    // products with ones), so numerator and denominator see identical P.
-    bf16x8 pb[BN / 16];
+    // P^T = exp2(s * scale_log2 - m) as bf16 B operands, one per 16-key step,
+    // and O^T += V^T P^T, over the live key blocks.  The row sum adds the
+    // same bf16 weights that multiply V (pairwise dot products with ones),
+    // so numerator and denominator see identical P.
     const float nm = m == -INFINITY ? 0.f : -m;   // a row that has seen no key yet
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        pb[2 * kb + (j >> 3)][j & 7] =
-            (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j], scale_log2, nm));
     const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-#pragma unroll
-    for (int c = 0; c < BN / 16; ++c) {
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 0, 1), ones, l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 2, 3), ones, l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 4, 5), ones, l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 6, 7), ones, l, false);
-    }
-
-    // O^T += V^T P^T over the live key blocks.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
       if (live[kb]) {
+        bf16x8 pb[2];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          pb[j >> 3][j & 7] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][j], scale_log2, nm));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 0, 1), ones, l, false);
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 2, 3), ones, l, false);
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 4, 5), ones, l, false);
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 6, 7), ones, l, false);
+        }
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int c = 2 * kb; c < 2 * kb + 2; ++c)
-            acc[db] = mfma32(tr_operand<D>(Vc, 16 * c, 32 * db), pb[c], acc[db]);
+          for (int c = 0; c < 2; ++c)
+            acc[db] = mfma32(tr_operand<D>(Vc, 32 * kb + 16 * c, 32 * db), pb[c], acc[db]);
       }
   };
   for (int i = 0; i < n_tiles; i += 2) {
