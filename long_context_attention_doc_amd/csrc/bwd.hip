@@ -240,17 +240,23 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   // tile x its two halves.
   const int e_begin = kptr[ktile], e_end = kptr[ktile + 1];
   const int h_end = (hkv + 1) * group;
+  // The query tiles are taken from the document's last one down to the
+  // diagonal: the workgroups of neighbouring key tiles then all start on
+  // the same query tile and move down it in step, so each Q/dO tile is
+  // fetched from HBM about once per XCD instead of once per staggered
+  // workgroup (walking up from each diagonal, 64 concurrent workgroups
+  // span about 4 MB of Q/dO, the size of an XCD's L2).
   auto first = [&](int& ee, int& hh) {
-    ee = e_begin;
+    ee = e_end - 1;
     hh = hkv * group;
     if (e_begin >= e_end) { hh = h_end; return; }
-    while (ee < e_end && packed_kind(qpack[ee]) == kTileAnchor) ++ee;
-    if (ee >= e_end) hh = h_end;             // nothing live besides the anchor
+    while (ee >= e_begin && packed_kind(qpack[ee]) == kTileAnchor) --ee;
+    if (ee < e_begin) hh = h_end;            // nothing live besides the anchor
   };
   auto advance = [&](int& ee, int& hh) {
     do {
-      ++ee;
-      if (ee >= e_end) { ee = e_begin; ++hh; }
+      --ee;
+      if (ee < e_begin) { ee = e_end - 1; ++hh; }
     } while (hh < h_end && packed_kind(qpack[ee]) == kTileAnchor);
   };
 
