@@ -49,3 +49,29 @@ def test_bench_workloads_bound(name, bound):
         flops = f * w.D * w.Hq * fl["pairs_per_head"]
         nbytes = kernel_algorithmic_bytes(kern, w.B, w.S, w.Hq, w.Hkv, w.D)
         assert roofline_point(flops, nbytes, 1.0, PEAK_TF, PEAK_GBS)["bound"] == bound
+
+
+def test_counter_summary_goes_stale_with_source_or_build_flags(monkeypatch, tmp_path):
+    """bench.py reports a kernel's HBM traffic from a committed counter summary
+    only while the summary's recorded hash matches the kernel's source file
+    and its extra build flags; a change of either makes it null."""
+    import bench
+    from long_context_attention_doc_amd import build as B
+    csrc = tmp_path / "long_context_attention_doc_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    (csrc / "bwd.hip").write_text("// kernel source v1\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(B, "SOURCE_FLAGS", {"bwd.hip": ["-mllvm", "-some-option"]})
+    h = bench._src_hash("bwd_dkdv")
+    (tmp_path / "profiles" / "bwd_dkdv_64k_hbm_counters.txt").write_text(
+        f"hbm_bytes_per_launch: 1.5e+09\nsource_sha256_16: {h}   (source + flags)\n")
+    assert bench._traffic("bwd_dkdv", "64k") == 1.5e9
+    assert bench._traffic("bwd_dkdv", "8k") is None                # no summary for that workload
+    monkeypatch.setattr(B, "SOURCE_FLAGS", {})                     # flags changed
+    assert bench._src_hash("bwd_dkdv") != h
+    assert bench._traffic("bwd_dkdv", "64k") is None
+    monkeypatch.setattr(B, "SOURCE_FLAGS", {"bwd.hip": ["-mllvm", "-some-option"]})
+    (csrc / "bwd.hip").write_text("// kernel source v2\n")          # source changed
+    assert bench._traffic("bwd_dkdv", "64k") is None
+
