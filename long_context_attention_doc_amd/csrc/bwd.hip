@@ -142,10 +142,12 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
 // every query, so nothing is reduced across waves; a 64-query tile of the
 // plan is taken as two 32-query halves.  The two waves that share a SIMD
 // belong to different workgroups and are not held in step by a barrier.
-//   * The workgroup's K rows sit in swizzled LDS (B operand of S = Q K^T);
-//     the V operand (B of dP = dO V^T) stays in registers.
+//   * The workgroup's K rows sit in LDS with padded rows (B operand of
+//     S = Q K^T, read row-wise only); the V operand (B of dP = dO V^T) stays
+//     in registers.
 //   * Q and dO half tiles go straight into double-buffered swizzled LDS, one
-//     half ahead; row reads feed S and dP, transposing reads feed Q^T, dO^T.
+//     half ahead, the key tile's query tiles taken from the document's last
+//     one down; row reads feed S and dP, transposing reads feed Q^T, dO^T.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
