@@ -7,11 +7,13 @@ preprocessing), dK/dV and the anchor-key reduction (the library's anchor_attn_fw
 
 Prints ONE JSON line.  `value` is fwd+bwd TFLOP/s counting only unmasked
 (query, key) pairs (14*D flops per pair and query head); inputs are resident
-in HBM before the timed region starts.  `roofline` reports the dominant
-kernel's achieved rate from HIP events recorded by the library around each of
-its launches on the call's stream during the timed steps.  `cpu_baseline`
-times the float64 CPU oracle on a bounded sample of the same workload.
-"""
+in HBM before the timed region starts, and the timed steps run without any
+per-kernel instrumentation.  A second pass of as many steps, with HIP events
+recorded by the library around each of its launches on the call's stream,
+gives the per-kernel times: `roofline` reports the dominant kernel's achieved
+rate from them, against the nominal peak and against the peak at the engine
+clock sampled during the timed steps.  `cpu_baseline` times the float64 CPU
+oracle on a bounded sample of the same workload."""
 from __future__ import annotations
 
 import argparse
@@ -138,6 +140,67 @@ def device_peak() -> dict | None:
     return None
 
 
+class ClockSampler:
+    """Engine clock and socket power of GPU 0, polled from the firmware's
+    metrics table (amdsmi Python API) by a background thread while the timed
+    steps run.  It only reads; without amdsmi or a device it records nothing."""
+
+    def __init__(self, period_s: float = 0.01):
+        import threading
+        self.period = period_s
+        self.mhz, self.watts = [], []
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:   # no amdsmi or no device: no samples
+            self._smi = None
+
+    def _sample(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 0 < c < 0xFFFF]
+        if not clks and isinstance(m.get("current_gfxclk"), int):
+            clks = [m["current_gfxclk"]]
+        if clks:
+            self.mhz.append(sum(clks) / len(clks))
+        pw = m.get("current_socket_power")
+        if isinstance(pw, (int, float)) and 0 < pw < 0xFFFF:
+            self.watts.append(float(pw))
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self._sample()
+            except Exception:   # a failed read ends the sampling
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self._smi is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.mhz:
+            return None
+        return {"gfx_mhz_mean": sum(self.mhz) / len(self.mhz), "gfx_mhz_min": min(self.mhz),
+                "gfx_mhz_max": max(self.mhz), "samples": len(self.mhz),
+                "socket_power_w_mean": (sum(self.watts) / len(self.watts)) if self.watts else None,
+                "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), polled every 10 ms "
+                          "during the timed steps"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,8 +213,9 @@ def main() -> int:
     ap.add_argument("--no-fwd-workspace", action="store_true",
                     help="self-contained backward: rebuild positions, plan and rotated q, k "
                          "instead of reusing the forward's workspace")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip the extra timing of the step captured in a HIP graph and replayed")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph and replayed")
+    ap.add_argument("--no-graph", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--mode", default="anchor", choices=sorted(MODES),
                     help="anchor (default, the method) | anchor_continuous | intra_doc_reset | "
                          "intra_doc_continuous | full_causal | interleaved: the pages' other "
@@ -227,24 +291,37 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    api.profile_begin(64 * max(1, args.steps))
+    # The timed steps: no per-kernel events (the library's profiling is off),
+    # only the events around the whole region and between fwd and bwd.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        step(marks[i])
-    e1.record()
-    torch.cuda.synchronize()
-    prof = api.profile_end()
+    with ClockSampler() as clk:
+        e0.record()
+        for i in range(args.steps):
+            step(marks[i])
+        e1.record()
+        torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     bwd_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / args.steps
     fwd_ms = ms - bwd_ms
     per_step = sorted(c.elapsed_time(b) for a, b, c in marks)     # start of step -> end of backward
     median_ms = per_step[len(per_step) // 2]
+    # A second pass of as many steps with the library's per-kernel HIP events
+    # (recorded on the call's stream around every launch) gives the kernel
+    # times of the roofline.
+    api.profile_begin(64 * max(1, args.steps))
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record()
+    for i in range(args.steps):
+        step()
+    p1.record()
+    torch.cuda.synchronize()
+    prof = api.profile_end()
+    profiled_ms = p0.elapsed_time(p1) / args.steps
 
     # The same step captured once in a HIP graph and replayed: the kernels and
     # their work are identical, the host launch gaps between them are gone.
     graph_ms = None
-    if not args.no_graph:
+    if args.graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -284,8 +361,17 @@ def main() -> int:
     # (2.5 PFLOP/s / 8 TB/s = 312.5 flop/B): the short-documents workload's
     # kernels fall below it
     rp = roofline_point(algo, algo_bytes, avg_ms * 1e-3, PEAK_BF16_TFLOPS, PEAK_HBM_GBS)
+    clock = clk.summary()
+    dpk = device_peak()
+    clock_peak = None
+    if clock and dpk:
+        # dense bf16 MFMA rate at the engine clock measured during the steps
+        clock_peak = dpk["compute_units"] * clock["gfx_mhz_mean"] * 1e6 * 4096 / 1e12
+        clock["bf16_dense_peak_tflops_at_clock"] = clock_peak
     roofline = {"bound": rp["bound"], "kernel": f"k_{dom}", "achieved": rp["achieved"],
                 "peak": rp["peak"], "unit": rp["unit"], "frac": rp["frac"],
+                "frac_at_measured_clock": (rp["achieved"] / clock_peak
+                                           if clock_peak and rp["unit"] == "TFLOP/s" else None),
                 "traffic": _traffic(dom, w.name) if args.mode == "anchor" else None,
                 "avg_launch_ms": avg_ms,
                 "algorithmic_flops_per_launch": algo,
@@ -308,13 +394,16 @@ def main() -> int:
         "graph_tflops": (total_flops / (graph_ms * 1e-3) / 1e12) if graph_ms else None,
         "tokens_per_s": tokens / (ms * 1e-3),
         "pct_of_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "pct_of_bf16_peak_at_measured_clock": (100.0 * tflops / clock_peak) if clock_peak else None,
+        "clock": clock,
+        "profiled_ms_per_step": profiled_ms,
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms if w.backward else None,
         "tflops_no_recompute": ((fl["total_no_recompute"] if w.backward else fl["fwd"])
                                 / (ms * 1e-3) / 1e12),
         "algorithmic_hbm_bytes": nbytes["total"],
         "algorithmic_hbm_gbs": nbytes["total"] / (ms * 1e-3) / 1e9,
         "pct_of_hbm_peak": 100.0 * nbytes["total"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "device": device_peak(),
+        "device": dpk,
         "kernel_ms_per_step": {k_: round(v_, 4) for k_, v_ in per_kernel_ms.items()},
         "roofline": roofline,
     }

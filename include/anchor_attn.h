@@ -261,10 +261,12 @@ aa_status anchor_attn_rope(const void* x, const int32_t* pos, int B, int S, int 
  * call synchronises `stream`).  *out (host) receives AA_OK or AA_EDOCS. */
 aa_status anchor_attn_device_status(const void* workspace, hipStream_t stream, int32_t* out);
 
-/* ---- optional per-kernel timing (diagnostics; not thread-safe) ----------
+/* ---- optional per-kernel timing (diagnostics) -----------------------------
  * Between anchor_attn_profile_begin() and anchor_attn_profile_end(), every
- * kernel the calls above enqueue is bracketed by HIP events recorded on the
- * call's stream.  begin() creates the events (it allocates; call it outside
+ * kernel that the calls above enqueue from the same host thread is bracketed
+ * by HIP events recorded on the call's stream.  The session belongs to the
+ * calling thread (thread-local state): calls from other threads are not
+ * timed and are unaffected.  begin() creates the events (it allocates; call it outside
  * any graph capture); end() waits for them and writes, for each kernel id
  * below, the summed milliseconds (ms[id], host) and launch count (count[id],
  * host) for ids < n, then releases the events.  At most `max_launches`

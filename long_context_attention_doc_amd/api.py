@@ -204,15 +204,20 @@ def anchor_attn_bwd(q, k, v, o, lse, dout, cu_doc_lens, rope_base: float, causal
     """Backward pass; returns (dq, dk, dv) bf16.  flags as for anchor_attn_fwd."""
     lib = load()
     _check_cu(cu_doc_lens, q.shape[0], q.shape[1], flags)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    ws_n = workspace_size(B, S, Hq, Hkv, D, True)
+    if (flags & FLAG_FWD_WORKSPACE) and (workspace is None or workspace.numel() < ws_n):
+        # a fresh workspace does not hold the forward's positions, plan and
+        # rotated q, k that the flag promises
+        raise ValueError("FLAG_FWD_WORKSPACE needs the forward's workspace, sized for the "
+                         f"backward ({ws_n} bytes)")
     for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need_bf16(n, t)
     _need_o(o, flags)
-    B, S, Hq, D = q.shape
-    Hkv = k.shape[2]
     if lse.dtype != torch.float32 or lse.shape != (B, Hq, S) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [B,Hq,S]")
     cu = _dev_cu(cu_doc_lens, q.device)
-    ws_n = workspace_size(B, S, Hq, Hkv, D, True)
     if workspace is None or workspace.numel() < ws_n:
         workspace = _workspace(ws_n, q.device)
     dq = torch.empty_like(q)
@@ -420,14 +425,18 @@ class _AnchorAttnFn(torch.autograd.Function):
         q, k, v, o, lse, cu = ctx.saved_tensors
         rope_base, causal, scale, flags = ctx.cfg
         # dO is taken in bf16 (an fp32 O's gradient arrives in fp32)
+        # The workspace stays with ctx: the backward writes only past the
+        # forward's part of it, so a second backward (retain_graph) finds the
+        # forward's state again.
         dq, dk, dv = anchor_attn_bwd(q, k, v, o, lse, do.to(torch.bfloat16).contiguous(), cu,
                                      rope_base, causal, scale, ctx.ws, flags=flags | FLAG_FWD_WORKSPACE)
-        ctx.ws = None
         return dq, dk, dv, None, None, None, None, None
 
 
 def anchor_attention(q, k, v, cu_doc_lens, rope_base: float, causal: bool = True,
                      softmax_scale: float | None = None, flags: int = 0):
-    """AnchorAttention with autograd: q [B,S,Hq,D], k/v [B,S,Hkv,D] bf16 on the GPU."""
+    """AnchorAttention with autograd: q [B,S,Hq,D], k/v [B,S,Hkv,D] bf16 on the GPU.
+    A host cu_doc_lens is validated here, before it is copied to the device."""
+    _check_cu(cu_doc_lens, q.shape[0], q.shape[1], flags)
     cu = _dev_cu(cu_doc_lens, q.device)
     return _AnchorAttnFn.apply(q, k, v, cu, float(rope_base), bool(causal), softmax_scale, int(flags))

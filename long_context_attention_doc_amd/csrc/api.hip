@@ -167,14 +167,16 @@ RopeTheta make_theta(int D, double base) {
     if ((expr) != hipSuccess) return AA_EHIP;         \
   } while (0)
 
-// Opt-in per-kernel timing: events recorded around every launch.
+// Opt-in per-kernel timing: events recorded around every launch.  The state
+// is per host thread, so calls made from other threads neither see nor
+// disturb a profiling session; without one the library keeps no state.
 struct Profiler {
   bool on = false;
   int cap = 0, used = 0;
   hipEvent_t* ev = nullptr;   // 2 * cap events
   int* id = nullptr;          // kernel id of each recorded launch
 };
-Profiler g_prof;
+thread_local Profiler g_prof;
 
 // Brackets one launcher call with profiling events when profiling is on.
 #define AA_LAUNCH(kid, stream, expr)                                              \

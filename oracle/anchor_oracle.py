@@ -374,11 +374,6 @@ def backward(q, k, v, do, cu, rope_base: float, causal: bool = True, scale: floa
     return dq, dk, dv, q_rows, k_cols
 
 
-def rotated_bf16_reference(x, pos, base: float) -> np.ndarray:
-    """float64 rotation of x (last axis D, token axis first) for the RoPE-stage check."""
-    return rope(_f64(x), np.asarray(pos), base)
-
-
 # ----------------------------------------------------------------------------
 # Block-sparse tile plan, by brute force over the explicit mask
 # ----------------------------------------------------------------------------

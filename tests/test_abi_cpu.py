@@ -154,3 +154,24 @@ def test_python_binding_checks_host_cu():
         api.anchor_attn_fwd(q, kv, kv, np.asarray([0, 1, 5, 8, 9, 16], dtype=np.int32), 1e4)
     with pytest.raises(ValueError, match="cu_doc_lens"):
         api.anchor_attn_bwd(q, kv, kv, q, torch.zeros((2, 2, 8)), q, [0, 1, 8, 9, 15], 1e4)
+
+
+def test_python_binding_guards_the_forward_workspace_and_autograd_cu():
+    """FLAG_FWD_WORKSPACE without the forward's (backward-sized) workspace is
+    rejected before anything is launched, and the autograd entry point checks
+    a host cu_doc_lens before copying it to the device."""
+    import torch
+    from long_context_attention_doc_amd import api
+    q = torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16)
+    kv = torch.zeros((1, 8, 1, 64), dtype=torch.bfloat16)
+    lse = torch.zeros((1, 2, 8))
+    cu = np.asarray([0, 1, 8], dtype=np.int32)
+    small = torch.zeros(16, dtype=torch.uint8)
+    for ws in (None, small):
+        with pytest.raises(ValueError, match="FLAG_FWD_WORKSPACE"):
+            api.anchor_attn_bwd(q, kv, kv, q, lse, q, cu, 1e4, workspace=ws,
+                                flags=api.FLAG_FWD_WORKSPACE)
+    with pytest.raises(ValueError, match="cu_doc_lens"):
+        api.anchor_attention(q, kv, kv, np.asarray([0, 1, 7], dtype=np.int32), 1e4)
+    with pytest.raises(ValueError, match="anchor"):
+        api.anchor_attention(q, kv, kv, np.asarray([0, 8], dtype=np.int32), 1e4)

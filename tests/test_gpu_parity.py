@@ -139,6 +139,10 @@ def test_fp32_output(gpu_lib, case):
     say(f"[fp32-o] {name} O err fp32 {e32:.2e} (bf16 output {e16:.2e}) dq {e[0]:.2e} dk {e[1]:.2e} "
         f"dv {e[2]:.2e}")
     assert e32 <= O_TOL and max(e) <= G_TOL
+    # The bf16 output is the float32 one rounded to nearest even: the rounding
+    # moves an entry by at most 2^-9 of its size, so its error is bounded by
+    # the float32 error plus 2^-9 max|O| (max|O| within e32 of max|O_ref|).
+    assert e16 <= e32 + 2.0 ** -9 * (1.0 + e32), (e16, e32)
 
 
 def test_interleaved_heads_bit_identical(gpu_lib):
@@ -193,6 +197,27 @@ def test_backward_reusing_the_forward_workspace(gpu_lib, flags):
     g_self = gpu_lib.anchor_attn_bwd(q, k, v, o, lse, do, cu, 5e6, flags=flags)
     for a, b in zip(g_reuse, g_self):
         assert torch.equal(a, b)
+
+
+def test_autograd_backward_twice_with_retained_graph(gpu_lib):
+    """A second backward through a retained graph reuses the forward's
+    workspace kept by the autograd context: both give the same gradients, and
+    they match the direct backward."""
+    B, S, Hq, Hkv, D = 1, 600, 4, 2, 128
+    cu = W.cu_doc_lens_from_lengths([[250, 1, 348]], S)
+    q, k, v, do = _inputs(B, S, Hq, Hkv, D, 21)
+    qc, kc, vc = (t.cuda().requires_grad_(True) for t in (q, k, v))
+    o = gpu_lib.anchor_attention(qc, kc, vc, cu, 5e6)
+    o.backward(do.cuda(), retain_graph=True)
+    g1 = [t.grad.clone() for t in (qc, kc, vc)]
+    for t in (qc, kc, vc):
+        t.grad = None
+    o.backward(do.cuda())
+    g2 = [t.grad for t in (qc, kc, vc)]
+    o2, lse2 = gpu_lib.anchor_attn_fwd(q.cuda(), k.cuda(), v.cuda(), cu, 5e6)
+    g3 = gpu_lib.anchor_attn_bwd(q.cuda(), k.cuda(), v.cuda(), o2, lse2, do.cuda(), cu, 5e6)
+    for a, b, c in zip(g1, g2, g3):
+        assert torch.equal(a, b) and torch.equal(a, c)
 
 
 def test_autograd_function(gpu_lib):
@@ -278,6 +303,43 @@ def test_full_size_sampled(gpu_lib, wname):
     e_dq = rel_frob(dq_g, dq_r)
     say(f"[full] {wname} dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
     assert max(e_dq, e_dk, e_dv) <= G_TOL
+
+
+def _long_doc_keys(w):
+    """Keys of the row's longest document: its first tokens, the start of
+    its second and third 128-key tiles, its middle and its last token."""
+    cu = w.cu_doc_lens
+    n = int(np.argmax(np.diff(cu)))
+    s, e = int(cu[n]), int(cu[n + 1])
+    mid = (s + e) // 2
+    return s, e, np.array(sorted({s, s + 1, s + 63, s + 64, s + 128, s + 257, mid, mid + 1, e - 1}))
+
+
+@pytest.mark.parametrize("wname", ["8k", "64k"])
+def test_long_document_key_gradients(gpu_lib, wname):
+    """dK/dV of keys inside the workload's longest document (8K: 2,532
+    tokens, 64K: 17,752 tokens) at full size, so that the key-major kernel's
+    walk over every query tile of a long document is compared with the
+    oracle; the oracle sums over exactly the rows that see those keys."""
+    w = W.get(wname)
+    B, S, Hq, Hkv, D = w.B, w.S, w.Hq, w.Hkv, w.D
+    s, e, keys = _long_doc_keys(w)
+    say(f"[long-doc] {wname} document [{s}, {e}) ({e - s} tokens), keys {keys.tolist()}")
+    q, k, v, do = W.make_tensors(B, S, Hq, Hkv, D, w.tensor_seed)
+    cu = w.cu_doc_lens
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    say(f"[long-doc] {wname} fwd+bwd on GPU")
+    o, lse = gpu_lib.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base)
+    dq, dk, dv = gpu_lib.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base)
+    torch.cuda.synchronize()
+    for h in (0, Hq - 1):
+        say(f"[long-doc] {wname} oracle backward, head {h}")
+        _, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, w.rope_base, heads=[h], q_rows=[s],
+                                              k_cols=keys)
+        e_dk = rel_frob(f64(dk).reshape(B * S, Hkv, D)[keys][:, [h]], dk_r[:, [h]])
+        e_dv = rel_frob(f64(dv).reshape(B * S, Hkv, D)[keys][:, [h]], dv_r[:, [h]])
+        say(f"[long-doc] {wname} head {h}: dk {e_dk:.2e} dv {e_dv:.2e}")
+        assert max(e_dk, e_dv) <= G_TOL
 
 
 def test_anchor_key_gradients_8k(gpu_lib):

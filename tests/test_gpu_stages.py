@@ -106,18 +106,54 @@ def _rows_of(gp, bq, key="q"):
     return gp["qidx"][a:b].cpu().numpy(), gp["qkind"][a:b].cpu().numpy()
 
 
-@pytest.mark.parametrize("wname", ["64k", "128k_gqa", "short_docs"])
-def test_tile_plan_bit_exact_full_size_sampled(gpu_lib, wname):
-    """Full-size plans in the kernels' tile shapes; sampled query tiles (query
-    major) and key tiles (key major) are checked against the brute force."""
+def _kind_totals(gp):
+    n = int(gp["n_live"].cpu().item())
+    kk = gp["kkind"][:n].cpu().numpy()
+    return [int((kk == 1).sum()), int((kk == 2).sum()), int((kk == 3).sum())]
+
+
+# F/P/A totals of the 128 x 64 plans of the workloads, recorded independently
+# of this repository when the workloads were specified
+# (tests/golden/workload_partitions_and_tiles.json)
+def _recorded_totals(wname):
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "workload_partitions_and_tiles.json")))
+    return g["tile_totals"].get(wname, {})
+
+
+@pytest.mark.parametrize("wname", ["64k", "short_docs"])
+def test_tile_plan_bit_exact_full_size_whole(gpu_lib, wname):
+    """Whole full-size plans in the kernels' tile shapes (forward and dQ:
+    128 x 64 query-major; dK/dV: 64 x 128 key-major), every entry against the
+    brute force, plus the kind totals."""
     w = W.get(wname)
+    cu = w.cu_doc_lens
+    for BM, BN in ((128, 64), (64, 128)):
+        say(f"[plan] {wname} tile={BM}x{BN}: GPU plan")
+        gp = gpu_lib.anchor_attn_tile_plan(cu, w.B, w.S, BM, BN)
+        say(f"[plan] {wname} tile={BM}x{BN}: oracle plan")
+        ref = oracle.tile_plan(cu, w.B, w.S, BM, BN)
+        _cmp_plan(gp, ref, w.B)
+        rec = _recorded_totals(wname).get(f"{BM}x{BN}")
+        say(f"[plan] {wname} tile={BM}x{BN}: F/P/A {_kind_totals(gp)} (recorded {rec})")
+        if rec:
+            assert _kind_totals(gp) == rec[:3]
+
+
+def test_tile_plan_full_size_128k_sampled(gpu_lib):
+    """128K GQA: sampled query tiles (query major) and key tiles (key major)
+    against the brute force, and the kind totals of the 128 x 64 plan."""
+    w = W.get("128k_gqa")
     cu = w.cu_doc_lens
     rng = np.random.default_rng(5)
     for BM, BN in ((128, 64), (64, 128)):
-        say(f"[plan] {wname} tile={BM}x{BN}")
+        say(f"[plan] 128k_gqa tile={BM}x{BN}")
         gp = gpu_lib.anchor_attn_tile_plan(cu, w.B, w.S, BM, BN)
         nq, nk = gp["nq"], gp["nk"]
-        # live-tile total from the closed form is not available; check sampled rows/cols
+        if (BM, BN) == (128, 64):
+            assert _kind_totals(gp) == [391396, 3733, 653]
         for b in range(w.B):
             for qt in sorted(set([0, 1, nq - 1] + list(rng.integers(0, nq, 6)))):
                 ref = oracle.tile_kinds_row(cu, w.B, w.S, BM, BN, b, int(qt))
@@ -154,9 +190,16 @@ def test_rope_stage_within_one_ulp(gpu_lib, wname):
     pair_mag = np.repeat(np.abs(xin[..., 0::2]) + np.abs(xin[..., 1::2]), 2, axis=-1)
     bound = ulp + 2.0 ** -22 * pair_mag
     assert np.all(diff <= bound), float((diff / bound).max())
+    # A result differs from RNE(float64) only when the float32 value and the
+    # exact one straddle a bf16 rounding midpoint.  With the float32 error at
+    # most delta = 2^-23 (|x0| + |x1|) (cos/sin, the products and the sum each
+    # rounded once), that happens with probability at most delta / ulp for a
+    # result placed uniformly in its ulp; the mean over the elements is the
+    # expected mismatch rate, and the measured rate stays within twice it.
+    pred = float(np.minimum(1.0, 2.0 ** -23 * pair_mag / ulp).mean())
     rate = float((diff > 0).mean())
-    say(f"[rope] {wname} mismatch rate {rate:.2e}")
-    assert rate <= 1e-3
+    say(f"[rope] {wname} mismatch rate {rate:.2e} (bound-derived expectation {pred:.2e})")
+    assert rate <= 2.0 * pred + 1e-5
     # the anchor (position 0) is unchanged: R_0 = I
     assert torch.equal(y[0, 0], x[0, 0])
 

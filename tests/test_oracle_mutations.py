@@ -36,6 +36,12 @@ MUTANTS = [
     ("interleaved chunks ignored", "    if seg_doc is None:\n        return seg", "    if True:\n        return seg"),
     ("document label without its row", "    label_of_seg = row * span + seg_doc + 1",
      "    label_of_seg = seg_doc + 1"),
+    ("key-major column classified as its query tile",
+     "    return np.array([_classify(m[qt * BM:(qt + 1) * BM], e[qt * BM:(qt + 1) * BM], kt, anchor)",
+     "    return np.array([_classify(m[qt * BM:(qt + 1) * BM], e[qt * BM:(qt + 1) * BM], qt, anchor)"),
+    ("key-major column shifted by one key",
+     "    cols = np.arange(b * S + kt * BN, b * S + min(S, (kt + 1) * BN))",
+     "    cols = np.arange(b * S + kt * BN + 1, b * S + min(S, (kt + 1) * BN + 1))"),
 ]
 PIN_FILES = ("test_oracle_pins.py", "test_oracle_modes.py", "test_oracle_interleaved.py")
 
@@ -54,6 +60,6 @@ def test_mutant_is_caught(tmp_path, name, old, new):
     env["PYTHONPATH"] = str(tmp_path) + os.pathsep + ROOT
     res = subprocess.run(
         [sys.executable, "-m", "pytest", *[os.path.join(ROOT, "tests", f) for f in PIN_FILES], "-x", "-q",
-         "-p", "no:cacheprovider", "-m", "not gpu"],
+         "-p", "no:cacheprovider", "-m", "not gpu and not slow"],
         cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=600)
     assert res.returncode != 0, f"mutant '{name}' survived the pins:\n{res.stdout[-2000:]}"

@@ -453,3 +453,156 @@ def test_plan_key_major_is_transpose():
     for b in range(B):
         for qt in range(nq):
             assert (b, qt, 0) in qm
+
+
+# ---------------------------------------------------------------- key-major checker
+def _brute_kinds(rows, S, BM, BN, causal=True, anchor=True):
+    """Tile kinds [B, nq, nk] by scalar loops over every element, from the
+    document lengths alone (no oracle mask): a query sees its row's anchor
+    (with ``anchor``) and the keys of its own document not after it (any of
+    them when not ``causal``).  Kinds: FULL when all BM*BN elements exist and
+    are seen, ANCHOR for key tile 0 when only column 0 is seen, PARTIAL for
+    any other tile with a seen element."""
+    B = len(rows)
+    nq, nk = -(-S // BM), -(-S // BN)
+    doc = []
+    for lens in rows:
+        d = []
+        if anchor:
+            d.append(-1)
+        for n, L in enumerate(lens):
+            d.extend([n] * L)
+        doc.append(d)
+    out = np.zeros((B, nq, nk), dtype=np.uint8)
+    for b in range(B):
+        for qt in range(nq):
+            for kt in range(nk):
+                seen = exist = 0
+                only_anchor = True
+                for i in range(qt * BM, (qt + 1) * BM):
+                    for j in range(kt * BN, (kt + 1) * BN):
+                        if i >= S or j >= S:
+                            continue
+                        exist += 1
+                        if anchor and (i == 0 or doc[b][i] == -1):
+                            ok = j == 0
+                        elif anchor and j == 0:
+                            ok = True
+                        else:
+                            ok = doc[b][i] == doc[b][j] and (j <= i or not causal)
+                        if ok:
+                            seen += 1
+                            if j != 0:
+                                only_anchor = False
+                if seen == 0:
+                    continue
+                if seen == exist == BM * BN:
+                    out[b, qt, kt] = oracle.KIND_FULL
+                elif anchor and kt == 0 and only_anchor:
+                    out[b, qt, kt] = oracle.KIND_ANCHOR
+                else:
+                    out[b, qt, kt] = oracle.KIND_PARTIAL
+    return out
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_plan_rows_and_columns_scalar_brute_force(case):
+    """tile_kinds_row, tile_kinds_col and tile_plan against element loops."""
+    rng = np.random.default_rng(300 + case)
+    anchor = case % 2 == 0
+    causal = case != 5
+    B = 2
+    S = int(rng.integers(20, 90))
+    BM, BN = [(16, 16), (32, 16), (16, 32)][case % 3]
+    if anchor:
+        rows = [W.random_partition(rng, S, 6) for _ in range(B)]
+        if case == 0:
+            rows[1] = [S - 1]
+        cu = _cu(rows, S)
+    else:
+        rows = [W.random_partition(rng, S + 1, 6) for _ in range(B)]   # partitions of S tokens
+        cu = W.cu_doc_lens_no_anchor(rows, S)
+    ref = _brute_kinds(rows, S, BM, BN, causal, anchor)
+    nq, nk = ref.shape[1:]
+    for b in range(B):
+        for qt in range(nq):
+            got = oracle.tile_kinds_row(cu, B, S, BM, BN, b, qt, causal, anchor)
+            assert np.array_equal(got, ref[b, qt]), (b, qt)
+        for kt in range(nk):
+            got = oracle.tile_kinds_col(cu, B, S, BM, BN, b, kt, causal, anchor)
+            assert np.array_equal(got, ref[b, :, kt]), (b, kt)
+    p = oracle.tile_plan(cu, B, S, BM, BN, causal, anchor)
+    for b in range(B):
+        for kt in range(nk):
+            a, z = p["kptr"][b * nk + kt], p["kptr"][b * nk + kt + 1]
+            live = np.nonzero(ref[b, :, kt])[0]
+            assert list(p["qidx"][a:z]) == list(live)
+            assert list(p["qkind"][a:z]) == list(ref[b, live, kt])
+
+
+def test_tile_kinds_col_is_the_key_major_plan():
+    """tile_kinds_col(b, kt) is column kt of the plan's key-major CSR, for
+    ragged S, two rows, with and without the anchor, causal or not."""
+    rng = np.random.default_rng(17)
+    for S, BM, BN in [(333, 64, 32), (300, 32, 64), (129, 64, 64)]:
+        for anchor in (True, False):
+            for causal in (True, False):
+                if anchor:
+                    cu = _cu([W.random_partition(rng, S, 7) for _ in range(2)], S)
+                else:
+                    cu = W.cu_doc_lens_no_anchor([W.random_partition(rng, S + 1, 7)
+                                                  for _ in range(2)], S)
+                p = oracle.tile_plan(cu, 2, S, BM, BN, causal, anchor)
+                nq, nk = p["nq"], p["nk"]
+                for b in range(2):
+                    for kt in range(nk):
+                        col = oracle.tile_kinds_col(cu, 2, S, BM, BN, b, kt, causal, anchor)
+                        a, z = p["kptr"][b * nk + kt], p["kptr"][b * nk + kt + 1]
+                        assert list(np.nonzero(col)[0]) == list(p["qidx"][a:z])
+                        assert list(col[np.nonzero(col)[0]]) == list(p["qkind"][a:z])
+                        assert len(col) == nq
+
+
+# ---------------------------------------------------------------- seeded workloads
+APPENDIX = os.path.join(GOLDEN, "workload_partitions_and_tiles.json")
+
+
+def test_workload_partitions_reproduce_the_recorded_ones():
+    g = json.load(open(APPENDIX))
+    for name, lens in g["partitions"].items():
+        w = W.get(name)
+        for r in w.doc_rows:
+            assert list(r) == lens, name
+
+
+def _tile_totals(name, BM, BN):
+    w = W.get(name)
+    p = oracle.tile_plan(w.cu_doc_lens, w.B, w.S, BM, BN)
+    kk = p["kkind"]
+    tot = [int((kk == oracle.KIND_FULL).sum()), int((kk == oracle.KIND_PARTIAL).sum()),
+           int((kk == oracle.KIND_ANCHOR).sum())]
+    # the key-major CSR holds the same tiles
+    assert len(p["qidx"]) == len(kk) == p["qptr"][-1] == p["kptr"][-1]
+    return w, tot
+
+
+def _check_totals(name):
+    g = json.load(open(APPENDIX))
+    rec = g["tile_totals"][name]
+    for shape, (F, P, A, eff) in rec.items():
+        BM, BN = map(int, shape.split("x"))
+        w, tot = _tile_totals(name, BM, BN)
+        assert tot == [F, P, A], (name, shape, tot)
+        pairs = sum(1 + sum(n * (n + 1) // 2 + n for n in r) for r in w.doc_rows)
+        assert round(pairs / ((F + P) * BM * BN), 3) == eff, (name, shape)
+
+
+@pytest.mark.parametrize("name", ["tiny", "8k"])
+def test_plan_tile_totals_of_the_workloads(name):
+    _check_totals(name)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["short_docs", "64k"])
+def test_plan_tile_totals_of_the_large_workloads(name):
+    _check_totals(name)
