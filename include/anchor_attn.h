@@ -155,6 +155,33 @@ aa_status anchor_attn_bwd_ex(const void* q, const void* k, const void* v, const 
                              void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 
+/* ---- allocation-free backward --------------------------------------------
+ * For callers that cannot allocate device memory at all (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * anchor_attn_bwd_ex with the same arguments, layouts and results, minus the
+ * workspace.  Its workspace is a fixed array of AA_NOALLOC_SCRATCH_BYTES in
+ * the library's code object, one per device, held from the library's load
+ * until the process ends; the call allocates nothing.
+ *   - Shapes whose backward workspace (anchor_attn_workspace_size(..., 1))
+ *     exceeds AA_NOALLOC_SCRATCH_BYTES are rejected with AA_EWORKSPACE before
+ *     anything is launched (160 MiB holds the backward of 8192 tokens x 32
+ *     heads x 128 features).
+ *   - AA_FLAG_FWD_WORKSPACE is rejected (AA_EINVAL): the scratch never holds
+ *     a forward's state.
+ *   - `stream` must belong to the current device (AA_EINVAL otherwise); the
+ *     first call on a device looks up its array's address.
+ *   - Every call on one device shares that device's array: calls that overlap
+ *     on one GPU (other streams, other threads) race and give wrong results.
+ *   - The device status word lives in the scratch, out of the caller's
+ *     reach: an invalid device cu_doc_lens shows as NaN gradients. */
+#define AA_NOALLOC_SCRATCH_BYTES (160u << 20)
+aa_status anchor_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout,
+                                  const int32_t* cu_doc_lens, int n_seg, double rope_base,
+                                  int causal, int flags, int B, int S, int Hq, int Hkv, int D,
+                                  float softmax_scale, void* dq, void* dk, void* dv,
+                                  hipStream_t stream);
+
 /* ---- interleaved document chunks -----------------------------------------
  * Arch page §5, "AnchorAttention with Interleaved Chunks" (Figure 5 middle
  * and right): documents are cut into chunks shuffled across a row, every

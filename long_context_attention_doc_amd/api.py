@@ -31,6 +31,7 @@ DKV_TILE = (64, 128)
 EXPORTS = (
     "anchor_attn_strerror", "anchor_attn_version", "anchor_attn_workspace_size",
     "anchor_attn_fwd", "anchor_attn_bwd", "anchor_attn_fwd_ex", "anchor_attn_bwd_ex",
+    "anchor_attn_bwd_noalloc",
     "anchor_attn_chunks_workspace_size", "anchor_attn_fwd_chunks", "anchor_attn_bwd_chunks",
     "anchor_attn_chunk_layout",
     "anchor_attn_position_ids",
@@ -70,6 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "anchor_attn_fwd_ex": (I, [P, P, P, P, I, D, I, I, I, I, I, I, I, F, P, P, P, Z, P]),
         "anchor_attn_bwd_ex": (I, [P, P, P, P, P, P, P, I, D, I, I, I, I, I, I, I, F, P, P, P, P, Z,
                                    P]),
+        "anchor_attn_bwd_noalloc": (I, [P, P, P, P, P, P, P, I, D, I, I, I, I, I, I, I, F, P, P, P,
+                                        P]),
         "anchor_attn_chunks_workspace_size": (Z, [I, I, I, I, I, I, I]),
         "anchor_attn_fwd_chunks": (I, [P, P, P, P, P, I, D, I, I, I, I, I, I, I, F, P, P, P, Z, P]),
         "anchor_attn_bwd_chunks": (I, [P, P, P, P, P, P, P, P, I, D, I, I, I, I, I, I, I, F, P, P, P, P,
@@ -235,6 +238,47 @@ def anchor_attn_bwd(q, k, v, o, lse, dout, cu_doc_lens, rope_base: float, causal
                                    S, Hq, Hkv, D, float(softmax_scale or 0.0), _ptr(dq), _ptr(dk),
                                    _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q.device)),
                "anchor_attn_bwd")
+    return dq, dk, dv
+
+
+# Size of the device array behind anchor_attn_bwd_noalloc (AA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 160 << 20
+
+
+def anchor_attn_bwd_noalloc(q, k, v, o, lse, dout, cu_doc_lens, rope_base: float,
+                            causal: bool = True, softmax_scale: float | None = None,
+                            flags: int = 0, out=None):
+    """The allocation-free backward: as anchor_attn_bwd, with the library's
+    fixed per-device scratch as its workspace.  Shapes whose backward
+    workspace exceeds NOALLOC_SCRATCH_BYTES are refused.  ``out`` may give
+    (dq, dk, dv) to write into; otherwise they are allocated here (the library
+    call itself allocates nothing)."""
+    lib = load()
+    _check_cu(cu_doc_lens, q.shape[0], q.shape[1], flags)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    need = workspace_size(B, S, Hq, Hkv, D, True)
+    if need > NOALLOC_SCRATCH_BYTES:
+        raise ValueError(f"anchor_attn_bwd_noalloc: this shape needs {need} bytes of scratch, more "
+                         f"than the fixed {NOALLOC_SCRATCH_BYTES}")
+    for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _need_bf16(n, t)
+    _need_o(o, flags)
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, S) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B,Hq,S]")
+    cu = _dev_cu(cu_doc_lens, q.device)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    for n, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _need_bf16(n, t)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must have the shape of its input")
+    _check(lib.anchor_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                       _ptr(cu), cu.numel() - 1, float(rope_base), int(bool(causal)),
+                                       int(flags), B, S, Hq, Hkv, D, float(softmax_scale or 0.0),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _stream(q.device)),
+           "anchor_attn_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "anchor_attn.h"
 #include "aa_internal.h"
 
@@ -690,6 +692,60 @@ aa_status anchor_attn_profile_end(double* ms, int32_t* count, int n) {
   delete[] g_prof.id;
   g_prof = Profiler();
   return rc;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward.  Its workspace is `scratch`, a fixed device array
+// of the library's code object: every GPU the library runs on holds its own
+// copy from the module's load until the process ends, and every call on that
+// GPU shares it (the last call's contents stay; the backward clears the one
+// word that must start at zero itself, the device status word).  In host code
+// `scratch` names a host-side stand-in, never the device memory: its device
+// address is looked up once per device, with that device current, and only
+// that address is handed to the kernels.
+static __device__ __align__(256) unsigned char scratch[AA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this device's scratch array (looked up on the first call
+// on the device).
+aa_status scratch_of_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  AA_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return AA_EUNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    AA_HIP(hipStreamGetDevice(stream, &sdev));
+    if (sdev != dev) return AA_EINVAL;   // the stream must belong to the current device
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return AA_EHIP;
+  *out = g_scratch_ptr[dev];
+  return AA_OK;
+}
+}  // namespace
+
+aa_status anchor_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, const int32_t* cu_doc_lens,
+                                  int n_seg, double rope_base, int causal, int flags, int B, int S,
+                                  int Hq, int Hkv, int D, float softmax_scale, void* dq, void* dk,
+                                  void* dv, hipStream_t stream) {
+  if (flags & AA_FLAG_FWD_WORKSPACE) return AA_EINVAL;   // the scratch holds no forward state
+  if (!shape_ok(B, S, Hq, Hkv, D) || (D != 64 && D != 128)) return AA_EINVAL;
+  if (layout(B, S, Hq, Hkv, D, true).total > (size_t)AA_NOALLOC_SCRATCH_BYTES) return AA_EWORKSPACE;
+  void* ws = nullptr;
+  const aa_status s = scratch_of_current_device(stream, &ws);
+  if (s != AA_OK) return s;
+  return bwd_impl(q, k, v, o, lse, dout, cu_doc_lens, n_seg, rope_base, causal, flags, B, S, Hq,
+                  Hkv, D, softmax_scale, dq, dk, dv, ws, (size_t)AA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 aa_status anchor_attn_device_status(const void* workspace, hipStream_t stream, int32_t* out) {

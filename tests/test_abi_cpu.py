@@ -175,3 +175,22 @@ def test_python_binding_guards_the_forward_workspace_and_autograd_cu():
         api.anchor_attention(q, kv, kv, np.asarray([0, 1, 7], dtype=np.int32), 1e4)
     with pytest.raises(ValueError, match="anchor"):
         api.anchor_attention(q, kv, kv, np.asarray([0, 8], dtype=np.int32), 1e4)
+
+
+def test_noalloc_backward_refuses_what_does_not_fit(lib):
+    """The allocation-free backward refuses, before any HIP call, shapes whose
+    workspace exceeds its fixed scratch and the forward-workspace option."""
+    from long_context_attention_doc_amd import api
+    fake = ctypes.c_void_p(256)
+    assert lib.anchor_attn_workspace_size(1, 32768, 32, 32, 128, 1) > api.NOALLOC_SCRATCH_BYTES
+    assert lib.anchor_attn_workspace_size(1, 8192, 32, 32, 128, 1) <= api.NOALLOC_SCRATCH_BYTES
+    rc = lib.anchor_attn_bwd_noalloc(fake, fake, fake, fake, fake, fake, fake, 2, 1e4, 1, 0, 1,
+                                     32768, 32, 32, 128, 0.0, fake, fake, fake, None)
+    assert rc == api.AA_EWORKSPACE
+    rc = lib.anchor_attn_bwd_noalloc(fake, fake, fake, fake, fake, fake, fake, 2, 1e4, 1,
+                                     api.FLAG_FWD_WORKSPACE, 1, 256, 2, 2, 64, 0.0, fake, fake,
+                                     fake, None)
+    assert rc == api.AA_EINVAL
+    rc = lib.anchor_attn_bwd_noalloc(fake, fake, fake, fake, fake, fake, fake, 2, 1e4, 1, 0, 1,
+                                     256, 3, 2, 64, 0.0, fake, fake, fake, None)
+    assert rc == api.AA_EINVAL
