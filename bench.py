@@ -12,7 +12,7 @@ per-kernel instrumentation.  A second pass of as many steps, with HIP events
 recorded by the library around each of its launches on the call's stream,
 gives the per-kernel times: `roofline` reports the dominant kernel's achieved
 rate from them, against the nominal peak and against the peak at the engine
-clock sampled during the timed steps.  `cpu_baseline` times the float64 CPU
+clock sampled while the same steps run on for a few seconds afterwards.  `cpu_baseline` times the float64 CPU
 oracle on a bounded sample of the same workload."""
 from __future__ import annotations
 
@@ -141,34 +141,38 @@ def device_peak() -> dict | None:
 
 
 class ClockSampler:
-    """Engine clock and socket power of GPU 0, polled from the firmware's
-    metrics table (amdsmi Python API) by a background thread while the timed
-    steps run.  It only reads; without amdsmi or a device it records nothing."""
+    """Engine clock and socket power of GPU 0 from the firmware's metrics
+    table (amdsmi Python API), read by a background thread.  The firmware
+    refreshes the table about once a second, so only refreshes stamped after
+    the sampler started count (each one once).  It only reads; without amdsmi
+    or a device it records nothing."""
 
-    def __init__(self, period_s: float = 0.01):
+    def __init__(self, period_s: float = 0.02):
         import threading
         self.period = period_s
-        self.mhz, self.watts = [], []
+        self.samples = []          # (firmware timestamp, mean MHz over the XCDs, socket W)
         self._stop = threading.Event()
         self._thread = None
+        self._t0 = None
         try:
             import amdsmi
             amdsmi.amdsmi_init()
             self._smi = amdsmi
             self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._t0 = self._smi.amdsmi_get_gpu_metrics_info(self._h).get("firmware_timestamp")
         except Exception:   # no amdsmi or no device: no samples
             self._smi = None
 
     def _sample(self):
         m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        ts = m.get("firmware_timestamp")
+        if ts == self._t0 or (self.samples and ts == self.samples[-1][0]):
+            return
         clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 0 < c < 0xFFFF]
-        if not clks and isinstance(m.get("current_gfxclk"), int):
-            clks = [m["current_gfxclk"]]
-        if clks:
-            self.mhz.append(sum(clks) / len(clks))
         pw = m.get("current_socket_power")
-        if isinstance(pw, (int, float)) and 0 < pw < 0xFFFF:
-            self.watts.append(float(pw))
+        if clks:
+            self.samples.append((ts, sum(clks) / len(clks),
+                                 float(pw) if isinstance(pw, (int, float)) and 0 < pw < 0xFFFF else None))
 
     def _run(self):
         while not self._stop.is_set():
@@ -191,14 +195,19 @@ class ClockSampler:
             self._thread.join()
         return False
 
-    def summary(self):
-        if not self.mhz:
+    def summary(self, skip: int = 1):
+        """Mean over the refreshes after the first `skip` (the first one after
+        the start may still describe the ramp)."""
+        use = self.samples[skip:] if len(self.samples) > skip else []
+        if not use:
             return None
-        return {"gfx_mhz_mean": sum(self.mhz) / len(self.mhz), "gfx_mhz_min": min(self.mhz),
-                "gfx_mhz_max": max(self.mhz), "samples": len(self.mhz),
-                "socket_power_w_mean": (sum(self.watts) / len(self.watts)) if self.watts else None,
-                "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), polled every 10 ms "
-                          "during the timed steps"}
+        mhz = [u[1] for u in use]
+        w = [u[2] for u in use if u[2] is not None]
+        return {"gfx_mhz_mean": sum(mhz) / len(mhz), "gfx_mhz_min": min(mhz), "gfx_mhz_max": max(mhz),
+                "refreshes": len(use), "socket_power_w_mean": (sum(w) / len(w)) if w else None,
+                "source": "amdsmi gpu_metrics current_gfxclks (mean over the XCDs) and "
+                          "current_socket_power, firmware refreshes (about 1 s apart) during a pass "
+                          "of the same steps run right after the timed and profiled steps"}
 
 
 def main() -> int:
@@ -213,6 +222,8 @@ def main() -> int:
     ap.add_argument("--no-fwd-workspace", action="store_true",
                     help="self-contained backward: rebuild positions, plan and rotated q, k "
                          "instead of reusing the forward's workspace")
+    ap.add_argument("--clock-s", type=float, default=4.0,
+                    help="seconds of extra steps during which the engine clock is sampled (0: skip)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed")
     ap.add_argument("--no-graph", action="store_true", help=argparse.SUPPRESS)
@@ -294,12 +305,11 @@ def main() -> int:
     # The timed steps: no per-kernel events (the library's profiling is off),
     # only the events around the whole region and between fwd and bwd.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with ClockSampler() as clk:
-        e0.record()
-        for i in range(args.steps):
-            step(marks[i])
-        e1.record()
-        torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(marks[i])
+    e1.record()
+    torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     bwd_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / args.steps
     fwd_ms = ms - bwd_ms
@@ -317,6 +327,16 @@ def main() -> int:
     torch.cuda.synchronize()
     prof = api.profile_end()
     profiled_ms = p0.elapsed_time(p1) / args.steps
+    # The engine clock under this load: the firmware's metrics refresh about
+    # once a second, so the same steps run on for a few refreshes.
+    clk = ClockSampler()
+    if args.clock_s > 0 and clk._smi is not None:
+        t_end = time.perf_counter() + args.clock_s
+        with clk:
+            while time.perf_counter() < t_end:
+                for _ in range(5):
+                    step()
+                torch.cuda.synchronize()
 
     # The same step captured once in a HIP graph and replayed: the kernels and
     # their work are identical, the host launch gaps between them are gone.

@@ -422,7 +422,12 @@ __device__ __forceinline__ void wait_all_but_tiles(int tiles) {
 #ifndef AA_FWD_STAGES
 #define AA_FWD_STAGES 2
 #endif
-constexpr int kFwdBM = 128, kFwdBN = AA_FWD_BN;   // forward and dQ: query tile x key tile
+#ifndef AA_FWD_BM
+#define AA_FWD_BM 128
+#endif
+constexpr int kFwdBM = AA_FWD_BM, kFwdBN = AA_FWD_BN;   // forward and dQ: query tile x key tile
+constexpr int kFwdThreads = 2 * kFwdBM;                  // one wave per 32 queries
+constexpr int kFwdBlocksPerCU = 512 / kFwdThreads;       // two waves per SIMD
 constexpr int kFwdStages = AA_FWD_STAGES;         // K/V tiles in LDS (prefetch depth + 1)
 constexpr int kDkvBM = 64, kDkvBN = 128;          // dK/dV: query tile x key tile
 

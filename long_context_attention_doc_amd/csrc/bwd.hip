@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
 // and dP^T = V dO^T, transposing reads feed K^T in dQ^T = K^T dS^T.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_bwd_dq(
+__global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_bwd_dq(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dvec,
     const float* __restrict__ ds0, const float* __restrict__ table,
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
   const size_t kv_row_stride = (size_t)Hkv * D;
   const bf16* kbase = kr + tok0 * kv_row_stride + hkv * D;
   const bf16* vbase = v + tok0 * kv_row_stride + hkv * D;
-  DirectTile<D, BN, 256> dl;
+  DirectTile<D, BN, kFwdThreads> dl;
   dl.init(kv_row_stride);
   auto issue = [&](int buf, int kt) {
     dl.load(buf ? Ks1 : Ks0, kbase, kv_row_stride, kt * BN, S - 1);
@@ -602,12 +602,12 @@ hipError_t launch_bwd_dq(const BwdArgs& a, const PlanBufs& pq, hipStream_t st) {
   const int n_items = a.B * pq.nq * a.Hq;
   const dim3 grid(padded_grid(n_items));
   if (a.D == 128)
-    hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
+    hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(kFwdThreads), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
                        pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.tok_map,
                        a.dq);
   else
-    hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
+    hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(kFwdThreads), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
                        pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.tok_map,
                        a.dq);

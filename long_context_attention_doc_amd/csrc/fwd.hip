@@ -44,7 +44,7 @@
 namespace aa {
 
 template <int D, bool ROTATE_Q>
-__global__ __launch_bounds__(256, 2) void k_fwd(
+__global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_fwd(
     const bf16* __restrict__ q_raw, const float* __restrict__ table, const int32_t* __restrict__ pos,
     int npos, bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ v,
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(
   const size_t kv_row_stride = (size_t)Hkv * D;
   const bf16* kbase = kr + tok0 * kv_row_stride + hkv * D;
   const bf16* vbase = v + tok0 * kv_row_stride + hkv * D;
-  DirectTile<D, BN, 256> dl;
+  DirectTile<D, BN, kFwdThreads> dl;
   dl.init(kv_row_stride);
   auto issue = [&](int buf, int kt) {
     dl.load(buf ? Ks1 : Ks0, kbase, kv_row_stride, kt * BN, S - 1);
@@ -306,7 +306,7 @@ hipError_t launch_fwd(const bf16* q_raw, const float* table, int npos, bf16* qr,
   const int n_items = B * pb.nq * Hq;
   const dim3 grid(padded_grid(n_items));
 #define AA_LAUNCH_FWD(DD, RQ)                                                                    \
-  hipLaunchKernelGGL((k_fwd<DD, RQ>), grid, dim3(256), 0, st, q_raw, table, tt.pos, npos, qr, kr, \
+  hipLaunchKernelGGL((k_fwd<DD, RQ>), grid, dim3(kFwdThreads), 0, st, q_raw, table, tt.pos, npos, qr, kr, \
                      v, tt.lo, tt.hi, pb.qptr, pb.kpack, pb.order, status, S, Hq, Hkv, pb.nq,     \
                      n_items, scale_log2, anchor, o, o_f32, lse, tok_map)
   if (D == 128) {
