@@ -96,12 +96,14 @@ enum {
  *       anchor_attn_fwd_ex left in it for the same q, k, cu_doc_lens,
  *       rope_base, causal, other flags and shape: it was sized for the
  *       backward (anchor_attn_workspace_size(..., for_bwd = 1)) and given to
- *       the forward, and nothing wrote to it in between.  The backward then
- *       reuses the forward's position IDs, query-major plan, RoPE table and
- *       rotated q, k instead of rebuilding them (the forward's workspace
- *       layout is a prefix of the backward's).  anchor_attn_fwd_ex ignores
- *       it; the other entry points reject it.  If the promise does not hold
- *       the results are wrong; nothing detects it. */
+ *       the forward, and nothing wrote to it in between.  (A forward given a
+ *       workspace of that size also builds the backward's key-major tile plan,
+ *       in the same pass as its own.)  The backward then reuses the forward's
+ *       position IDs, both tile plans, RoPE table and rotated q, k instead of
+ *       rebuilding them (the forward's workspace layout is a prefix of the
+ *       backward's).  anchor_attn_fwd_ex ignores it; the other entry points
+ *       reject it.  If the promise does not hold the results are wrong;
+ *       nothing detects it. */
 #define AA_FLAG_FWD_WORKSPACE 4
 /*   AA_FLAG_O_FP32  (anchor_attn_fwd_ex, anchor_attn_bwd_ex,
  *       anchor_attn_fwd_chunks, anchor_attn_bwd_chunks) O is float32

@@ -74,9 +74,27 @@ struct PlanBufs {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_positions(const int32_t* cu, int n_seg, int B, int S, int causal, int mode,
                             int anchor, TokenTables tt, int32_t* status, hipStream_t st);
-hipError_t launch_plan(const int32_t* lo, const int32_t* hi, int B, int S, int anchor, PlanBufs pb,
-                       bool key_major, hipStream_t st);
-hipError_t launch_rope_table(int S, int D, const RopeTheta& th, float* table, hipStream_t st);
+// Where a plan build gets its token tables: with cu (device cu_doc_lens) it
+// computes them into tt (position IDs, key intervals) and checks the segment
+// layout into status; with cu null it reads tt.
+struct PlanSrc {
+  const int32_t* cu;
+  int n_seg, causal, mode;
+  TokenTables tt;
+  int32_t* status;
+};
+// Tile plans in one pass over the rows: a query-major plan pq (kinds,
+// qptr/kidx/kkind/kpack, n_live, and the work order when pq->order is set)
+// and/or a key-major plan pk (kinds_t, kptr/qidx/qkind/qpack; pk->cntk must
+// be zero beforehand; n_live when pq is null).  Either may be null.
+hipError_t launch_plans(const PlanSrc& src, int B, int S, int anchor, const PlanBufs* pq,
+                        const PlanBufs* pk, hipStream_t st);
+// Clears *status (when not null) and n int32 values at p.
+hipError_t launch_clear(int32_t* status, int32_t* p, int n, hipStream_t st);
+// The RoPE table.  It runs first in every attention call, so it also clears
+// *status and the n_zero int32 values at zero (when not null).
+hipError_t launch_rope_table(int S, int D, const RopeTheta& th, float* table, int32_t* status,
+                             int32_t* zero, int n_zero, hipStream_t st);
 hipError_t launch_chunk_layout(const int32_t* cu, const int32_t* chunk_doc, int n_chunks, int B,
                                int S, int causal, int mode, int anchor, ChunkBufs cb,
                                TokenTables tt, int32_t* status, hipStream_t st);

@@ -192,11 +192,6 @@ thread_local Profiler g_prof;
     }                                                                             \
   } while (0)
 
-hipError_t launch_zero_status(int32_t* status, hipStream_t st) {
-  hipLaunchKernelGGL(k_zero_status, dim3(1), dim3(64), 0, st, status);
-  return hipGetLastError();
-}
-
 // Positions, plan(s), RoPE table, rotated q and k: the prologue shared by
 // the forward and the backward.
 aa_status prologue(const Layout& L, char* ws, const void* q, const void* k,
@@ -206,19 +201,19 @@ aa_status prologue(const Layout& L, char* ws, const void* q, const void* k,
   TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
   const int mode = (flags & AA_FLAG_CONTINUOUS_POS) ? 1 : 0;
   const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
-  AA_LAUNCH(AA_K_STATUS, st, launch_zero_status(status, st));
-  AA_LAUNCH(AA_K_POSITIONS, st,
-            launch_positions(cu, n_seg, B, S, causal, mode, anchor, tt, status, st));
-  AA_LAUNCH(AA_K_PLAN, st,
-            launch_plan(tt.lo, tt.hi, B, S, anchor, plan_bufs(L.pq, ws), false, st));
-  if (bwd)
-    AA_LAUNCH(AA_K_PLAN, st,
-              launch_plan(tt.lo, tt.hi, B, S, anchor, plan_bufs(L.pk, ws), true, st));
   float* table = (float*)(ws + L.table);
+  PlanBufs pq = plan_bufs(L.pq, ws), pk = plan_bufs(L.pk, ws);
   // Position IDs reach S when a document without an anchor fills a row under
-  // reset IDs (its tokens count 1 .. S), so the table has S + 1 rows.
+  // reset IDs (its tokens count 1 .. S), so the table has S + 1 rows.  The
+  // table kernel runs first: it also clears the status word and the
+  // key-major plan's counters.
   AA_LAUNCH(AA_K_ROPE_TABLE, st,
-            launch_rope_table(S + 1, D, make_theta(D, rope_base), table, st));
+            launch_rope_table(S + 1, D, make_theta(D, rope_base), table, status,
+                              bwd ? pk.cntk : nullptr, B * pk.nk, st));
+  // token tables and both plans (the key-major one when the workspace holds
+  // the backward's layout) in one pass
+  const PlanSrc src{cu, n_seg, causal, mode, tt, status};
+  AA_LAUNCH(AA_K_PLAN, st, launch_plans(src, B, S, anchor, &pq, bwd ? &pk : nullptr, st));
   if (rotate_q)
     AA_LAUNCH(AA_K_ROPE, st,
               launch_rope_apply((const bf16*)q, nullptr, tt.pos, table, S + 1, B, S, Hq, D,
@@ -242,18 +237,17 @@ aa_status prologue_chunks(const Layout& L, const ChunkLayout& C, char* ws, const
   const int mode = (flags & AA_FLAG_CONTINUOUS_POS) ? 1 : 0;
   const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   const ChunkBufs cb = chunk_bufs(C, ws);
-  AA_LAUNCH(AA_K_STATUS, st, launch_zero_status(status, st));
+  float* table = (float*)(ws + L.table);
+  PlanBufs pq = plan_bufs(L.pq, ws), pk = plan_bufs(L.pk, ws);
+  AA_LAUNCH(AA_K_ROPE_TABLE, st,
+            launch_rope_table(S + 1, D, make_theta(D, rope_base), table, status,
+                              bwd ? pk.cntk : nullptr, B * pk.nk, st));
   AA_LAUNCH(AA_K_CHUNKS, st,
             launch_chunk_layout(cu, chunk_doc, n_chunks, B, S, causal, mode, anchor, cb, tt,
                                 status, st));
-  AA_LAUNCH(AA_K_PLAN, st,
-            launch_plan(tt.lo, tt.hi, B, S, anchor, plan_bufs(L.pq, ws), false, st));
-  if (bwd)
-    AA_LAUNCH(AA_K_PLAN, st,
-              launch_plan(tt.lo, tt.hi, B, S, anchor, plan_bufs(L.pk, ws), true, st));
-  float* table = (float*)(ws + L.table);
-  AA_LAUNCH(AA_K_ROPE_TABLE, st,
-            launch_rope_table(S + 1, D, make_theta(D, rope_base), table, st));
+  // the plans from the permuted token tables the layout kernel wrote
+  const PlanSrc src{nullptr, 0, causal, mode, tt, status};
+  AA_LAUNCH(AA_K_PLAN, st, launch_plans(src, B, S, anchor, &pq, bwd ? &pk : nullptr, st));
   AA_LAUNCH(AA_K_ROPE, st,
             launch_rope_apply((const bf16*)q, cb.src, tt.pos, table, S + 1, B, S, Hq, D,
                               (bf16*)(ws + L.qrot), st));
@@ -308,14 +302,20 @@ static aa_status fwd_impl(const void* q, const void* k, const void* v, const int
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(lse, 4) || !aligned(cu_doc_lens, 4) || !aligned(workspace, kAlign))
     return AA_EINVAL;
-  const Layout L = layout(B, S, Hq, Hkv, D, false);
-  if (ws_bytes < L.total) return AA_EWORKSPACE;
+  const Layout Lf = layout(B, S, Hq, Hkv, D, false);
+  if (ws_bytes < Lf.total) return AA_EWORKSPACE;
+  // A workspace that holds the backward's layout (of which the forward's is
+  // a prefix) also gets the backward's key-major plan, built in the same pass
+  // as the forward's plan, for a backward with AA_FLAG_FWD_WORKSPACE.
+  const Layout Lb = layout(B, S, Hq, Hkv, D, true);
+  const bool with_bwd_plan = ws_bytes >= Lb.total;
+  const Layout& L = with_bwd_plan ? Lb : Lf;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)D);
   char* ws = (char*)workspace;
   // the forward rotates Q as it loads it (and leaves the rotated q in the
   // workspace for the backward); the RoPE pass rotates K only
   aa_status s = prologue(L, ws, q, k, cu_doc_lens, n_seg, rope_base, causal, flags, B, S, Hq,
-                         Hkv, D, false, stream, /*rotate_q=*/false);
+                         Hkv, D, with_bwd_plan, stream, /*rotate_q=*/false);
   if (s != AA_OK) return s;
   TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
   const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
@@ -347,13 +347,9 @@ static aa_status bwd_impl(const void* q, const void* k, const void* v, const voi
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)D);
   char* ws = (char*)workspace;
   if (flags & AA_FLAG_FWD_WORKSPACE) {
-    // the forward's status word, token tables, query-major plan, RoPE table
-    // and rotated q, k are still in place (the forward's layout is a prefix of
-    // this one); only the key-major plan is new
-    const TokenTables tt{(int32_t*)(ws + L.pos), (int32_t*)(ws + L.lo), (int32_t*)(ws + L.hi)};
-    const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
-    AA_LAUNCH(AA_K_PLAN, stream,
-              launch_plan(tt.lo, tt.hi, B, S, anchor, plan_bufs(L.pk, ws), true, stream));
+    // the forward's status word, token tables, both plans, RoPE table and
+    // rotated q, k are still in place (the forward built the key-major plan
+    // too, the workspace holding the backward's layout): nothing to rebuild
   } else {
     aa_status s = prologue(L, ws, q, k, cu_doc_lens, n_seg, rope_base, causal, flags, B, S, Hq,
                            Hkv, D, true, stream);
@@ -616,11 +612,11 @@ aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, in
   pb.qptr = qptr; pb.kidx = kidx; pb.kkind = kkind;
   pb.kptr = kptr; pb.qidx = qidx; pb.qkind = qkind; pb.n_live = n_live;
   pb.kpack = nullptr; pb.qpack = nullptr; pb.order = nullptr;
-  hipLaunchKernelGGL(k_zero_status, dim3(1), dim3(64), 0, stream, status);
-  AA_HIP(hipGetLastError());
   const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
-  AA_HIP(launch_positions(cu_doc_lens, n_seg, B, S, causal, 0, anchor, tt, status, stream));
-  AA_HIP(launch_plan(tt.lo, tt.hi, B, S, anchor, pb, true, stream));
+  // the same one-pass build as the attention calls, both layouts of one plan
+  AA_HIP(launch_clear(status, pb.cntk, B * pb.nk, stream));
+  const PlanSrc src{cu_doc_lens, n_seg, causal, 0, tt, status};
+  AA_HIP(launch_plans(src, B, S, anchor, &pb, &pb, stream));
   return AA_OK;
 }
 
@@ -642,7 +638,7 @@ aa_status anchor_attn_rope(const void* x, const int32_t* pos, int B, int S, int 
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
   if (!aligned(x, 16) || !aligned(x_rot, 16) || !aligned(table, 16) || !aligned(pos, 4))
     return AA_EINVAL;
-  AA_HIP(launch_rope_table(S, D, make_theta(D, rope_base), table, stream));
+  AA_HIP(launch_rope_table(S, D, make_theta(D, rope_base), table, nullptr, nullptr, 0, stream));
   AA_HIP(launch_rope_apply((const bf16*)x, nullptr, pos, table, S, B, S, H, D, (bf16*)x_rot, stream));
   return AA_OK;
 }

@@ -21,25 +21,15 @@
 
 namespace aa {
 
-// One thread per token: segment lookup by binary search over cu_doc_lens,
-// position ID, visible-key interval, and validation of the segment layout.
-// Every derived index is clamped into the row so that later kernels stay in
-// bounds even when cu_doc_lens is invalid (the status word reports it).
-// mode 0: reset (a document's first token gets 1); 1: continuous (row-local
-// index).  anchor 0: no anchor, every token belongs to a document.
-__global__ void k_positions(const int32_t* __restrict__ cu, int n_seg, int B, int S, int causal,
-                            int mode, int anchor, int32_t* __restrict__ pos,
-                            int32_t* __restrict__ lo, int32_t* __restrict__ hi,
-                            int32_t* __restrict__ status) {
-  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)B * S;
-  if (t < n_seg) {
-    if (cu[t] >= cu[t + 1]) status[0] = kStatusBadDocs;
-  }
-  if (t == 0) {
-    if (cu[0] != 0 || (long long)cu[n_seg] != total) status[0] = kStatusBadDocs;
-  }
-  if (t >= total) return;
+// Token t's segment (binary search over cu_doc_lens), position ID and the
+// closed interval [lo, hi] of keys it sees besides the anchor; *bad is set
+// when the segment layout around t is invalid.  Every derived index is
+// clamped into the row so that later kernels stay in bounds even then (the
+// status word reports it).  mode 0: reset (a document's first token gets 1);
+// 1: continuous (row-local index).  anchor 0: every token is a document token.
+__device__ __forceinline__ void token_tables(long long t, const int32_t* __restrict__ cu, int n_seg,
+                                             int S, int causal, int mode, int anchor, int& p,
+                                             int& l, int& h, bool& bad) {
   int a = 0, bnd = n_seg - 1;             // largest k with cu[k] <= t
   while (a < bnd) {
     const int mid = (a + bnd + 1) >> 1;
@@ -47,15 +37,13 @@ __global__ void k_positions(const int32_t* __restrict__ cu, int n_seg, int B, in
   }
   const long long s = cu[a], e = cu[a + 1];
   const long long rs = (t / S) * (long long)S;
-  bool bad = !(s <= t && t < e && s >= rs && e <= rs + S);
+  bad = !(s <= t && t < e && s >= rs && e <= rs + S);
   if (anchor) {
     if (t == rs && e != rs + 1) bad = true;        // the anchor is a segment of its own
     if (t == rs + 1 && s != t) bad = true;         // so the next segment starts right after it
   }
-  if (bad) status[0] = kStatusBadDocs;
   const int local = (int)(t - rs);
   const int first = anchor ? 1 : 0;                // first row-local index of a document
-  int p, l, h;
   if (anchor && t == rs) {
     p = 0; l = 1; h = 0;                           // anchor: sees only itself (column 0)
   } else {
@@ -66,85 +54,158 @@ __global__ void k_positions(const int32_t* __restrict__ cu, int n_seg, int B, in
     l = (int)sl;
     h = causal ? local : (int)(el - 1);
   }
+}
+
+// The global checks of cu_doc_lens, spread over the threads of a launch:
+// strictly increasing, from 0 to B*S.
+__device__ __forceinline__ void check_offsets(long long g, const int32_t* __restrict__ cu, int n_seg,
+                                              long long total, int32_t* __restrict__ status) {
+  if (g < n_seg && cu[g] >= cu[g + 1]) status[0] = kStatusBadDocs;
+  if (g == 0 && (cu[0] != 0 || (long long)cu[n_seg] != total)) status[0] = kStatusBadDocs;
+}
+
+// One thread per token: the token tables and the layout checks.
+__global__ void k_positions(const int32_t* __restrict__ cu, int n_seg, int B, int S, int causal,
+                            int mode, int anchor, int32_t* __restrict__ pos,
+                            int32_t* __restrict__ lo, int32_t* __restrict__ hi,
+                            int32_t* __restrict__ status) {
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)B * S;
+  check_offsets(t, cu, n_seg, total, status);
+  if (t >= total) return;
+  int p, l, h;
+  bool bad;
+  token_tables(t, cu, n_seg, S, causal, mode, anchor, p, l, h, bad);
+  if (bad) status[0] = kStatusBadDocs;
   pos[t] = p;
   lo[t] = l;
   hi[t] = h;
 }
 
-// One workgroup per (row b, query tile qt): classify every key tile.
-// A tile is live when some query row of it sees some key of it (the anchor
-// column 0 is seen by every query); FULL when all BM x BN elements exist and
-// are seen; ANCHOR when it is key tile 0 and only column 0 is seen; PARTIAL
-// otherwise.  Also counts the live tiles of the query tile.
-__global__ void k_tile_kinds(const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
-                             int S, int BM, int BN, int nq, int nk, int anchor,
-                             uint8_t* __restrict__ kinds, int32_t* __restrict__ cntq) {
+// Kind of the tile of query rows [r, r + nrows) (their intervals in slo/shi)
+// and key tile kt of BN keys: live when some query row sees some key of it
+// (the anchor column 0 is seen by every query); FULL when all BM x BN
+// elements exist and are seen; ANCHOR when it is key tile 0 and only column
+// 0 is seen; PARTIAL otherwise; 0 when dead.
+__device__ __forceinline__ uint8_t tile_kind(const int* slo, const int* shi, int r, int nrows,
+                                             int BM, int kt, int BN, int S, int anchor) {
+  const int c0 = kt * BN;
+  const int c1 = min(S, c0 + BN) - 1;
+  const bool cols_exist = (c0 + BN) <= S;
+  bool any_live = false, any_doc = false, all_full = nrows == BM && cols_exist;
+  for (int i = r; i < r + nrows; ++i) {
+    const int a = max(slo[i], c0), z = min(shi[i], c1);
+    const int ndoc = z >= a ? z - a + 1 : 0;
+    const int n = ndoc + (anchor && kt == 0 ? 1 : 0);
+    any_live |= n > 0;
+    any_doc |= ndoc > 0;
+    all_full &= n == BN;
+  }
+  if (!any_live) return 0;
+  return all_full ? kTileFull : ((anchor && kt == 0 && !any_doc) ? kTileAnchor : kTilePartial);
+}
+
+// One workgroup per (row b, block of RB rows): with cu given, the token
+// tables of its rows (and its share of the layout checks); otherwise it reads
+// them.  Then the kinds of every tile whose query tile lies in its rows, for
+// up to two plans: a query-major one (dense kinds row and live count of each
+// of its query tiles) and a key-major one (dense key-major kinds, live counts
+// of the key tiles added atomically to cntk, which must start at zero).
+// RB is a multiple of each plan's BM and at most 256.
+struct KindsOut {
+  int BM, BN, nq, nk;
+  uint8_t* kinds;      // [B][nq][nk] (query-major) or [B][nk][nq] (key-major)
+  int32_t* cnt;        // [B*nq] (query-major) or [B*nk] (key-major)
+  int key_major;
+};
+
+__global__ __launch_bounds__(256) void k_plan_kinds(
+    const int32_t* __restrict__ cu, int n_seg, int B, int S, int causal, int mode, int anchor,
+    int32_t* __restrict__ pos, int32_t* __restrict__ lo, int32_t* __restrict__ hi,
+    int32_t* __restrict__ status, int RB, int nrb, KindsOut p0, KindsOut p1) {
   __shared__ int slo[256], shi[256];
-  __shared__ int wcount[8];
-  const int tile = blockIdx.x;            // b * nq + qt
-  const int b = tile / nq, qt = tile % nq;
-  const int r0 = qt * BM;
-  const int nrows = min(BM, S - r0);
-  for (int r = threadIdx.x; r < BM; r += blockDim.x) {
-    if (r < nrows) {
-      const size_t t = (size_t)b * S + r0 + r;
-      slo[r] = lo[t];
-      shi[r] = hi[t];
+  __shared__ int wcount[4];
+  const int b = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+  const int r0 = rb * RB;
+  const int nrows = min(RB, S - r0);
+  const size_t tok0 = (size_t)b * S + r0;
+  if (cu) {
+    check_offsets((long long)blockIdx.x * blockDim.x + threadIdx.x, cu, n_seg, (long long)B * S,
+                  status);
+    for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
+      int p, l, h;
+      bool bad;
+      token_tables((long long)(tok0 + r), cu, n_seg, S, causal, mode, anchor, p, l, h, bad);
+      if (bad) status[0] = kStatusBadDocs;
+      pos[tok0 + r] = p;
+      lo[tok0 + r] = l;
+      hi[tok0 + r] = h;
+      slo[r] = l;
+      shi[r] = h;
+    }
+  } else {
+    for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
+      slo[r] = lo[tok0 + r];
+      shi[r] = hi[tok0 + r];
     }
   }
   __syncthreads();
-  int cnt = 0;
-  for (int kt = threadIdx.x; kt < nk; kt += blockDim.x) {
-    const int c0 = kt * BN;
-    const int c1 = min(S, c0 + BN) - 1;
-    const bool cols_exist = (c0 + BN) <= S;
-    bool any_live = false, any_doc = false, all_full = nrows == BM && cols_exist;
-    for (int r = 0; r < nrows; ++r) {
-      const int a = max(slo[r], c0), z = min(shi[r], c1);
-      const int ndoc = z >= a ? z - a + 1 : 0;
-      const int n = ndoc + (anchor && kt == 0 ? 1 : 0);
-      any_live |= n > 0;
-      any_doc |= ndoc > 0;
-      all_full &= n == BN;
+  for (int pl = 0; pl < 2; ++pl) {
+    const KindsOut& P = pl ? p1 : p0;
+    if (!P.kinds) continue;
+    for (int sub = 0; sub < RB / P.BM; ++sub) {
+      const int qt = r0 / P.BM + sub;
+      if (qt >= P.nq) break;                      // uniform
+      const int rr = sub * P.BM;
+      const int n = min(P.BM, nrows - rr);
+      int cnt = 0;
+      for (int kt = threadIdx.x; kt < P.nk; kt += blockDim.x) {
+        const uint8_t kind = tile_kind(slo, shi, rr, n, P.BM, kt, P.BN, S, anchor);
+        if (P.key_major) {
+          P.kinds[((size_t)b * P.nk + kt) * P.nq + qt] = kind;
+          if (kind) atomicAdd(P.cnt + (size_t)b * P.nk + kt, 1);
+        } else {
+          P.kinds[((size_t)b * P.nq + qt) * P.nk + kt] = kind;
+          cnt += kind != 0;
+        }
+      }
+      if (!P.key_major) {
+        for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+        if ((threadIdx.x & 63) == 0) wcount[threadIdx.x >> 6] = cnt;
+        __syncthreads();
+        if (threadIdx.x == 0) P.cnt[(size_t)b * P.nq + qt] = wcount[0] + wcount[1] + wcount[2] + wcount[3];
+        __syncthreads();
+      }
     }
-    uint8_t kind = 0;
-    if (any_live)
-      kind = all_full ? kTileFull : ((anchor && kt == 0 && !any_doc) ? kTileAnchor : kTilePartial);
-    kinds[(size_t)tile * nk + kt] = kind;
-    cnt += kind != 0;
-  }
-  // block reduction of the live count
-  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
-  if ((threadIdx.x & 63) == 0) wcount[threadIdx.x >> 6] = cnt;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int tot = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += wcount[w];
-    cntq[tile] = tot;
   }
 }
 
-// Single-workgroup exclusive scan: ptr[i] = sum(cnt[0..i)), ptr[n] = total.
-__global__ void k_scan(const int32_t* __restrict__ cnt, int n, int32_t* __restrict__ ptr,
-                       int32_t* __restrict__ total_out) {
-  __shared__ int buf[1024];
-  __shared__ int carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < n; base += 1024) {
+// Clears the status word (when given) and n int32 counters.
+__global__ void k_clear(int32_t* __restrict__ status, int32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0 && status) status[0] = kStatusOk;
+  if (i < n) p[i] = 0;
+}
+
+// Exclusive scan by one workgroup of NT threads: ptr[i] = sum(cnt[0..i)),
+// ptr[n] = total (also to *total_out when not null).  buf: NT ints of LDS.
+template <int NT>
+__device__ void block_scan(const int32_t* __restrict__ cnt, int n, int32_t* __restrict__ ptr,
+                           int32_t* __restrict__ total_out, int* buf) {
+  int carry = 0;
+  for (int base = 0; base < n; base += NT) {
     const int i = base + threadIdx.x;
     const int x = i < n ? cnt[i] : 0;
     buf[threadIdx.x] = x;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
+    for (int off = 1; off < NT; off <<= 1) {
       const int y = (int)threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
       __syncthreads();
       buf[threadIdx.x] += y;
       __syncthreads();
     }
     if (i < n) ptr[i] = carry + buf[threadIdx.x] - x;
-    __syncthreads();
-    if (threadIdx.x == 1023) carry += buf[1023];
+    carry += buf[NT - 1];
     __syncthreads();
   }
   if (threadIdx.x == 0) {
@@ -153,39 +214,12 @@ __global__ void k_scan(const int32_t* __restrict__ cnt, int n, int32_t* __restri
   }
 }
 
-// Transposed copy of the kind matrix: kinds_t[b][kt][qt] = kinds[b][qt][kt],
-// 64 x 64 blocks through LDS.
-__global__ void k_transpose_kinds(const uint8_t* __restrict__ kinds, int nq, int nk,
-                                  uint8_t* __restrict__ kinds_t) {
-  __shared__ uint8_t blk[64][65];
-  const int b = blockIdx.z;
-  const int q0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
-  const uint8_t* src = kinds + (size_t)b * nq * nk;
-  uint8_t* dst = kinds_t + (size_t)b * nq * nk;
-  for (int i = threadIdx.y; i < 64; i += blockDim.y) {
-    const int q = q0 + i, k = k0 + threadIdx.x;
-    blk[i][threadIdx.x] = (q < nq && k < nk) ? src[(size_t)q * nk + k] : 0;
-  }
-  __syncthreads();
-  for (int i = threadIdx.y; i < 64; i += blockDim.y) {
-    const int k = k0 + i, q = q0 + threadIdx.x;
-    if (k < nk && q < nq) dst[(size_t)k * nq + q] = blk[threadIdx.x][i];
-  }
-}
-
-// One wave per row of a dense [rows][n] kind matrix: number of live entries.
-__global__ void k_row_count(const uint8_t* __restrict__ m, int rows, int n,
-                            int32_t* __restrict__ cnt) {
-  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const uint8_t* r = m + (size_t)row * n;
-  int c = 0;
-  for (int i0 = 0; i0 < n; i0 += 64) {
-    const int i = i0 + lane;
-    c += __popcll(__builtin_amdgcn_ballot_w64(i < n && r[i] != 0));
-  }
-  if (lane == 0) cnt[row] = c;
+// Single-workgroup exclusive scan.
+__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ cnt, int n,
+                                               int32_t* __restrict__ ptr,
+                                               int32_t* __restrict__ total_out) {
+  __shared__ int buf[1024];
+  block_scan<1024>(cnt, n, ptr, total_out, buf);
 }
 
 // One wave per row: the live entries of the row, ascending, at ptr[row].
@@ -216,11 +250,20 @@ __global__ void k_row_compact(const uint8_t* __restrict__ m, int rows, int n,
 // LDS and derives the same flags; thread i writes tile i at its rank, the
 // number of tiles that go before it.  Plans with more than kMaxLptTiles tiles
 // keep the natural order, head after head.
+// With ptr not null, the workgroup after the last one needed for the order
+// also writes the plan's exclusive scan of the counts (ptr, *total_out), so a
+// query-major plan needs no separate scan launch.
 constexpr int kMaxLptTiles = 16384;
 __global__ __launch_bounds__(256) void k_tile_order(const int32_t* __restrict__ cnt, int n,
-                                                   int32_t* __restrict__ order) {
+                                                   int32_t* __restrict__ order,
+                                                   int32_t* __restrict__ ptr,
+                                                   int32_t* __restrict__ total_out) {
   __shared__ int w[kMaxLptTiles];
   __shared__ int wmax[4], wsum[4];
+  if (ptr && blockIdx.x == gridDim.x - 1) {
+    block_scan<256>(cnt, n, ptr, total_out, w);
+    return;
+  }
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (n > kMaxLptTiles) {
     if (i < n) order[i] = i;
@@ -264,7 +307,7 @@ __global__ __launch_bounds__(256) void k_tile_order(const int32_t* __restrict__ 
 
 hipError_t launch_tile_order(const int32_t* cnt, int n, int32_t* order, hipStream_t st) {
   hipLaunchKernelGGL(k_tile_order, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cnt, n,
-                     order);
+                     order, (int32_t*)nullptr, (int32_t*)nullptr);
   return hipGetLastError();
 }
 
@@ -279,26 +322,50 @@ hipError_t launch_positions(const int32_t* cu, int n_seg, int B, int S, int caus
   return hipGetLastError();
 }
 
-hipError_t launch_plan(const int32_t* lo, const int32_t* hi, int B, int S, int anchor, PlanBufs pb,
-                       bool key_major, hipStream_t st) {
-  const int nq = pb.nq, nk = pb.nk;
-  hipLaunchKernelGGL(k_tile_kinds, dim3(B * nq), dim3(256), 0, st, lo, hi, S, pb.BM, pb.BN, nq,
-                     nk, anchor, pb.kinds, pb.cntq);
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pb.cntq, B * nq, pb.qptr, pb.n_live);
-  hipLaunchKernelGGL(k_row_compact, dim3((B * nq + 3) / 4), dim3(256), 0, st, pb.kinds, B * nq, nk,
-                     pb.qptr, pb.kidx, pb.kkind, pb.kpack);
-  if (pb.order && !key_major)   // the key-major launches read the query-major plan's flags
-    hipLaunchKernelGGL(k_tile_order, dim3((B * nq + 255) / 256), dim3(256), 0, st, pb.cntq, B * nq,
-                       pb.order);
-  if (key_major) {
-    hipLaunchKernelGGL(k_transpose_kinds, dim3((nk + 63) / 64, (nq + 63) / 64, B), dim3(64, 4), 0,
-                       st, pb.kinds, nq, nk, pb.kinds_t);
-    hipLaunchKernelGGL(k_row_count, dim3((B * nk + 3) / 4), dim3(256), 0, st, pb.kinds_t, B * nk,
-                       nq, pb.cntk);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pb.cntk, B * nk, pb.kptr,
-                       (int32_t*)nullptr);
-    hipLaunchKernelGGL(k_row_compact, dim3((B * nk + 3) / 4), dim3(256), 0, st, pb.kinds_t, B * nk,
-                       nq, pb.kptr, pb.qidx, pb.qkind, pb.qpack);
+hipError_t launch_clear(int32_t* status, int32_t* p, int n, hipStream_t st) {
+  const int blocks = n > 0 ? (n + 255) / 256 : 1;
+  hipLaunchKernelGGL(k_clear, dim3(blocks), dim3(256), 0, st, status, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_plans(const PlanSrc& src, int B, int S, int anchor, const PlanBufs* pq,
+                        const PlanBufs* pk, hipStream_t st) {
+  KindsOut o[2] = {};
+  int RB = 0;
+  if (pq) {
+    o[0] = KindsOut{pq->BM, pq->BN, pq->nq, pq->nk, pq->kinds, pq->cntq, 0};
+    RB = pq->BM;
+  }
+  if (pk) {
+    o[1] = KindsOut{pk->BM, pk->BN, pk->nq, pk->nk, pk->kinds_t, pk->cntk, 1};
+    RB = RB > pk->BM ? RB : pk->BM;
+  }
+  if (RB == 0 || RB > 256 || (pq && RB % pq->BM) || (pk && RB % pk->BM))
+    return hipErrorInvalidValue;
+  const int nrb = (S + RB - 1) / RB;
+  // the launch must cover the n_seg offsets it checks (RB <= 256 threads per
+  // RB rows, and n_seg <= B*S)
+  hipLaunchKernelGGL(k_plan_kinds, dim3(B * nrb), dim3(256), 0, st, src.cu, src.n_seg, B, S,
+                     src.causal, src.mode, anchor, src.tt.pos, src.tt.lo, src.tt.hi, src.status, RB,
+                     nrb, o[0], o[1]);
+  if (pq) {
+    const int n = B * pq->nq;
+    if (pq->order) {
+      // work order and scan in one launch (the scan takes the last workgroup)
+      hipLaunchKernelGGL(k_tile_order, dim3((unsigned)((n + 255) / 256) + 1), dim3(256), 0, st,
+                         pq->cntq, n, pq->order, pq->qptr, pq->n_live);
+    } else {
+      hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pq->cntq, n, pq->qptr, pq->n_live);
+    }
+    hipLaunchKernelGGL(k_row_compact, dim3((n + 3) / 4), dim3(256), 0, st, pq->kinds, n, pq->nk,
+                       pq->qptr, pq->kidx, pq->kkind, pq->kpack);
+  }
+  if (pk) {
+    const int n = B * pk->nk;
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pk->cntk, n, pk->kptr,
+                       pq ? (int32_t*)nullptr : pk->n_live);
+    hipLaunchKernelGGL(k_row_compact, dim3((n + 3) / 4), dim3(256), 0, st, pk->kinds_t, n, pk->nq,
+                       pk->kptr, pk->qidx, pk->qkind, pk->qpack);
   }
   return hipGetLastError();
 }

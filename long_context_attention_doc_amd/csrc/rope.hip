@@ -17,9 +17,14 @@
 
 namespace aa {
 
-// table[(pos * (D/2) + p) * 2 + {0,1}] = {cos, sin}(pos * theta_p)
-__global__ void k_rope_table(int S, int half, RopeTheta th, float* __restrict__ table) {
+// table[(pos * (D/2) + p) * 2 + {0,1}] = {cos, sin}(pos * theta_p).  The
+// first kernel of a call: it also clears the call's device status word and
+// the counters the plan build adds to (either may be null).
+__global__ void k_rope_table(int S, int half, RopeTheta th, float* __restrict__ table,
+                             int32_t* __restrict__ status, int32_t* __restrict__ zero, int n_zero) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0 && status) status[0] = kStatusOk;
+  if (zero && i < n_zero) zero[i] = 0;
   if (i >= (long long)S * half) return;
   const int p = (int)(i % half);
   const long long pos = i / half;
@@ -48,11 +53,13 @@ __global__ void k_rope_apply(const bf16* __restrict__ x, const int32_t* __restri
   *(bf16x8*)(y + i * 8) = rope_rotate8(xv, table + ((size_t)p * (D / 2) + d0 / 2) * 2);
 }
 
-hipError_t launch_rope_table(int S, int D, const RopeTheta& th, float* table, hipStream_t st) {
-  const long long n = (long long)S * (D / 2);
+hipError_t launch_rope_table(int S, int D, const RopeTheta& th, float* table, int32_t* status,
+                             int32_t* zero, int n_zero, hipStream_t st) {
+  long long n = (long long)S * (D / 2);
+  if (zero && n_zero > n) n = n_zero;
   const int threads = 256;
   hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0,
-                     st, S, D / 2, th, table);
+                     st, S, D / 2, th, table, status, zero, n_zero);
   return hipGetLastError();
 }
 
