@@ -377,61 +377,88 @@ def backward(q, k, v, do, cu, rope_base: float, causal: bool = True, scale: floa
 # ----------------------------------------------------------------------------
 # Block-sparse tile plan, by brute force over the explicit mask
 # ----------------------------------------------------------------------------
-def _classify(m: np.ndarray, e: np.ndarray, kt: int, anchor: bool = True) -> int:
-    """Kind of one tile from its allowed / exists element masks [BM, BN]."""
+def _classify(m: np.ndarray, e: np.ndarray, anchor_col: bool) -> int:
+    """Kind of one tile from its allowed / exists element masks [BM, BN];
+    anchor_col: the tile's first column is the row's anchor key."""
     if not m.any():
         return KIND_NONE
     if e.all() and m.all():
         return KIND_FULL
-    if anchor and kt == 0 and not m[:, 1:].any():
+    if anchor_col and not m[:, 1:].any():
         return KIND_ANCHOR
     return KIND_PARTIAL
 
 
+def _grid(S: int, B_: int, origin: int) -> int:
+    """Tiles of size B_ along a row of S tokens: ceil(S / B_), whatever the
+    origin (with origin 1 the last tile may be short or empty)."""
+    return -(-S // B_)
+
+
 def tile_kinds_row(cu, B: int, S: int, BM: int, BN: int, b: int, qt: int,
-                   causal: bool = True, anchor: bool = True) -> np.ndarray:
-    """Kinds of every key tile for query tile qt of row b, from the dense mask."""
-    nk = -(-S // BN)
-    rows = np.arange(b * S + qt * BM, b * S + min(S, (qt + 1) * BM))
+                   causal: bool = True, anchor: bool = True, origin: int = 0) -> np.ndarray:
+    """Kinds of every key tile for query tile qt of row b, from the dense mask.
+    Query tile qt holds rows origin + qt*BM .. origin + (qt+1)*BM - 1 and key
+    tile kt keys origin + kt*BN .. (row-local, cut at S); with origin 1 the
+    row's anchor (query and key 0) lies outside every tile."""
+    nk = _grid(S, BN, origin)
+    r0 = origin + qt * BM
+    rows = np.arange(b * S + r0, b * S + min(S, r0 + BM))
     cols = np.arange(b * S, (b + 1) * S)
-    m = np.zeros((BM, nk * BN), dtype=bool)
-    e = np.zeros((BM, nk * BN), dtype=bool)
-    m[:len(rows), :S] = allowed(cu, B, S, rows, cols, causal, anchor)
-    e[:len(rows), :S] = True
-    return np.array([_classify(m[:, kt * BN:(kt + 1) * BN], e[:, kt * BN:(kt + 1) * BN], kt, anchor)
-                     for kt in range(nk)], dtype=np.uint8)
+    width = origin + nk * BN
+    m = np.zeros((BM, width), dtype=bool)
+    e = np.zeros((BM, width), dtype=bool)
+    if len(rows):
+        m[:len(rows), :S] = allowed(cu, B, S, rows, cols, causal, anchor)
+        e[:len(rows), :S] = True
+    out = []
+    for kt in range(nk):
+        c0 = origin + kt * BN
+        out.append(_classify(m[:, c0:c0 + BN], e[:, c0:c0 + BN], anchor and c0 == 0))
+    return np.array(out, dtype=np.uint8)
 
 
 def tile_kinds_col(cu, B: int, S: int, BM: int, BN: int, b: int, kt: int,
-                   causal: bool = True, anchor: bool = True) -> np.ndarray:
-    """Kinds of every query tile for key tile kt of row b, from the dense mask."""
-    nq = -(-S // BM)
-    cols = np.arange(b * S + kt * BN, b * S + min(S, (kt + 1) * BN))
+                   causal: bool = True, anchor: bool = True, origin: int = 0) -> np.ndarray:
+    """Kinds of every query tile for key tile kt of row b, from the dense mask
+    (tiles placed as in tile_kinds_row)."""
+    nq = _grid(S, BM, origin)
+    c0 = origin + kt * BN
+    cols = np.arange(b * S + c0, b * S + min(S, c0 + BN))
     rows = np.arange(b * S, (b + 1) * S)
-    m = np.zeros((nq * BM, BN), dtype=bool)
-    e = np.zeros((nq * BM, BN), dtype=bool)
-    m[:S, :len(cols)] = allowed(cu, B, S, rows, cols, causal, anchor)
-    e[:S, :len(cols)] = True
-    return np.array([_classify(m[qt * BM:(qt + 1) * BM], e[qt * BM:(qt + 1) * BM], kt, anchor)
-                     for qt in range(nq)], dtype=np.uint8)
+    height = origin + nq * BM
+    m = np.zeros((height, BN), dtype=bool)
+    e = np.zeros((height, BN), dtype=bool)
+    if len(cols):
+        m[:S, :len(cols)] = allowed(cu, B, S, rows, cols, causal, anchor)
+        e[:S, :len(cols)] = True
+    out = []
+    for qt in range(nq):
+        r0 = origin + qt * BM
+        out.append(_classify(m[r0:r0 + BM], e[r0:r0 + BM], anchor and c0 == 0))
+    return np.array(out, dtype=np.uint8)
 
 
-def tile_plan(cu, B: int, S: int, BM: int, BN: int, causal: bool = True, anchor: bool = True):
+def tile_plan(cu, B: int, S: int, BM: int, BN: int, causal: bool = True, anchor: bool = True,
+              origin: int = 0):
     """Live (query-tile, key-tile) pairs and their kinds, from the dense mask.
 
     A tile is live when it holds at least one allowed element.  FULL: all
-    BM*BN elements exist (no ragged edge) and are allowed.  ANCHOR: key tile 0
-    whose only allowed elements lie in column 0 (the row's anchor).  PARTIAL:
-    any other live tile.  Returns a dict of int32/uint8 arrays:
-    qptr [B*nq+1], kidx, kkind (query-major, key tiles ascending) and
-    kptr [B*nk+1], qidx, qkind (key-major, query tiles ascending).
+    BM*BN elements exist (no ragged edge) and are allowed.  ANCHOR: the key
+    tile that starts at the anchor column (key tile 0 at origin 0) whose only
+    allowed elements lie in that column.  PARTIAL: any other live tile.  With
+    origin 1 the grid starts after the anchor (query tile qt holds rows
+    1 + qt*BM ..), so no tile holds the anchor's row or column.  Returns a dict
+    of int32/uint8 arrays: qptr [B*nq+1], kidx, kkind (query-major, key tiles
+    ascending) and kptr [B*nk+1], qidx, qkind (key-major, query tiles
+    ascending).
     """
-    nq = -(-S // BM)
-    nk = -(-S // BN)
+    nq = _grid(S, BM, origin)
+    nk = _grid(S, BN, origin)
     kinds = np.zeros((B, nq, nk), dtype=np.uint8)
     for b in range(B):
         for qt in range(nq):
-            kinds[b, qt] = tile_kinds_row(cu, B, S, BM, BN, b, qt, causal, anchor)
+            kinds[b, qt] = tile_kinds_row(cu, B, S, BM, BN, b, qt, causal, anchor, origin)
     qptr = [0]
     kidx, kkind = [], []
     for b in range(B):

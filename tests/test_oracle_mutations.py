@@ -23,10 +23,12 @@ MUTANTS = [
     ("dK not un-rotated", "dk[:, gi, :] = rope(dk_rot[:, gi, :], pos[k_cols], rope_base, inverse=True)",
      "dk[:, gi, :] = rope(dk_rot[:, gi, :], pos[k_cols], rope_base)"),
     ("anchor column dropped", "return same_batch_row & (sees_anchor | same_doc)", "return same_batch_row & same_doc"),
-    ("anchor kind on any key tile", "    if anchor and kt == 0 and not m[:, 1:].any():",
-     "    if anchor and not m[:, 1:].any():"),
-    ("anchor kind without an anchor", "    if anchor and kt == 0 and not m[:, 1:].any():",
-     "    if kt == 0 and not m[:, 1:].any():"),
+    ("anchor kind on any key tile", "anchor and c0 == 0))\n    return np.array(out, dtype=np.uint8)\n\n\ndef tile_kinds_col",
+     "anchor))\n    return np.array(out, dtype=np.uint8)\n\n\ndef tile_kinds_col"),
+    ("anchor kind without an anchor", "        out.append(_classify(m[:, c0:c0 + BN], e[:, c0:c0 + BN], anchor and c0 == 0))",
+     "        out.append(_classify(m[:, c0:c0 + BN], e[:, c0:c0 + BN], c0 == 0))"),
+    ("grid origin ignored for query tiles", "    r0 = origin + qt * BM\n    rows = np.arange(",
+     "    r0 = qt * BM\n    rows = np.arange("),
     ("no-anchor mask keeps the anchor column", "    if not anchor:\n        return same_batch_row & same_doc",
      "    if False:\n        return same_batch_row & same_doc"),
     ("no-anchor first token at position 0", "    if anchor:\n        pos = np.where(is_anchor, 0, pos)",
@@ -36,12 +38,12 @@ MUTANTS = [
     ("interleaved chunks ignored", "    if seg_doc is None:\n        return seg", "    if True:\n        return seg"),
     ("document label without its row", "    label_of_seg = row * span + seg_doc + 1",
      "    label_of_seg = seg_doc + 1"),
-    ("key-major column classified as its query tile",
-     "    return np.array([_classify(m[qt * BM:(qt + 1) * BM], e[qt * BM:(qt + 1) * BM], kt, anchor)",
-     "    return np.array([_classify(m[qt * BM:(qt + 1) * BM], e[qt * BM:(qt + 1) * BM], qt, anchor)"),
+    ("key-major column with the anchor flag on every tile",
+     "        out.append(_classify(m[r0:r0 + BM], e[r0:r0 + BM], anchor and c0 == 0))",
+     "        out.append(_classify(m[r0:r0 + BM], e[r0:r0 + BM], anchor))"),
     ("key-major column shifted by one key",
-     "    cols = np.arange(b * S + kt * BN, b * S + min(S, (kt + 1) * BN))",
-     "    cols = np.arange(b * S + kt * BN + 1, b * S + min(S, (kt + 1) * BN + 1))"),
+     "    c0 = origin + kt * BN\n    cols = np.arange(b * S + c0, b * S + min(S, c0 + BN))",
+     "    c0 = origin + kt * BN\n    cols = np.arange(b * S + c0 + 1, b * S + min(S, c0 + BN + 1))"),
 ]
 PIN_FILES = ("test_oracle_pins.py", "test_oracle_modes.py", "test_oracle_interleaved.py")
 

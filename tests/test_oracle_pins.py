@@ -456,13 +456,14 @@ def test_plan_key_major_is_transpose():
 
 
 # ---------------------------------------------------------------- key-major checker
-def _brute_kinds(rows, S, BM, BN, causal=True, anchor=True):
+def _brute_kinds(rows, S, BM, BN, causal=True, anchor=True, origin=0):
     """Tile kinds [B, nq, nk] by scalar loops over every element, from the
     document lengths alone (no oracle mask): a query sees its row's anchor
     (with ``anchor``) and the keys of its own document not after it (any of
-    them when not ``causal``).  Kinds: FULL when all BM*BN elements exist and
-    are seen, ANCHOR for key tile 0 when only column 0 is seen, PARTIAL for
-    any other tile with a seen element."""
+    them when not ``causal``).  Tile (qt, kt) holds rows origin + qt*BM ..
+    and keys origin + kt*BN .. below S.  Kinds: FULL when all BM*BN elements
+    exist and are seen, ANCHOR for the tile starting at key 0 when only column
+    0 is seen, PARTIAL for any other tile with a seen element."""
     B = len(rows)
     nq, nk = -(-S // BM), -(-S // BN)
     doc = []
@@ -479,8 +480,8 @@ def _brute_kinds(rows, S, BM, BN, causal=True, anchor=True):
             for kt in range(nk):
                 seen = exist = 0
                 only_anchor = True
-                for i in range(qt * BM, (qt + 1) * BM):
-                    for j in range(kt * BN, (kt + 1) * BN):
+                for i in range(origin + qt * BM, origin + (qt + 1) * BM):
+                    for j in range(origin + kt * BN, origin + (kt + 1) * BN):
                         if i >= S or j >= S:
                             continue
                         exist += 1
@@ -498,16 +499,18 @@ def _brute_kinds(rows, S, BM, BN, causal=True, anchor=True):
                     continue
                 if seen == exist == BM * BN:
                     out[b, qt, kt] = oracle.KIND_FULL
-                elif anchor and kt == 0 and only_anchor:
+                elif anchor and origin + kt * BN == 0 and only_anchor:
                     out[b, qt, kt] = oracle.KIND_ANCHOR
                 else:
                     out[b, qt, kt] = oracle.KIND_PARTIAL
     return out
 
 
+@pytest.mark.parametrize("origin", [0, 1])
 @pytest.mark.parametrize("case", range(6))
-def test_plan_rows_and_columns_scalar_brute_force(case):
-    """tile_kinds_row, tile_kinds_col and tile_plan against element loops."""
+def test_plan_rows_and_columns_scalar_brute_force(case, origin):
+    """tile_kinds_row, tile_kinds_col and tile_plan against element loops,
+    with the tile grid at the row's first token or right after the anchor."""
     rng = np.random.default_rng(300 + case)
     anchor = case % 2 == 0
     causal = case != 5
@@ -522,16 +525,16 @@ def test_plan_rows_and_columns_scalar_brute_force(case):
     else:
         rows = [W.random_partition(rng, S + 1, 6) for _ in range(B)]   # partitions of S tokens
         cu = W.cu_doc_lens_no_anchor(rows, S)
-    ref = _brute_kinds(rows, S, BM, BN, causal, anchor)
+    ref = _brute_kinds(rows, S, BM, BN, causal, anchor, origin)
     nq, nk = ref.shape[1:]
     for b in range(B):
         for qt in range(nq):
-            got = oracle.tile_kinds_row(cu, B, S, BM, BN, b, qt, causal, anchor)
+            got = oracle.tile_kinds_row(cu, B, S, BM, BN, b, qt, causal, anchor, origin)
             assert np.array_equal(got, ref[b, qt]), (b, qt)
         for kt in range(nk):
-            got = oracle.tile_kinds_col(cu, B, S, BM, BN, b, kt, causal, anchor)
+            got = oracle.tile_kinds_col(cu, B, S, BM, BN, b, kt, causal, anchor, origin)
             assert np.array_equal(got, ref[b, :, kt]), (b, kt)
-    p = oracle.tile_plan(cu, B, S, BM, BN, causal, anchor)
+    p = oracle.tile_plan(cu, B, S, BM, BN, causal, anchor, origin)
     for b in range(B):
         for kt in range(nk):
             a, z = p["kptr"][b * nk + kt], p["kptr"][b * nk + kt + 1]
@@ -606,3 +609,32 @@ def test_plan_tile_totals_of_the_workloads(name):
 @pytest.mark.parametrize("name", ["short_docs", "64k"])
 def test_plan_tile_totals_of_the_large_workloads(name):
     _check_totals(name)
+
+
+@pytest.mark.parametrize("BM,BN", [(128, 64), (64, 128), (64, 64)])
+def test_plan_after_the_anchor_aligned_documents_closed_form(BM, BN):
+    """With the grid after the anchor, documents whose lengths are multiples
+    of both tile sides start on tile edges: each one is its own causal block
+    triangle (query tile i of a document sees its key tiles j with
+    j*BN <= (i+1)*BM - 1, FULL when every key of j precedes every row of i),
+    no tile is shared by two documents, and no tile holds the anchor."""
+    L = max(BM, BN) * 2
+    n_docs = 3
+    S = 1 + n_docs * L
+    cu = _cu([[L] * n_docs], S)
+    p = oracle.tile_plan(cu, 1, S, BM, BN, origin=1)
+    got = {}
+    for qt in range(p["nq"]):
+        for e in range(p["qptr"][qt], p["qptr"][qt + 1]):
+            got[(qt, int(p["kidx"][e]))] = int(p["kkind"][e])
+    want = {}
+    for d in range(n_docs):
+        q0, k0 = d * L // BM, d * L // BN
+        for i in range(L // BM):
+            for j in range((i + 1) * BM // BN + (1 if ((i + 1) * BM) % BN else 0)):
+                if j * BN > (i + 1) * BM - 1:
+                    continue
+                full = (j + 1) * BN - 1 <= i * BM
+                want[(q0 + i, k0 + j)] = oracle.KIND_FULL if full else oracle.KIND_PARTIAL
+    assert got == want
+    assert oracle.KIND_ANCHOR not in got.values()
