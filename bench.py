@@ -255,6 +255,8 @@ def main() -> int:
         doc_rows = workloads.rows_without_anchor(doc_rows)
     cu_np = (w.cu_doc_lens if anchor else workloads.cu_doc_lens_no_anchor(doc_rows, w.S))
     cu = torch.from_numpy(cu_np).to(dev)
+    # the binding's choice of tile grid (after the anchor for short documents)
+    flags |= api.grid_flag(cu_np, w.B, w.S, flags)
     ws_f = torch.empty(api.workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, False), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(api.workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, True), dtype=torch.uint8, device=dev)
     chunk_doc = None
@@ -409,7 +411,8 @@ def main() -> int:
                    "mode": args.mode, "batch": w.B, "seq_len": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "rope_base": w.rope_base, "documents_per_row": len(doc_rows[0]),
                    "backward": w.backward, "unmasked_pairs_per_head": fl["pairs_per_head"],
-                   "bwd_reuses_forward_workspace": reuse},
+                   "bwd_reuses_forward_workspace": reuse,
+                   "tile_grid": "after the anchor" if flags & api.FLAG_GRID_AFTER_ANCHOR else "from the first token"},
         "graph_ms_per_step": graph_ms,
         "graph_tflops": (total_flops / (graph_ms * 1e-3) / 1e12) if graph_ms else None,
         "tokens_per_s": tokens / (ms * 1e-3),

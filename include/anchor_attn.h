@@ -111,6 +111,20 @@ enum {
  *       without the bf16 rounding, and the backward reads O in that dtype
  *       (16-byte aligned in both cases).  The other entry points reject it. */
 #define AA_FLAG_O_FP32 8
+/*   AA_FLAG_GRID_AFTER_ANCHOR  (the *_ex, chunk and no-alloc attention entry
+ *       points, and anchor_attn_tile_plan) place the tile grid after each
+ *       row's anchor: query tile qt holds rows 1 + qt*BM .. and key tile kt
+ *       keys 1 + kt*BN .. (row-local, cut at S; nq and nk stay ceil(S/BM),
+ *       ceil(S/BN)), so no tile holds the anchor's row or column and there is
+ *       no AA_TILE_ANCHOR kind; the anchor row's outputs and gradient are
+ *       formed outside the tiles.  Results are the same either way (up to
+ *       float32 summation order); the choice is about speed: documents whose
+ *       lengths are multiples of the tiles then start on tile edges and touch
+ *       fewer tiles (many short documents), while long documents gain
+ *       nothing.  The attention entry points reject it with
+ *       AA_FLAG_NO_ANCHOR; a forward and a backward that share a workspace
+ *       (AA_FLAG_FWD_WORKSPACE) must agree on it. */
+#define AA_FLAG_GRID_AFTER_ANCHOR 16
 
 /* Human-readable text for a status code (static storage). */
 const char* anchor_attn_strerror(aa_status s);
@@ -257,7 +271,9 @@ size_t anchor_attn_plan_capacity(int B, int S, int BM, int BN);
  * anchor_attn_plan_capacity() entries; n_live (device int32) receives the
  * number of live tiles.  BM and BN are powers of two in [16, 256].  flags:
  * AA_FLAG_NO_ANCHOR plans rows without an anchor (no anchor column, no
- * AA_TILE_ANCHOR kinds); AA_FLAG_CONTINUOUS_POS does not change a plan. */
+ * AA_TILE_ANCHOR kinds); AA_FLAG_GRID_AFTER_ANCHOR places the grid after the
+ * anchor (the attention kernels' grid for rows with an anchor);
+ * AA_FLAG_CONTINUOUS_POS does not change a plan. */
 aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, int S, int BM, int BN,
                                 int causal, int flags,
                                 int32_t* qptr, int32_t* kidx, uint8_t* kkind,

@@ -22,6 +22,9 @@ FLAG_CONTINUOUS_POS, FLAG_NO_ANCHOR = 1, 2
 FLAG_FWD_WORKSPACE = 4
 # O in float32 instead of bf16 (forward output and backward input)
 FLAG_O_FP32 = 8
+# anchor_attn_tile_plan: the tile grid after each row's anchor (the attention
+# kernels' grid for rows with an anchor)
+FLAG_GRID_AFTER_ANCHOR = 16
 TILE_FULL, TILE_PARTIAL, TILE_ANCHOR = 1, 2, 3
 
 # Tile shapes the attention kernels run with (query tile x key tile).
@@ -136,6 +139,23 @@ def _check_host_cu(cu, B: int, S: int, anchor: bool) -> None:
 def _check_cu(cu, B: int, S: int, flags: int) -> None:
     if not (isinstance(cu, torch.Tensor) and cu.is_cuda):
         _check_host_cu(cu, B, S, not flags & FLAG_NO_ANCHOR)
+
+
+# Mean document length up to which the tile grid goes after the anchor.
+GRID_AFTER_ANCHOR_MAX_MEAN_DOC = 512
+
+
+def grid_flag(cu_doc_lens, B: int, S: int, flags: int = 0) -> int:
+    """FLAG_GRID_AFTER_ANCHOR when rows carry an anchor and their documents
+    are short on average (at most GRID_AFTER_ANCHOR_MAX_MEAN_DOC tokens; the
+    grid after the anchor then saves whole tiles per document), else 0.  Read
+    from a host copy of cu_doc_lens; a device copy gives 0."""
+    import numpy as np
+    if flags & FLAG_NO_ANCHOR or (isinstance(cu_doc_lens, torch.Tensor) and cu_doc_lens.is_cuda):
+        return 0
+    n_seg = np.asarray(cu_doc_lens.cpu() if isinstance(cu_doc_lens, torch.Tensor) else cu_doc_lens).size - 1
+    n_docs = max(1, n_seg - B)
+    return FLAG_GRID_AFTER_ANCHOR if B * (S - 1) <= GRID_AFTER_ANCHOR_MAX_MEAN_DOC * n_docs else 0
 
 
 def _need_o(o: torch.Tensor, flags: int) -> None:
@@ -482,5 +502,7 @@ def anchor_attention(q, k, v, cu_doc_lens, rope_base: float, causal: bool = True
     """AnchorAttention with autograd: q [B,S,Hq,D], k/v [B,S,Hkv,D] bf16 on the GPU.
     A host cu_doc_lens is validated here, before it is copied to the device."""
     _check_cu(cu_doc_lens, q.shape[0], q.shape[1], flags)
+    # the forward and its backward share the grid choice (and the workspace)
+    flags |= grid_flag(cu_doc_lens, q.shape[0], q.shape[1], flags)
     cu = _dev_cu(cu_doc_lens, q.device)
     return _AnchorAttnFn.apply(q, k, v, cu, float(rope_base), bool(causal), softmax_scale, int(flags))

@@ -51,8 +51,14 @@ struct ChunkBufs {
 };
 
 // Buffers of one tile plan.
+// Tile (qt, kt) of a plan holds rows origin + qt*BM .. and keys
+// origin + kt*BN .. (row-local, cut at S; nq = ceil(S/BM), nk = ceil(S/BN)).
+// With origin 1 (rows that start with the shared anchor) no tile holds the
+// anchor's query row or key column: every query sees the anchor column
+// outside the tiles, and the anchor row sees only itself.
 struct PlanBufs {
   int BM, BN, nq, nk;
+  int origin;          // 0 or 1
   size_t cap;          // B * nq * nk
   uint8_t* kinds;      // dense [B][nq][nk]
   uint8_t* kinds_t;    // dense [B][nk][nq] (key-major copy)
@@ -137,6 +143,8 @@ struct BwdArgs {
   int B, S, Hq, Hkv, D;
   float scale;
   int anchor;          // 0: rows without a shared anchor (intra-document attention)
+  int origin = 0;      // the tile grid's first row (PlanBufs::origin); blocks of the
+                       // preprocess follow it
   // Rows permuted so that documents are contiguous: position p (over B*S) is
   // token tok_map[p] of the caller's o, lse, dq, dk, dv; qr, kr, v, dout and
   // the token tables are in permuted order.  Null: no permutation.

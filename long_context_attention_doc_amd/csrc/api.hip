@@ -49,9 +49,15 @@ PlanLayout plan_layout(int B, int S, int BM, int BN, size_t base) {
   return p;
 }
 
-PlanBufs plan_bufs(const PlanLayout& l, char* ws) {
+// Where the attention kernels' tile grid starts in a row: after the anchor
+// with AA_FLAG_GRID_AFTER_ANCHOR, else at the row's first token.
+int grid_origin(int flags) { return (flags & AA_FLAG_GRID_AFTER_ANCHOR) ? 1 : 0; }
+
+// origin: where the tile grid starts in a row (1 after a shared anchor).
+PlanBufs plan_bufs(const PlanLayout& l, char* ws, int origin) {
   PlanBufs b;
   b.BM = l.BM; b.BN = l.BN; b.nq = l.nq; b.nk = l.nk; b.cap = l.cap;
+  b.origin = origin;
   b.kinds = (uint8_t*)(ws + l.kinds);
   b.kinds_t = (uint8_t*)(ws + l.kinds_t);
   b.cntq = (int32_t*)(ws + l.cntq);
@@ -202,7 +208,8 @@ aa_status prologue(const Layout& L, char* ws, const void* q, const void* k,
   const int mode = (flags & AA_FLAG_CONTINUOUS_POS) ? 1 : 0;
   const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   float* table = (float*)(ws + L.table);
-  PlanBufs pq = plan_bufs(L.pq, ws), pk = plan_bufs(L.pk, ws);
+  const int origin = grid_origin(flags);
+  PlanBufs pq = plan_bufs(L.pq, ws, origin), pk = plan_bufs(L.pk, ws, origin);
   // Position IDs reach S when a document without an anchor fills a row under
   // reset IDs (its tokens count 1 .. S), so the table has S + 1 rows.  The
   // table kernel runs first: it also clears the status word and the
@@ -238,7 +245,8 @@ aa_status prologue_chunks(const Layout& L, const ChunkLayout& C, char* ws, const
   const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   const ChunkBufs cb = chunk_bufs(C, ws);
   float* table = (float*)(ws + L.table);
-  PlanBufs pq = plan_bufs(L.pq, ws), pk = plan_bufs(L.pk, ws);
+  const int origin = grid_origin(flags);
+  PlanBufs pq = plan_bufs(L.pq, ws, origin), pk = plan_bufs(L.pk, ws, origin);
   AA_LAUNCH(AA_K_ROPE_TABLE, st,
             launch_rope_table(S + 1, D, make_theta(D, rope_base), table, status,
                               bwd ? pk.cntk : nullptr, B * pk.nk, st));
@@ -290,12 +298,19 @@ static bool flags_ok(int flags, int extra = 0) {
   return (flags & ~(AA_FLAG_CONTINUOUS_POS | AA_FLAG_NO_ANCHOR | extra)) == 0;
 }
 
+// Flags of the attention entry points: the grid after the anchor needs rows
+// that have one.
+static bool attn_flags_ok(int flags, int extra) {
+  if ((flags & AA_FLAG_GRID_AFTER_ANCHOR) && (flags & AA_FLAG_NO_ANCHOR)) return false;
+  return flags_ok(flags, extra | AA_FLAG_O_FP32 | AA_FLAG_GRID_AFTER_ANCHOR);
+}
+
 static aa_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* cu_doc_lens,
                           int n_seg, double rope_base, int causal, int flags, int B, int S, int Hq,
                           int Hkv, int D, float softmax_scale, void* o, float* lse,
                           void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !cu_doc_lens || !o || !lse || !workspace) return AA_EINVAL;
-  if (!flags_ok(flags, AA_FLAG_FWD_WORKSPACE | AA_FLAG_O_FP32)) return AA_EINVAL;
+  if (!attn_flags_ok(flags, AA_FLAG_FWD_WORKSPACE)) return AA_EINVAL;
   if (!shape_ok(B, S, Hq, Hkv, D) || n_seg < B) return AA_EINVAL;
   if (D != 64 && D != 128) return AA_EUNSUPPORTED;
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
@@ -321,7 +336,7 @@ static aa_status fwd_impl(const void* q, const void* k, const void* v, const int
   const int anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
   AA_LAUNCH(AA_K_FWD, stream,
             launch_fwd((const bf16*)q, (const float*)(ws + L.table), S + 1, (bf16*)(ws + L.qrot),
-                       (const bf16*)(ws + L.krot), (const bf16*)v, tt, plan_bufs(L.pq, ws),
+                       (const bf16*)(ws + L.krot), (const bf16*)v, tt, plan_bufs(L.pq, ws, grid_origin(flags)),
                        (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D, scale, anchor, o,
                        (flags & AA_FLAG_O_FP32) ? 1 : 0, lse, nullptr, stream));
   return AA_OK;
@@ -334,7 +349,7 @@ static aa_status bwd_impl(const void* q, const void* k, const void* v, const voi
                           void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !dout || !cu_doc_lens || !dq || !dk || !dv || !workspace)
     return AA_EINVAL;
-  if (!flags_ok(flags, AA_FLAG_FWD_WORKSPACE | AA_FLAG_O_FP32)) return AA_EINVAL;
+  if (!attn_flags_ok(flags, AA_FLAG_FWD_WORKSPACE)) return AA_EINVAL;
   if (!shape_ok(B, S, Hq, Hkv, D) || n_seg < B) return AA_EINVAL;
   if (D != 64 && D != 128) return AA_EUNSUPPORTED;
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
@@ -378,10 +393,12 @@ static aa_status bwd_impl(const void* q, const void* k, const void* v, const voi
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
   a.scale = scale;
   a.anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
+  a.origin = grid_origin(flags);
   AA_LAUNCH(AA_K_BWD_PRE, stream, launch_bwd_pre(a, stream));
   AA_LAUNCH(AA_K_BWD_DKDV, stream,
-            launch_bwd_dkdv(a, plan_bufs(L.pk, ws), plan_bufs(L.pq, ws), stream));
-  AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
+            launch_bwd_dkdv(a, plan_bufs(L.pk, ws, a.origin), plan_bufs(L.pq, ws, a.origin),
+                            stream));
+  AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws, a.origin), stream));
   // without an anchor, key 0 is an ordinary key and dk/dv of it are complete
   if (a.anchor) AA_LAUNCH(AA_K_BWD_ANCHOR, stream, launch_bwd_anchor(a, stream));
   return AA_OK;
@@ -435,7 +452,7 @@ static aa_status chunk_args_ok(const int32_t* cu, const int32_t* chunk_doc, int 
   if (!cu || !chunk_doc) return AA_EINVAL;
   if (!shape_ok(B, S, Hq, Hkv, D) || n_chunks < B) return AA_EINVAL;
   if (D != 64 && D != 128) return AA_EUNSUPPORTED;
-  if (!flags_ok(flags, extra_flags)) return AA_EINVAL;
+  if (!(extra_flags ? attn_flags_ok(flags, 0) : flags_ok(flags))) return AA_EINVAL;
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return AA_EINVAL;
   if (!aligned(cu, 4) || !aligned(chunk_doc, 4)) return AA_EINVAL;
   return AA_OK;
@@ -466,7 +483,7 @@ aa_status anchor_attn_fwd_chunks(const void* q, const void* k, const void* v,
   const int32_t* src = (const int32_t*)(ws + C.src);
   AA_LAUNCH(AA_K_FWD, stream,
             launch_fwd(nullptr, nullptr, 0, (bf16*)(ws + L.qrot), (const bf16*)(ws + L.krot),
-                       (const bf16*)(ws + C.vperm), tt, plan_bufs(L.pq, ws),
+                       (const bf16*)(ws + C.vperm), tt, plan_bufs(L.pq, ws, grid_origin(flags)),
                        (const int32_t*)(ws + L.status), B, S, Hq, Hkv, D, scale, anchor, o,
                        (flags & AA_FLAG_O_FP32) ? 1 : 0, lse, src, stream));
   return AA_OK;
@@ -522,10 +539,12 @@ aa_status anchor_attn_bwd_chunks(const void* q, const void* k, const void* v, co
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
   a.scale = scale;
   a.anchor = (flags & AA_FLAG_NO_ANCHOR) ? 0 : 1;
+  a.origin = grid_origin(flags);
   AA_LAUNCH(AA_K_BWD_PRE, stream, launch_bwd_pre(a, stream));
   AA_LAUNCH(AA_K_BWD_DKDV, stream,
-            launch_bwd_dkdv(a, plan_bufs(L.pk, ws), plan_bufs(L.pq, ws), stream));
-  AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws), stream));
+            launch_bwd_dkdv(a, plan_bufs(L.pk, ws, a.origin), plan_bufs(L.pq, ws, a.origin),
+                            stream));
+  AA_LAUNCH(AA_K_BWD_DQ, stream, launch_bwd_dq(a, plan_bufs(L.pq, ws, a.origin), stream));
   if (a.anchor) AA_LAUNCH(AA_K_BWD_ANCHOR, stream, launch_bwd_anchor(a, stream));
   return AA_OK;
 }
@@ -597,7 +616,7 @@ aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, in
     return AA_EINVAL;
   if (B < 1 || S < 1 || (long long)B * S > 0x7fffffffLL || n_seg < B) return AA_EINVAL;
   if (!tile_ok(BM) || !tile_ok(BN)) return AA_EUNSUPPORTED;
-  if (!flags_ok(flags)) return AA_EINVAL;
+  if (!flags_ok(flags, AA_FLAG_GRID_AFTER_ANCHOR)) return AA_EINVAL;
   if (!aligned(workspace, kAlign)) return AA_EINVAL;
   const size_t need = anchor_attn_plan_workspace_size(B, S, BM, BN);
   if (ws_bytes < need) return AA_EWORKSPACE;
@@ -607,7 +626,7 @@ aa_status anchor_attn_tile_plan(const int32_t* cu_doc_lens, int n_seg, int B, in
   TokenTables tt{(int32_t*)(ws + up(4)), (int32_t*)(ws + up(4) + up(T * 4)),
                  (int32_t*)(ws + up(4) + 2 * up(T * 4))};
   const PlanLayout pl = plan_layout(B, S, BM, BN, up(4) + 3 * up(T * 4));
-  PlanBufs pb = plan_bufs(pl, ws);
+  PlanBufs pb = plan_bufs(pl, ws, (flags & AA_FLAG_GRID_AFTER_ANCHOR) ? 1 : 0);
   // the caller's output arrays replace the workspace copies
   pb.qptr = qptr; pb.kidx = kidx; pb.kkind = kkind;
   pb.kptr = kptr; pb.qidx = qidx; pb.qkind = qkind; pb.n_live = n_live;

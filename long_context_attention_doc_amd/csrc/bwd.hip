@@ -41,9 +41,10 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
     const void* __restrict__ o, int o_f32, const bf16* __restrict__ dout,
     const float* __restrict__ lse,
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi, int S, int Hq, int Hkv,
-    int nblk, float scale, int anchor, float* __restrict__ dvec, float* __restrict__ ds0,
-    float* __restrict__ part_dk, float* __restrict__ part_dv, float* __restrict__ qstats,
-    const int32_t* __restrict__ tok_map) {
+    int nblk, float scale, int anchor, int origin, float* __restrict__ dvec,
+    float* __restrict__ ds0, float* __restrict__ part_dk, float* __restrict__ part_dv,
+    float* __restrict__ qstats, const int32_t* __restrict__ tok_map,
+    const int32_t* __restrict__ status, bf16* __restrict__ dq) {
   constexpr int LPR = D / 8;                // lanes per row
   constexpr int RPP = 256 / LPR;            // rows per pass of the workgroup
   __shared__ float red_k[RPP][D + 4];
@@ -65,8 +66,14 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
     for (int i = 0; i < 8; ++i) { k0[i] = (float)kk[i]; v0[i] = (float)vv[i]; }
   }
   float pk[8] = {0, 0, 0, 0, 0, 0, 0, 0}, pv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r0 = 0; r0 < kPreRows; r0 += RPP) {
-    const int row = blk * kPreRows + r0 + slot;
+  // Blocks follow the query tiles of the tile grid (rows origin + 64*blk ..).
+  // With the grid after the anchor, block 0 also takes the anchor row in a
+  // pass of its own (r0 = -RPP, slot 0 only): its Dv, its anchor-column
+  // terms and its dq, which no query tile covers.
+  const bool anchor_pass = origin && blk == 0;
+  for (int r0 = anchor_pass ? -RPP : 0; r0 < kPreRows; r0 += RPP) {
+    const bool arow = r0 < 0;
+    const int row = arow ? (slot == 0 ? 0 : S) : origin + blk * kPreRows + r0 + slot;
     const bool valid = row < S;
     const size_t tok = tok0 + (valid ? row : S - 1);
     const size_t otok = tok_map ? (size_t)tok_map[tok] : tok;   // the caller's O and LSE row
@@ -106,7 +113,15 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
       dvec[((size_t)b * Hq + hq) * S + row] = d_o;
       ds0[((size_t)b * Hq + hq) * S + row] = dsv;
     }
-    if ((tid % LPR) == 0) {
+    if (arow && valid) {
+      // dq of the anchor row: scale * dS_00 k'_0, position 0 (no rotation)
+      bf16x8 w;
+      const bool bad = status[0] != kStatusOk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = (bf16)(bad ? NAN : scale * dsv * k0[i]);
+      *(bf16x8*)(dq + (otok * Hq + hq) * D + f0) = w;
+    }
+    if ((tid % LPR) == 0 && !arow) {
       // tile-aligned record for the dK/dV kernel; rows past S see nothing
       float* rec = qstats + (((size_t)b * Hq + hq) * nblk + blk) * 4 * kPreRows;
       const int rr = r0 + slot;
@@ -157,9 +172,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     const int32_t* __restrict__ kptr, const int32_t* __restrict__ qpack,
     const int32_t* __restrict__ order_flags, const int32_t* __restrict__ status, int S, int Hq,
     int Hkv,
-    int nk, int nblk, int n_items, float scale, int anchor, const int32_t* __restrict__ tok_map,
-    bf16* __restrict__ dk,
-    bf16* __restrict__ dv) {
+    int nk, int nblk, int n_items, float scale, int anchor, int origin,
+    const int32_t* __restrict__ tok_map, bf16* __restrict__ dk, bf16* __restrict__ dv) {
   constexpr int BM = kDkvBM, BN = kDkvBN;    // plan tiles: 64 queries x 128 keys
   constexpr int BH = BM / 2;                 // queries per step
   constexpr int NKK = D / 16;
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   const int group = Hq / Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
-  const int key = kt * BN + wave * 32 + col;     // row-local key of this lane's column
+  const int key = origin + kt * BN + wave * 32 + col;   // row-local key of this lane's column
   const bool kvalid = key < S;
   const size_t tok0 = (size_t)b * S;
   const size_t ktok = tok0 + (kvalid ? key : S - 1);
@@ -205,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
 #pragma unroll
     for (int u = 0; u < BN * NCH / 256; ++u) {
       const int idx = u * 256 + tid, r = idx / NCH, c = idx % NCH;
-      const int krow = min(kt * BN + r, S - 1);
+      const int krow = min(origin + kt * BN + r, S - 1);
       *(bf16x8*)(Ks + r * KLD + c * 8) = *(const bf16x8*)(kb0 + (size_t)krow * kv_row_stride + c * 8);
     }
   }
@@ -223,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   DirectTile<D, BH, 256> dl;
   dl.init(q_row_stride);
   auto issue = [&](int buf, int hq, int qt, int half) {
-    const int row0 = qt * BM + half * BH;
+    const int row0 = origin + qt * BM + half * BH;
     dl.load_at(lds_addr(Qs[0]) + buf * (BH * D * 2), qr + tok0 * q_row_stride + (size_t)hq * D,
                q_row_stride, row0, S - 1);
     dl.load_at(lds_addr(Gs[0]) + buf * (BH * D * 2), dout + tok0 * q_row_stride + (size_t)hq * D,
@@ -269,7 +283,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   int kro = (32 * wave + col) * KLD + 8 * h;
   int cur = 0;
   while (hq < h_end) {
-    const bool need_mask = packed_kind(qpack[e]) != kTileFull || (anchor && kt == 0);
+    const bool need_mask =
+        packed_kind(qpack[e]) != kTileFull || (anchor && kt == 0 && origin == 0);
     int e1 = e, h1 = hq, half1 = half ^ 1;
     if (half1 == 0) advance(e1, h1);
     const int qt1 = h1 < h_end ? packed_idx(qpack[e1]) : 0;
@@ -376,7 +391,7 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_bwd_dq(
     const int32_t* __restrict__ hi, const int32_t* __restrict__ qptr,
     const int32_t* __restrict__ kpack, const int32_t* __restrict__ order,
     const int32_t* __restrict__ status, int S, int Hq, int Hkv, int nq, int n_items, float scale,
-    int anchor, const int32_t* __restrict__ tok_map, bf16* __restrict__ dq) {
+    int anchor, int origin, const int32_t* __restrict__ tok_map, bf16* __restrict__ dq) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
@@ -399,7 +414,7 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_bwd_dq(
   const int hkv = hq / (Hq / Hkv);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
-  const int qrow = qt * BM + wave * 32 + col;
+  const int qrow = origin + qt * BM + wave * 32 + col;
   const bool qvalid = qrow < S;
   const size_t tok0 = (size_t)b * S;
   const size_t tok = tok0 + (qvalid ? qrow : S - 1);
@@ -434,8 +449,8 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_bwd_dq(
   DirectTile<D, BN, kFwdThreads> dl;
   dl.init(kv_row_stride);
   auto issue = [&](int buf, int kt) {
-    dl.load(buf ? Ks1 : Ks0, kbase, kv_row_stride, kt * BN, S - 1);
-    dl.load(buf ? Vs1 : Vs0, vbase, kv_row_stride, kt * BN, S - 1);
+    dl.load(buf ? Ks1 : Ks0, kbase, kv_row_stride, origin + kt * BN, S - 1);
+    dl.load(buf ? Vs1 : Vs0, vbase, kv_row_stride, origin + kt * BN, S - 1);
   };
 
   int e_first = qptr[tile];
@@ -448,7 +463,8 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_bwd_dq(
     constexpr int BUF = decltype(bufc)::value;
     const int ent = kpack[e_first + i];
     const int kt = packed_idx(ent);
-    const bool need_mask = packed_kind(ent) != kTileFull || (anchor && kt == 0);
+    const bool need_mask = packed_kind(ent) != kTileFull || (anchor && kt == 0 && origin == 0);
+    const int key0 = origin + kt * BN;   // the tile's first key (row-local)
     const bool more = i + 1 < n_tiles;
     const int ent_next = more ? kpack[e_first + i + 1] : 0;
     wait_direct_loads();
@@ -462,7 +478,7 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_bwd_dq(
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       // a block none of the wave's queries may see contributes exactly zero
-      const int k0 = kt * BN + 32 * kb;
+      const int k0 = key0 + 32 * kb;
       if (need_mask && !__builtin_amdgcn_ballot_w64(qlo <= k0 + 31 && qhi >= k0)) continue;
       f32x16 st, dpt;
 #pragma unroll
@@ -477,7 +493,7 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_bwd_dq(
 #pragma unroll
       for (int j = 0; j < 16; ++j) st[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[j], scale_log2, nlse2));
       if (need_mask) {
-        const int a = qlo - kt * BN - 4 * h - kb * 32, z = qhi - kt * BN - 4 * h - kb * 32;
+        const int a = qlo - k0 - 4 * h, z = qhi - k0 - 4 * h;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int off = 8 * (j >> 2) + (j & 3);
@@ -573,12 +589,12 @@ hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)blocks);
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_pre<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.o_f32, a.dout,
-                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.dvec, a.ds0,
-                       a.part_dk, a.part_dv, a.qstats, a.tok_map);
+                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.origin,
+                       a.dvec, a.ds0, a.part_dk, a.part_dv, a.qstats, a.tok_map, a.status, a.dq);
   else
     hipLaunchKernelGGL(k_bwd_pre<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.o, a.o_f32, a.dout,
-                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.dvec, a.ds0,
-                       a.part_dk, a.part_dv, a.qstats, a.tok_map);
+                       a.lse, a.tt.lo, a.tt.hi, a.S, a.Hq, a.Hkv, a.nblk, a.scale, a.anchor, a.origin,
+                       a.dvec, a.ds0, a.part_dk, a.part_dv, a.qstats, a.tok_map, a.status, a.dq);
   return hipGetLastError();
 }
 
@@ -590,11 +606,13 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, const PlanBufs& pk, const PlanBufs&
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_dkdv<128>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout,
                        a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, flags, a.status, a.S,
-                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, a.tok_map, a.dk, a.dv);
+                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, pk.origin, a.tok_map,
+                       a.dk, a.dv);
   else
     hipLaunchKernelGGL(k_bwd_dkdv<64>, grid, dim3(256), 0, st, a.qr, a.kr, a.v, a.dout,
                        a.qstats, a.table, a.tt.pos, pk.kptr, pk.qpack, flags, a.status, a.S,
-                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, a.tok_map, a.dk, a.dv);
+                       a.Hq, a.Hkv, pk.nk, a.nblk, n_items, a.scale, a.anchor, pk.origin, a.tok_map,
+                       a.dk, a.dv);
   return hipGetLastError();
 }
 
@@ -604,13 +622,13 @@ hipError_t launch_bwd_dq(const BwdArgs& a, const PlanBufs& pq, hipStream_t st) {
   if (a.D == 128)
     hipLaunchKernelGGL(k_bwd_dq<128>, grid, dim3(kFwdThreads), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
-                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.tok_map,
-                       a.dq);
+                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, pq.origin,
+                       a.tok_map, a.dq);
   else
     hipLaunchKernelGGL(k_bwd_dq<64>, grid, dim3(kFwdThreads), 0, st, a.qr, a.kr, a.v, a.dout, a.lse,
                        a.dvec, a.ds0, a.table, a.tt.pos, a.tt.lo, a.tt.hi, pq.qptr, pq.kpack,
-                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, a.tok_map,
-                       a.dq);
+                       pq.order, a.status, a.S, a.Hq, a.Hkv, pq.nq, n_items, a.scale, a.anchor, pq.origin,
+                       a.tok_map, a.dq);
   return hipGetLastError();
 }
 

@@ -50,8 +50,8 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_fwd(
     const int32_t* __restrict__ lo, const int32_t* __restrict__ hi,
     const int32_t* __restrict__ qptr, const int32_t* __restrict__ kpack,
     const int32_t* __restrict__ order, const int32_t* __restrict__ status, int S, int Hq, int Hkv,
-    int nq, int n_items, float scale_log2, int anchor, void* __restrict__ o, int o_f32,
-    float* __restrict__ lse, const int32_t* __restrict__ tok_map) {
+    int nq, int n_items, float scale_log2, int anchor, int origin, void* __restrict__ o,
+    int o_f32, float* __restrict__ lse, const int32_t* __restrict__ tok_map) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int NKK = D / 16;    // 16-wide reduction steps over d
   constexpr int NDB = D / 32;    // 32-row blocks of d in O^T
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_fwd(
   const int hkv = hq / (Hq / Hkv);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
-  const int qrow = qt * BM + wave * 32 + col;
+  const int qrow = origin + qt * BM + wave * 32 + col;
   const bool qvalid = qrow < S;
   const size_t tok = (size_t)b * S + (qvalid ? qrow : S - 1);
   int qlo = lo[tok], qhi = hi[tok];
@@ -103,8 +103,8 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_fwd(
   DirectTile<D, BN, kFwdThreads> dl;
   dl.init(kv_row_stride);
   auto issue = [&](int buf, int kt) {
-    dl.load(buf ? Ks1 : Ks0, kbase, kv_row_stride, kt * BN, S - 1);
-    dl.load(buf ? Vs1 : Vs0, vbase, kv_row_stride, kt * BN, S - 1);
+    dl.load(buf ? Ks1 : Ks0, kbase, kv_row_stride, origin + kt * BN, S - 1);
+    dl.load(buf ? Vs1 : Vs0, vbase, kv_row_stride, origin + kt * BN, S - 1);
   };
 
   // Live key tiles e_first .. e_end-1 (only key tile 0 can be anchor-only).
@@ -163,7 +163,10 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_fwd(
     constexpr int BUF = decltype(bufc)::value;
     const int ent = kpack[e_first + i];
     const int kt = packed_idx(ent);
-    const bool need_mask = packed_kind(ent) != kTileFull || (anchor && kt == 0);
+    // (at origin 0 key tile 0 holds the anchor column, which the softmax
+    // start already counts)
+    const bool need_mask = packed_kind(ent) != kTileFull || (anchor && kt == 0 && origin == 0);
+    const int key0 = origin + kt * BN;   // the tile's first key (row-local)
     const bool more = i + 1 < n_tiles;
     const int ent_next = more ? kpack[e_first + i + 1] : 0;
     wait_direct_loads();
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_fwd(
     bool live[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int k0 = kt * BN + 32 * kb;
+      const int k0 = key0 + 32 * kb;
       live[kb] = !need_mask || __builtin_amdgcn_ballot_w64(qlo <= k0 + 31 && qhi >= k0) != 0;
     }
 
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_fwd(
       }
     if (need_mask) {
       // keys outside [qlo, qhi] (row-local) are masked
-      const int a = qlo - kt * BN - 4 * h, z = qhi - kt * BN - 4 * h;
+      const int a = qlo - key0 - 4 * h, z = qhi - key0 - 4 * h;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
         if (live[kb]) {
@@ -296,6 +299,51 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_fwd(
       lse[((size_t)b * Hq + hq) * S + (otok - tok0)] = bad ? NAN : val;
     }
   }
+
+  // The anchor row, outside a grid that starts after it: it sees only
+  // itself, so O_0 = v_0 and LSE_0 = scale * q'_0 . k'_0 (position 0, so
+  // q'_0, k'_0 are the inputs themselves).  Wave 0 of the row's first query
+  // tile does it, one 8-feature piece per lane.
+  if (origin && qt == 0 && wave == 0) {
+    constexpr int NC = D / 8;
+    const size_t otok = tok_map ? (size_t)tok_map[tok0] : tok0;
+    float sp = 0.f;
+    if (lane < NC) {
+      const size_t qa = (tok0 * Hq + hq) * D + 8 * lane;
+      bf16x8 qv = *(const bf16x8*)((ROTATE_Q ? q_raw : qr) + qa);
+      if constexpr (ROTATE_Q) {
+        qv = rope_rotate8(qv, table + 8 * lane);   // table row 0: the identity, bit for bit
+        *(bf16x8*)(qr + qa) = qv;
+      }
+      const bf16x8 kv = *(const bf16x8*)(kr + (tok0 * Hkv + hkv) * D + 8 * lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sp += (float)qv[i] * (float)kv[i];
+      const bf16x8 vv = *(const bf16x8*)(v + (tok0 * Hkv + hkv) * D + 8 * lane);
+      const size_t orow = (otok * Hq + hq) * D + 8 * lane;
+      if (o_f32) {
+        f32x4 w0, w1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w0[i] = bad ? NAN : (float)vv[i];
+          w1[i] = bad ? NAN : (float)vv[4 + i];
+        }
+        ((f32x4*)((float*)o + orow))[0] = w0;
+        ((f32x4*)((float*)o + orow))[1] = w1;
+      } else {
+        bf16x8 w = vv;
+        if (bad) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i] = (bf16)NAN;
+        }
+        *(bf16x8*)((bf16*)o + orow) = w;
+      }
+    }
+#pragma unroll
+    for (int off = NC / 2; off > 0; off >>= 1) sp += __shfl_xor(sp, off);
+    if (lane == 0)
+      lse[((size_t)b * Hq + hq) * S + (otok - tok0)] =
+          bad ? NAN : sp * scale_log2 * 0.69314718055994530942f;
+  }
 }
 
 hipError_t launch_fwd(const bf16* q_raw, const float* table, int npos, bf16* qr, const bf16* kr,
@@ -308,7 +356,7 @@ hipError_t launch_fwd(const bf16* q_raw, const float* table, int npos, bf16* qr,
 #define AA_LAUNCH_FWD(DD, RQ)                                                                    \
   hipLaunchKernelGGL((k_fwd<DD, RQ>), grid, dim3(kFwdThreads), 0, st, q_raw, table, tt.pos, npos, qr, kr, \
                      v, tt.lo, tt.hi, pb.qptr, pb.kpack, pb.order, status, S, Hq, Hkv, pb.nq,     \
-                     n_items, scale_log2, anchor, o, o_f32, lse, tok_map)
+                     n_items, scale_log2, anchor, pb.origin, o, o_f32, lse, tok_map)
   if (D == 128) {
     if (q_raw) AA_LAUNCH_FWD(128, true);
     else AA_LAUNCH_FWD(128, false);

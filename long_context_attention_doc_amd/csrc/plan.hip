@@ -88,30 +88,32 @@ __global__ void k_positions(const int32_t* __restrict__ cu, int n_seg, int B, in
 // elements exist and are seen; ANCHOR when it is key tile 0 and only column
 // 0 is seen; PARTIAL otherwise; 0 when dead.
 __device__ __forceinline__ uint8_t tile_kind(const int* slo, const int* shi, int r, int nrows,
-                                             int BM, int kt, int BN, int S, int anchor) {
-  const int c0 = kt * BN;
+                                             int BM, int c0, int BN, int S, int anchor) {
   const int c1 = min(S, c0 + BN) - 1;
   const bool cols_exist = (c0 + BN) <= S;
+  const bool anchor_col = anchor && c0 == 0;      // the tile starts at the anchor column
   bool any_live = false, any_doc = false, all_full = nrows == BM && cols_exist;
   for (int i = r; i < r + nrows; ++i) {
     const int a = max(slo[i], c0), z = min(shi[i], c1);
     const int ndoc = z >= a ? z - a + 1 : 0;
-    const int n = ndoc + (anchor && kt == 0 ? 1 : 0);
+    const int n = ndoc + (anchor_col ? 1 : 0);
     any_live |= n > 0;
     any_doc |= ndoc > 0;
     all_full &= n == BN;
   }
   if (!any_live) return 0;
-  return all_full ? kTileFull : ((anchor && kt == 0 && !any_doc) ? kTileAnchor : kTilePartial);
+  return all_full ? kTileFull : ((anchor_col && !any_doc) ? kTileAnchor : kTilePartial);
 }
 
-// One workgroup per (row b, block of RB rows): with cu given, the token
-// tables of its rows (and its share of the layout checks); otherwise it reads
-// them.  Then the kinds of every tile whose query tile lies in its rows, for
-// up to two plans: a query-major one (dense kinds row and live count of each
-// of its query tiles) and a key-major one (dense key-major kinds, live counts
-// of the key tiles added atomically to cntk, which must start at zero).
-// RB is a multiple of each plan's BM and at most 256.
+// One workgroup per (row b, block of RB rows starting at origin + rb*RB):
+// with cu given, the token tables of its rows (the first block of a row also
+// those of the rows before origin) and its share of the layout checks;
+// otherwise it reads them.  Then the kinds of every tile whose query tile
+// lies in its rows, for up to two plans of the same origin: a query-major one
+// (dense kinds row and live count of each of its query tiles) and a
+// key-major one (dense key-major kinds, live counts of the key tiles added
+// atomically to cntk, which must start at zero).  RB is a multiple of each
+// plan's BM and at most 256.
 struct KindsOut {
   int BM, BN, nq, nk;
   uint8_t* kinds;      // [B][nq][nk] (query-major) or [B][nk][nq] (key-major)
@@ -122,26 +124,29 @@ struct KindsOut {
 __global__ __launch_bounds__(256) void k_plan_kinds(
     const int32_t* __restrict__ cu, int n_seg, int B, int S, int causal, int mode, int anchor,
     int32_t* __restrict__ pos, int32_t* __restrict__ lo, int32_t* __restrict__ hi,
-    int32_t* __restrict__ status, int RB, int nrb, KindsOut p0, KindsOut p1) {
+    int32_t* __restrict__ status, int RB, int nrb, int origin, KindsOut p0, KindsOut p1) {
   __shared__ int slo[256], shi[256];
   __shared__ int wcount[4];
   const int b = blockIdx.x / nrb, rb = blockIdx.x % nrb;
-  const int r0 = rb * RB;
-  const int nrows = min(RB, S - r0);
+  const int r0 = origin + rb * RB;
+  const int nrows = max(0, min(RB, S - r0));
   const size_t tok0 = (size_t)b * S + r0;
   if (cu) {
     check_offsets((long long)blockIdx.x * blockDim.x + threadIdx.x, cu, n_seg, (long long)B * S,
                   status);
-    for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
+    // r < 0: the rows before the grid's origin, done by the row's first block
+    for (int r = (rb == 0 ? -origin : 0) + (int)threadIdx.x; r < nrows; r += blockDim.x) {
       int p, l, h;
       bool bad;
-      token_tables((long long)(tok0 + r), cu, n_seg, S, causal, mode, anchor, p, l, h, bad);
+      token_tables((long long)tok0 + r, cu, n_seg, S, causal, mode, anchor, p, l, h, bad);
       if (bad) status[0] = kStatusBadDocs;
       pos[tok0 + r] = p;
       lo[tok0 + r] = l;
       hi[tok0 + r] = h;
-      slo[r] = l;
-      shi[r] = h;
+      if (r >= 0) {
+        slo[r] = l;
+        shi[r] = h;
+      }
     }
   } else {
     for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
@@ -154,13 +159,13 @@ __global__ __launch_bounds__(256) void k_plan_kinds(
     const KindsOut& P = pl ? p1 : p0;
     if (!P.kinds) continue;
     for (int sub = 0; sub < RB / P.BM; ++sub) {
-      const int qt = r0 / P.BM + sub;
+      const int qt = rb * (RB / P.BM) + sub;
       if (qt >= P.nq) break;                      // uniform
       const int rr = sub * P.BM;
-      const int n = min(P.BM, nrows - rr);
+      const int n = max(0, min(P.BM, nrows - rr));
       int cnt = 0;
       for (int kt = threadIdx.x; kt < P.nk; kt += blockDim.x) {
-        const uint8_t kind = tile_kind(slo, shi, rr, n, P.BM, kt, P.BN, S, anchor);
+        const uint8_t kind = tile_kind(slo, shi, rr, n, P.BM, origin + kt * P.BN, P.BN, S, anchor);
         if (P.key_major) {
           P.kinds[((size_t)b * P.nk + kt) * P.nq + qt] = kind;
           if (kind) atomicAdd(P.cnt + (size_t)b * P.nk + kt, 1);
@@ -332,6 +337,7 @@ hipError_t launch_plans(const PlanSrc& src, int B, int S, int anchor, const Plan
                         const PlanBufs* pk, hipStream_t st) {
   KindsOut o[2] = {};
   int RB = 0;
+  const int origin = pq ? pq->origin : pk->origin;
   if (pq) {
     o[0] = KindsOut{pq->BM, pq->BN, pq->nq, pq->nk, pq->kinds, pq->cntq, 0};
     RB = pq->BM;
@@ -340,14 +346,15 @@ hipError_t launch_plans(const PlanSrc& src, int B, int S, int anchor, const Plan
     o[1] = KindsOut{pk->BM, pk->BN, pk->nq, pk->nk, pk->kinds_t, pk->cntk, 1};
     RB = RB > pk->BM ? RB : pk->BM;
   }
-  if (RB == 0 || RB > 256 || (pq && RB % pq->BM) || (pk && RB % pk->BM))
+  if (RB == 0 || RB > 256 || (pq && RB % pq->BM) || (pk && RB % pk->BM) ||
+      (pq && pk && pq->origin != pk->origin))
     return hipErrorInvalidValue;
   const int nrb = (S + RB - 1) / RB;
   // the launch must cover the n_seg offsets it checks (RB <= 256 threads per
   // RB rows, and n_seg <= B*S)
   hipLaunchKernelGGL(k_plan_kinds, dim3(B * nrb), dim3(256), 0, st, src.cu, src.n_seg, B, S,
                      src.causal, src.mode, anchor, src.tt.pos, src.tt.lo, src.tt.hi, src.status, RB,
-                     nrb, o[0], o[1]);
+                     nrb, origin, o[0], o[1]);
   if (pq) {
     const int n = B * pq->nq;
     if (pq->order) {

@@ -87,6 +87,7 @@ def _cases():
         ("no_anchor", 3, 2, 640, 2, 1, 128, False, 0, True, 10, 4),
         ("continuous", 4, 1, 777, 2, 2, 128, True, 1, True, 8, 5),
         ("noncausal", 5, 1, 500, 2, 2, 64, True, 0, False, 6, 3),
+        ("grid_after_anchor", 6, 2, 700, 4, 2, 128, True, 16, True, 12, 4),
     ]
 
 
@@ -95,7 +96,7 @@ def test_fwd_bwd_interleaved(gpu_lib, case):
     name, seed, B, S, Hq, Hkv, D, anchor, fpos, causal, max_docs, max_chunks = case
     cu, cd = _layout(100 + seed, B, S, anchor, max_docs, max_chunks)
     flags = fpos | (0 if anchor else gpu_lib.FLAG_NO_ANCHOR)
-    mode = "continuous" if fpos else "reset"
+    mode = "continuous" if fpos & 1 else "reset"
     say(f"[chunks] {name} B={B} S={S} chunks={len(cd)} flags={flags} causal={causal}")
     q, k, v, do = W.make_tensors(B, S, Hq, Hkv, D, 900 + seed)
     o, lse = gpu_lib.anchor_attn_fwd_chunks(q.cuda(), k.cuda(), v.cuda(), cu, cd, 1e4, causal, flags=flags)

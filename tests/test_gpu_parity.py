@@ -37,20 +37,24 @@ def _inputs(B, S, Hq, Hkv, D, seed):
     return q, k, v, do
 
 
+@pytest.mark.parametrize("grid", [0, 16], ids=["grid_first_token", "grid_after_anchor"])
 @pytest.mark.parametrize("case", _small_cases(), ids=lambda c: c[0])
-def test_fwd_bwd_small_full_compare(gpu_lib, case):
+def test_fwd_bwd_small_full_compare(gpu_lib, case, grid):
+    """Both tile grids (from the row's first token; after the anchor,
+    FLAG_GRID_AFTER_ANCHOR) against the oracle in full."""
     name, B, S, Hq, Hkv, D, rows, base, causal = case
-    say(f"[parity] {name} B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} causal={causal}")
+    say(f"[parity] {name} B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} causal={causal} grid={grid}")
     cu = W.cu_doc_lens_from_lengths(rows, S)
     q, k, v, do = _inputs(B, S, Hq, Hkv, D, 1234)
-    o, lse = gpu_lib.anchor_attn_fwd(q.cuda(), k.cuda(), v.cuda(), cu, base, causal)
+    o, lse = gpu_lib.anchor_attn_fwd(q.cuda(), k.cuda(), v.cuda(), cu, base, causal, flags=grid)
     o_ref, lse_ref, _, _ = oracle.forward(q, k, v, cu, base, causal)
     o_g = f64(o).reshape(B * S, Hq, D)
     say(f"[parity] {name} O err {o_err(o_g, o_ref):.2e}")
     assert o_err(o_g, o_ref) <= O_TOL, o_err(o_g, o_ref)
     lse_g = f64(lse).transpose(1, 0, 2).reshape(Hq, B * S)
     assert np.abs(lse_g - lse_ref).max() <= LSE_TOL
-    dq, dk, dv = gpu_lib.anchor_attn_bwd(q.cuda(), k.cuda(), v.cuda(), o, lse, do.cuda(), cu, base, causal)
+    dq, dk, dv = gpu_lib.anchor_attn_bwd(q.cuda(), k.cuda(), v.cuda(), o, lse, do.cuda(), cu, base, causal,
+                                         flags=grid)
     dq_r, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, base, causal)
     e = (rel_frob(f64(dq).reshape(B * S, Hq, D), dq_r), rel_frob(f64(dk).reshape(B * S, Hkv, D), dk_r),
          rel_frob(f64(dv).reshape(B * S, Hkv, D), dv_r))
@@ -60,7 +64,7 @@ def test_fwd_bwd_small_full_compare(gpu_lib, case):
 
 def _mode_cases():
     rng = np.random.default_rng(2025)
-    NA, CP = 2, 1     # FLAG_NO_ANCHOR, FLAG_CONTINUOUS_POS
+    NA, CP, GR = 2, 1, 16     # FLAG_NO_ANCHOR, FLAG_CONTINUOUS_POS, FLAG_GRID_AFTER_ANCHOR
     return [
         # name, B, S, Hq, Hkv, D, rows, base, causal, flags (rows cover S without an anchor)
         ("noanchor_reset_gqa", 2, 1000, 4, 2, 128, [W.random_partition(rng, 1001, 30) for _ in range(2)], 5e6, True, NA),
@@ -71,6 +75,8 @@ def _mode_cases():
         ("noanchor_s1", 2, 1, 2, 2, 64, [[1], [1]], 1e4, True, NA),
         ("anchor_continuous", 2, 1000, 4, 2, 128, [W.random_partition(rng, 1000, 30) for _ in range(2)], 5e6, True, CP),
         ("anchor_continuous_mixed", 2, 640, 2, 2, 128, [[1, 300, 1, 337], [639]], 5e5, True, CP),
+        ("anchor_continuous_grid_after", 2, 700, 4, 2, 64, [[128] * 5 + [59], [699]], 1e4, True, CP | GR),
+        ("noncausal_grid_after", 1, 600, 2, 2, 128, [[100, 1, 250, 248]], 1e4, False, GR),
     ]
 
 
@@ -181,14 +187,15 @@ def test_determinism(gpu_lib):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("flags", [0, 2], ids=["anchor", "no_anchor"])
+@pytest.mark.parametrize("flags", [0, 2, 16], ids=["anchor", "no_anchor", "anchor_grid_after"])
 def test_backward_reusing_the_forward_workspace(gpu_lib, flags):
     """AA_FLAG_FWD_WORKSPACE: the backward on the forward's workspace gives
     bit-identical gradients to a self-contained backward."""
     B, S, Hq, Hkv, D = 2, 1000, 4, 2, 128
     rng = np.random.default_rng(31)
-    rows = [W.random_partition(rng, S if flags == 0 else S + 1, 20) for _ in range(B)]
-    cu = W.cu_doc_lens_from_lengths(rows, S) if flags == 0 else W.cu_doc_lens_no_anchor(rows, S)
+    anchor = not flags & 2
+    rows = [W.random_partition(rng, S if anchor else S + 1, 20) for _ in range(B)]
+    cu = W.cu_doc_lens_from_lengths(rows, S) if anchor else W.cu_doc_lens_no_anchor(rows, S)
     q, k, v, do = (t.cuda() for t in _inputs(B, S, Hq, Hkv, D, 55))
     ws = torch.empty(gpu_lib.workspace_size(B, S, Hq, Hkv, D, True), dtype=torch.uint8, device="cuda")
     o, lse = gpu_lib.anchor_attn_fwd(q, k, v, cu, 5e6, workspace=ws, flags=flags)
@@ -214,8 +221,10 @@ def test_autograd_backward_twice_with_retained_graph(gpu_lib):
         t.grad = None
     o.backward(do.cuda())
     g2 = [t.grad for t in (qc, kc, vc)]
-    o2, lse2 = gpu_lib.anchor_attn_fwd(q.cuda(), k.cuda(), v.cuda(), cu, 5e6)
-    g3 = gpu_lib.anchor_attn_bwd(q.cuda(), k.cuda(), v.cuda(), o2, lse2, do.cuda(), cu, 5e6)
+    grid = gpu_lib.grid_flag(cu, B, S)      # the autograd path's choice of tile grid
+    o2, lse2 = gpu_lib.anchor_attn_fwd(q.cuda(), k.cuda(), v.cuda(), cu, 5e6, flags=grid)
+    g3 = gpu_lib.anchor_attn_bwd(q.cuda(), k.cuda(), v.cuda(), o2, lse2, do.cuda(), cu, 5e6,
+                                 flags=grid)
     for a, b, c in zip(g1, g2, g3):
         assert torch.equal(a, b) and torch.equal(a, c)
 
@@ -270,9 +279,10 @@ def test_full_size_sampled(gpu_lib, wname):
     q, k, v, do = W.make_tensors(B, S, Hq, Hkv, D, w.tensor_seed)
     cu = w.cu_doc_lens
     qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
-    say(f"[full] {wname} fwd+bwd on GPU")
-    o, lse = gpu_lib.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base)
-    dq, dk, dv = gpu_lib.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base)
+    grid = gpu_lib.grid_flag(cu, B, S)          # the benchmark's choice of tile grid
+    say(f"[full] {wname} fwd+bwd on GPU (grid flag {grid})")
+    o, lse = gpu_lib.anchor_attn_fwd(qc, kc, vc, cu, w.rope_base, flags=grid)
+    dq, dk, dv = gpu_lib.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, w.rope_base, flags=grid)
     torch.cuda.synchronize()
     assert not torch.isnan(o.float()).any()
     rng = np.random.default_rng(11)

@@ -71,6 +71,9 @@ def _cmp_plan(gp, ref, B):
     assert np.array_equal(gp["qkind"][:n].cpu().numpy(), ref["qkind"])
 
 
+GRID = 16   # FLAG_GRID_AFTER_ANCHOR: the grid the attention kernels use for rows with an anchor
+
+
 @pytest.mark.parametrize("tile", [(64, 64), (128, 64), (64, 128), (128, 128), (32, 16)])
 @pytest.mark.parametrize("case", _partitions()[:-1], ids=lambda c: c[0])
 def test_tile_plan_bit_exact_small(gpu_lib, case, tile):
@@ -79,9 +82,10 @@ def test_tile_plan_bit_exact_small(gpu_lib, case, tile):
     say(f"[plan] {name} B={B} S={S} tile={BM}x{BN}")
     cu = W.cu_doc_lens_from_lengths(rows, S)
     for causal in (True, False):
-        gp = gpu_lib.anchor_attn_tile_plan(cu, B, S, BM, BN, causal)
-        ref = oracle.tile_plan(cu, B, S, BM, BN, causal)
-        _cmp_plan(gp, ref, B)
+        for origin in (0, 1):
+            gp = gpu_lib.anchor_attn_tile_plan(cu, B, S, BM, BN, causal, flags=GRID if origin else 0)
+            ref = oracle.tile_plan(cu, B, S, BM, BN, causal, origin=origin)
+            _cmp_plan(gp, ref, B)
     cu_na = W.cu_doc_lens_no_anchor(W.rows_without_anchor(rows), S)
     for causal in (True, False):
         gp = gpu_lib.anchor_attn_tile_plan(cu_na, B, S, BM, BN, causal, flags=gpu_lib.FLAG_NO_ANCHOR)
@@ -92,10 +96,12 @@ def test_tile_plan_bit_exact_small(gpu_lib, case, tile):
 def test_tile_plan_bit_exact_8k_all_tiles(gpu_lib):
     w = W.get("8k")
     for BM, BN in ((128, 64), (64, 128), (128, 128)):
-        say(f"[plan] 8k tile={BM}x{BN}")
-        gp = gpu_lib.anchor_attn_tile_plan(w.cu_doc_lens, w.B, w.S, BM, BN)
-        ref = oracle.tile_plan(w.cu_doc_lens, w.B, w.S, BM, BN)
-        _cmp_plan(gp, ref, w.B)
+        for origin in (0, 1):
+            say(f"[plan] 8k tile={BM}x{BN} origin={origin}")
+            gp = gpu_lib.anchor_attn_tile_plan(w.cu_doc_lens, w.B, w.S, BM, BN,
+                                               flags=GRID if origin else 0)
+            ref = oracle.tile_plan(w.cu_doc_lens, w.B, w.S, BM, BN, origin=origin)
+            _cmp_plan(gp, ref, w.B)
 
 
 def _rows_of(gp, bq, key="q"):
@@ -123,45 +129,48 @@ def _recorded_totals(wname):
     return g["tile_totals"].get(wname, {})
 
 
+@pytest.mark.parametrize("origin", [0, 1], ids=["grid_first_token", "grid_after_anchor"])
 @pytest.mark.parametrize("wname", ["64k", "short_docs"])
-def test_tile_plan_bit_exact_full_size_whole(gpu_lib, wname):
+def test_tile_plan_bit_exact_full_size_whole(gpu_lib, wname, origin):
     """Whole full-size plans in the kernels' tile shapes (forward and dQ:
-    128 x 64 query-major; dK/dV: 64 x 128 key-major), every entry against the
-    brute force, plus the kind totals."""
+    128 x 64 query-major; dK/dV: 64 x 128 key-major), both grids, every entry
+    against the brute force; the kind totals of the 128 x 64 plan from the
+    row's first token also against the recorded ones."""
     w = W.get(wname)
     cu = w.cu_doc_lens
     for BM, BN in ((128, 64), (64, 128)):
-        say(f"[plan] {wname} tile={BM}x{BN}: GPU plan")
-        gp = gpu_lib.anchor_attn_tile_plan(cu, w.B, w.S, BM, BN)
-        say(f"[plan] {wname} tile={BM}x{BN}: oracle plan")
-        ref = oracle.tile_plan(cu, w.B, w.S, BM, BN)
+        say(f"[plan] {wname} tile={BM}x{BN} origin={origin}: GPU plan")
+        gp = gpu_lib.anchor_attn_tile_plan(cu, w.B, w.S, BM, BN, flags=GRID if origin else 0)
+        say(f"[plan] {wname} tile={BM}x{BN} origin={origin}: oracle plan")
+        ref = oracle.tile_plan(cu, w.B, w.S, BM, BN, origin=origin)
         _cmp_plan(gp, ref, w.B)
-        rec = _recorded_totals(wname).get(f"{BM}x{BN}")
-        say(f"[plan] {wname} tile={BM}x{BN}: F/P/A {_kind_totals(gp)} (recorded {rec})")
+        rec = _recorded_totals(wname).get(f"{BM}x{BN}") if origin == 0 else None
+        say(f"[plan] {wname} tile={BM}x{BN} origin={origin}: F/P/A {_kind_totals(gp)} (recorded {rec})")
         if rec:
             assert _kind_totals(gp) == rec[:3]
 
 
 def test_tile_plan_full_size_128k_sampled(gpu_lib):
     """128K GQA: sampled query tiles (query major) and key tiles (key major)
-    against the brute force, and the kind totals of the 128 x 64 plan."""
+    of the kernels' plans against the brute force, and the kind totals of the
+    128 x 64 plan from the row's first token."""
     w = W.get("128k_gqa")
     cu = w.cu_doc_lens
     rng = np.random.default_rng(5)
+    gp0 = gpu_lib.anchor_attn_tile_plan(cu, w.B, w.S, 128, 64)
+    assert _kind_totals(gp0) == [391396, 3733, 653]
     for BM, BN in ((128, 64), (64, 128)):
         say(f"[plan] 128k_gqa tile={BM}x{BN}")
-        gp = gpu_lib.anchor_attn_tile_plan(cu, w.B, w.S, BM, BN)
+        gp = gpu_lib.anchor_attn_tile_plan(cu, w.B, w.S, BM, BN, flags=GRID)
         nq, nk = gp["nq"], gp["nk"]
-        if (BM, BN) == (128, 64):
-            assert _kind_totals(gp) == [391396, 3733, 653]
         for b in range(w.B):
             for qt in sorted(set([0, 1, nq - 1] + list(rng.integers(0, nq, 6)))):
-                ref = oracle.tile_kinds_row(cu, w.B, w.S, BM, BN, b, int(qt))
+                ref = oracle.tile_kinds_row(cu, w.B, w.S, BM, BN, b, int(qt), origin=1)
                 idx, kind = _rows_of(gp, b * nq + int(qt), "q")
                 assert np.array_equal(idx, np.nonzero(ref)[0])
                 assert np.array_equal(kind, ref[ref != 0])
             for kt in sorted(set([0, 1, nk - 1] + list(rng.integers(0, nk, 4)))):
-                ref = oracle.tile_kinds_col(cu, w.B, w.S, BM, BN, b, int(kt))
+                ref = oracle.tile_kinds_col(cu, w.B, w.S, BM, BN, b, int(kt), origin=1)
                 idx, kind = _rows_of(gp, b * nk + int(kt), "k")
                 assert np.array_equal(idx, np.nonzero(ref)[0])
                 assert np.array_equal(kind, ref[ref != 0])
@@ -255,7 +264,7 @@ def test_tile_order_of_workload_plans(gpu_lib, wname):
     """The order the kernels use for the benchmark workloads: from the live-tile
     counts of the forward's query-major plan (128 x 64 tiles)."""
     w = W.get(wname)
-    plan = gpu_lib.anchor_attn_tile_plan(w.cu_doc_lens, w.B, w.S, 128, 64)
+    plan = gpu_lib.anchor_attn_tile_plan(w.cu_doc_lens, w.B, w.S, 128, 64, flags=GRID)
     qptr = plan["qptr"].cpu().numpy().astype(np.int64)
     cnt = np.diff(qptr).astype(np.int32)
     got = gpu_lib.anchor_attn_tile_order(torch.from_numpy(cnt).cuda()).cpu().numpy()
