@@ -180,11 +180,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   constexpr int NDB = D / 32;
   static_assert(BN == 4 * 32 && BH == 32, "four waves of 32 keys, 32-query steps");
   using T = SwzTile<D>;
-  // Two buffers of Q, dO and the query records, one LDS object each: the
-  // compiler can then tell that reads of one buffer do not alias the direct
-  // loads in flight into the other, and does not wait for those loads.
-  __shared__ __align__(16) bf16 Qs[2][BH * D];
-  __shared__ __align__(16) bf16 Gs[2][BH * D];
+  // Two buffers, each holding a Q and a dO half tile back to back: a dO
+  // read is then its Q read's address plus a constant (one address add for
+  // both operands).
+  __shared__ __align__(16) bf16 QG[2][2 * BH * D];
   __shared__ __align__(16) float s_st[2][4][BM];
   // This workgroup's keys (rotated), only ever read row-wise: rows padded by
   // 16 bytes instead of swizzled, so that 16 consecutive rows at one 16-byte
@@ -238,9 +237,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   dl.init(q_row_stride);
   auto issue = [&](int buf, int hq, int qt, int half) {
     const int row0 = origin + qt * BM + half * BH;
-    dl.load_at(lds_addr(Qs[0]) + buf * (BH * D * 2), qr + tok0 * q_row_stride + (size_t)hq * D,
+    dl.load_at(lds_addr(QG[0]) + buf * (4 * BH * D), qr + tok0 * q_row_stride + (size_t)hq * D,
                q_row_stride, row0, S - 1);
-    dl.load_at(lds_addr(Gs[0]) + buf * (BH * D * 2), dout + tok0 * q_row_stride + (size_t)hq * D,
+    dl.load_at(lds_addr(QG[0]) + buf * (4 * BH * D) + 2 * BH * D, dout + tok0 * q_row_stride + (size_t)hq * D,
                q_row_stride, row0, S - 1);
     if (wave == 0) {
       // the record index is wave-uniform: keep its arithmetic scalar
@@ -295,8 +294,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     // eight reads below stay one register plus immediate offsets (hoisted out
     // of the loop they would take eight registers)
     asm volatile("" : "+v"(kro));
-    const bf16* Qc = Qs[cur];
-    const bf16* Gc = Gs[cur];
+    const bf16* Qc = QG[cur];
+    const bf16* Gc = Qc + BH * D;
     const float* stc = &s_st[cur][0][0] + half * BH;
 
     // S = Q K^T, dP = dO V^T for the 32 queries: columns = this wave's keys.
