@@ -194,3 +194,20 @@ def test_noalloc_backward_refuses_what_does_not_fit(lib):
     rc = lib.anchor_attn_bwd_noalloc(fake, fake, fake, fake, fake, fake, fake, 2, 1e4, 1, 0, 1,
                                      256, 3, 2, 64, 0.0, fake, fake, fake, None)
     assert rc == api.AA_EINVAL
+
+
+def test_flag_constants_match_the_header(lib):
+    """The binding's FLAG_* values are the header's AA_FLAG_* bits, and the
+    stage entry points reject the attention-only options."""
+    from long_context_attention_doc_amd import api
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define AA_FLAG_(\w+) (\d+)", text))
+    assert defs, "no AA_FLAG_ defines found"
+    for name, val in defs.items():
+        assert getattr(api, "FLAG_" + name) == int(val), name
+    assert len(set(defs.values())) == len(defs)
+    fake = ctypes.c_void_p(1 << 20)
+    for f in (api.FLAG_O_FP32, api.FLAG_FWD_WORKSPACE):
+        assert lib.anchor_attn_position_ids(fake, 4, 1, 256, f, fake, fake, 1 << 40, None) == api.AA_EINVAL
+        assert lib.anchor_attn_chunk_layout(fake, fake, 4, 1, 256, 1, f, fake, fake, fake, 1 << 40,
+                                            None) == api.AA_EINVAL
