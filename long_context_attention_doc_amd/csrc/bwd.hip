@@ -68,74 +68,114 @@ __global__ __launch_bounds__(256) void k_bwd_pre(
   float pk[8] = {0, 0, 0, 0, 0, 0, 0, 0}, pv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   // Blocks follow the query tiles of the tile grid (rows origin + 64*blk ..).
   // With the grid after the anchor, block 0 also takes the anchor row in a
-  // pass of its own (r0 = -RPP, slot 0 only): its Dv, its anchor-column
-  // terms and its dq, which no query tile covers.
-  const bool anchor_pass = origin && blk == 0;
-  for (int r0 = anchor_pass ? -RPP : 0; r0 < kPreRows; r0 += RPP) {
-    const bool arow = r0 < 0;
-    const int row = arow ? (slot == 0 ? 0 : S) : origin + blk * kPreRows + r0 + slot;
-    const bool valid = row < S;
-    const size_t tok = tok0 + (valid ? row : S - 1);
-    const size_t otok = tok_map ? (size_t)tok_map[tok] : tok;   // the caller's O and LSE row
-    const size_t off = (tok * Hq + hq) * D + f0;
-    const bf16x8 qv = *(const bf16x8*)(qr + off);
-    float of[8];
-    if (o_f32) {
-      const f32x4* op = (const f32x4*)((const float*)o + (otok * Hq + hq) * D + f0);
-      const f32x4 o0 = op[0], o1 = op[1];
+  // pass of its own (slot 0 only): its Dv, its anchor-column terms and its
+  // dq, which no query tile covers.
+  //
+  // NP passes of RPP rows each: every pass's row loads are issued before the
+  // first row is reduced (one memory latency per workgroup instead of one
+  // per pass), with the O type a compile-time choice so that no branch
+  // splits the loads.
+  auto run = [&](auto o_is_f32, auto np_c, int r_first, bool arow) {
+    constexpr bool OF32 = decltype(o_is_f32)::value;
+    constexpr int NP = decltype(np_c)::value;
+    using OVec = std::conditional_t<OF32, f32x4, bf16x8>;
+    int row[NP];
+    bool valid[NP];
+    size_t tok[NP], otok[NP];
+    bf16x8 qv[NP], dv[NP];
+    OVec ov[NP][OF32 ? 2 : 1];
+    float L[NP];
+    int lov[NP], hiv[NP];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { of[i] = o0[i]; of[4 + i] = o1[i]; }
-    } else {
-      const bf16x8 ov = *(const bf16x8*)((const bf16*)o + (otok * Hq + hq) * D + f0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) of[i] = (float)ov[i];
+    for (int p = 0; p < NP; ++p) {
+      row[p] = arow ? (slot == 0 ? 0 : S) : origin + blk * kPreRows + r_first + p * RPP + slot;
+      valid[p] = row[p] < S;
+      tok[p] = tok0 + (valid[p] ? row[p] : S - 1);
+      otok[p] = tok[p];
     }
-    const bf16x8 dv = *(const bf16x8*)(dout + off);
-    float d_o = 0.f, s0 = 0.f, dp0 = 0.f;
+    if (tok_map) {   // the caller's O and LSE rows (one branch around all the loads)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float g = (float)dv[i];
-      d_o += g * of[i];
-      s0 += (float)qv[i] * k0[i];
-      dp0 += g * v0[i];
+      for (int p = 0; p < NP; ++p) otok[p] = (size_t)tok_map[tok[p]];
     }
 #pragma unroll
-    for (int off2 = LPR / 2; off2 > 0; off2 >>= 1) {
-      d_o += __shfl_xor(d_o, off2);
-      s0 += __shfl_xor(s0, off2);
-      dp0 += __shfl_xor(dp0, off2);
-    }
-    const float L = lse[((size_t)b * Hq + hq) * S + (otok - tok0)];
-    // without an anchor there is no anchor column: its weight and dS are zero
-    float p0 = valid && anchor ? __builtin_amdgcn_exp2f((s0 * scale - L) * kLog2e) : 0.f;
-    const float dsv = p0 * (dp0 - d_o);
-    if (valid && (tid % LPR) == 0) {
-      dvec[((size_t)b * Hq + hq) * S + row] = d_o;
-      ds0[((size_t)b * Hq + hq) * S + row] = dsv;
-    }
-    if (arow && valid) {
-      // dq of the anchor row: scale * dS_00 k'_0, position 0 (no rotation)
-      bf16x8 w;
-      const bool bad = status[0] != kStatusOk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = (bf16)(bad ? NAN : scale * dsv * k0[i]);
-      *(bf16x8*)(dq + (otok * Hq + hq) * D + f0) = w;
-    }
-    if ((tid % LPR) == 0 && !arow) {
-      // tile-aligned record for the dK/dV kernel; rows past S see nothing
-      float* rec = qstats + (((size_t)b * Hq + hq) * nblk + blk) * 4 * kPreRows;
-      const int rr = r0 + slot;
-      rec[rr] = valid ? L * kLog2e : 0.f;
-      rec[kPreRows + rr] = valid ? d_o : 0.f;
-      rec[2 * kPreRows + rr] = __int_as_float(valid ? lo[tok] : 1);
-      rec[3 * kPreRows + rr] = __int_as_float(valid ? hi[tok] : 0);
+    for (int p = 0; p < NP; ++p) {
+      const size_t off = (tok[p] * Hq + hq) * D + f0;
+      qv[p] = *(const bf16x8*)(qr + off);
+      dv[p] = *(const bf16x8*)(dout + off);
+      const size_t oo = (otok[p] * Hq + hq) * D + f0;
+      if constexpr (OF32) {
+        ov[p][0] = ((const f32x4*)((const float*)o + oo))[0];
+        ov[p][1] = ((const f32x4*)((const float*)o + oo))[1];
+      } else {
+        ov[p][0] = *(const bf16x8*)((const bf16*)o + oo);
+      }
+      L[p] = lse[((size_t)b * Hq + hq) * S + (otok[p] - tok0)];
+      lov[p] = lo[tok[p]];
+      hiv[p] = hi[tok[p]];
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pk[i] += dsv * (float)qv[i];
-      pv[i] += p0 * (float)dv[i];
+    for (int p = 0; p < NP; ++p) {
+      float of[8];
+      if constexpr (OF32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { of[i] = ov[p][0][i]; of[4 + i] = ov[p][1][i]; }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) of[i] = (float)ov[p][0][i];
+      }
+      float d_o = 0.f, s0 = 0.f, dp0 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float g = (float)dv[p][i];
+        d_o += g * of[i];
+        s0 += (float)qv[p][i] * k0[i];
+        dp0 += g * v0[i];
+      }
+#pragma unroll
+      for (int off2 = LPR / 2; off2 > 0; off2 >>= 1) {
+        d_o += __shfl_xor(d_o, off2);
+        s0 += __shfl_xor(s0, off2);
+        dp0 += __shfl_xor(dp0, off2);
+      }
+      // without an anchor there is no anchor column: its weight and dS are zero
+      const float p0 = valid[p] && anchor ? __builtin_amdgcn_exp2f((s0 * scale - L[p]) * kLog2e) : 0.f;
+      const float dsv = p0 * (dp0 - d_o);
+      if (valid[p] && (tid % LPR) == 0) {
+        dvec[((size_t)b * Hq + hq) * S + row[p]] = d_o;
+        ds0[((size_t)b * Hq + hq) * S + row[p]] = dsv;
+      }
+      if (arow && valid[p]) {
+        // dq of the anchor row: scale * dS_00 k'_0, position 0 (no rotation)
+        bf16x8 w;
+        const bool bad = status[0] != kStatusOk;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = (bf16)(bad ? NAN : scale * dsv * k0[i]);
+        *(bf16x8*)(dq + (otok[p] * Hq + hq) * D + f0) = w;
+      }
+      if ((tid % LPR) == 0 && !arow) {
+        // tile-aligned record for the dK/dV kernel; rows past S see nothing
+        float* rec = qstats + (((size_t)b * Hq + hq) * nblk + blk) * 4 * kPreRows;
+        const int rr = r_first + p * RPP + slot;
+        rec[rr] = valid[p] ? L[p] * kLog2e : 0.f;
+        rec[kPreRows + rr] = valid[p] ? d_o : 0.f;
+        rec[2 * kPreRows + rr] = __int_as_float(valid[p] ? lov[p] : 1);
+        rec[3 * kPreRows + rr] = __int_as_float(valid[p] ? hiv[p] : 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pk[i] += dsv * (float)qv[p][i];
+        pv[i] += p0 * (float)dv[p][i];
+      }
     }
-  }
+  };
+  constexpr int kPasses = kPreRows / RPP;
+  static_assert(kPasses * RPP == kPreRows, "whole passes per block");
+  auto all = [&](auto o_is_f32) {
+    if (origin && blk == 0) run(o_is_f32, std::integral_constant<int, 1>{}, 0, true);
+    run(o_is_f32, std::integral_constant<int, kPasses>{}, 0, false);
+  };
+  if (o_f32) all(std::true_type{});
+  else all(std::false_type{});
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     red_k[slot][f0 + i] = pk[i];
