@@ -53,6 +53,14 @@ def test_workspace_sizes(lib):
     assert f(1, 256, 30, 8, 128, 0) == 0       # Hq % Hkv != 0
     assert lib.anchor_attn_plan_capacity(1, 300, 64, 128) == 5 * 3
     assert lib.anchor_attn_plan_capacity(1, 300, 48, 128) == 0
+    # empty and degenerate shapes: no rows, no tokens, no heads, heads that do
+    # not group, more than 2^31 - 1 tokens in all
+    for shape in [(0, 256, 4, 2, 128), (1, 0, 4, 2, 128), (1, 256, 0, 1, 128), (1, 256, 4, 0, 128),
+                  (1, 256, 3, 2, 128), (2, 1 << 30, 4, 2, 128)]:
+        for for_bwd in (0, 1):
+            assert f(*shape, for_bwd) == 0, shape
+    # the smallest shape (one row of one token: the anchor alone) is valid
+    assert f(1, 1, 1, 1, 64, 1) > 0
 
 
 def test_argument_errors_before_launch(lib):

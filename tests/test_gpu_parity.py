@@ -77,6 +77,8 @@ def _mode_cases():
         ("anchor_continuous_mixed", 2, 640, 2, 2, 128, [[1, 300, 1, 337], [639]], 5e5, True, CP),
         ("anchor_continuous_grid_after", 2, 700, 4, 2, 64, [[128] * 5 + [59], [699]], 1e4, True, CP | GR),
         ("noncausal_grid_after", 1, 600, 2, 2, 128, [[100, 1, 250, 248]], 1e4, False, GR),
+        ("anchor_only_s1", 2, 1, 2, 2, 64, [[], []], 1e4, True, 0),           # rows of the anchor alone
+        ("anchor_only_s1_grid_after", 2, 1, 2, 2, 128, [[], []], 1e4, True, GR),
     ]
 
 
