@@ -438,14 +438,30 @@ __global__ __launch_bounds__(1024) void k_bwd_anchor(
   const int parts = 1024 / D;
   const int d = threadIdx.x % D, part = threadIdx.x / D;
   const bool bad = status[0] != kStatusOk;
-  float sk = 0.f, sv = 0.f;
+  // eight running sums per quantity: eight independent loads in flight per
+  // thread instead of one dependent chain
+  constexpr int U = 8;
+  float ak[U], av[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) { ak[u] = 0.f; av[u] = 0.f; }
   for (int hq = hkv * group; hq < (hkv + 1) * group; ++hq) {
     const size_t base = ((size_t)b * Hq + hq) * nblk * D + d;
-    for (int n = part; n < nblk; n += parts) {
-      sk += part_dk[base + (size_t)n * D];
-      sv += part_dv[base + (size_t)n * D];
+    int n = part;
+    for (; n + (U - 1) * parts < nblk; n += U * parts) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        ak[u] += part_dk[base + (size_t)(n + u * parts) * D];
+        av[u] += part_dv[base + (size_t)(n + u * parts) * D];
+      }
+    }
+    for (; n < nblk; n += parts) {
+      ak[0] += part_dk[base + (size_t)n * D];
+      av[0] += part_dv[base + (size_t)n * D];
     }
   }
+  float sk = 0.f, sv = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) { sk += ak[u]; sv += av[u]; }
   red[0][threadIdx.x] = sk;
   red[1][threadIdx.x] = sv;
   __syncthreads();
