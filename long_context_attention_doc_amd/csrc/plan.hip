@@ -105,6 +105,45 @@ __device__ __forceinline__ uint8_t tile_kind(const int* slo, const int* shi, int
   return all_full ? kTileFull : ((anchor_col && !any_doc) ? kTileAnchor : kTilePartial);
 }
 
+// The same kind in O(log BM) for rows whose intervals are monotone: lo and hi
+// non-decreasing over the rows, every row but the first one nonempty (lo <=
+// hi; only the anchor row, a row's first token, is empty), and with an
+// anchor no interval reaching column 0.  Every
+// valid layout is: documents are contiguous segments, a query's interval
+// starts at its document's first token and ends at itself (causal) or at its
+// document's last token.  Then the rows that see a key at or after c0 are a
+// suffix (hi rises) and those that see one at or before c1 a prefix (lo
+// rises), so some row sees a key of the tile exactly when the first row of
+// the suffix starts at or before c1; all rows see all of them exactly when
+// the last row starts at or before the tile's first document key and the
+// first row ends at or after its last key.
+__device__ __forceinline__ uint8_t tile_kind_monotone(const int* slo, const int* shi, int r,
+                                                      int nrows, int BM, int c0, int BN, int S,
+                                                      int anchor) {
+  if (nrows <= 0) return 0;
+  const int c1 = min(S, c0 + BN) - 1;
+  const bool cols_exist = (c0 + BN) <= S;
+  const bool anchor_col = anchor && c0 == 0;
+  // the first row may be the empty anchor row: it sees only column 0
+  const int rf = r + (slo[r] > shi[r] ? 1 : 0);
+  const int re = r + nrows;            // rows rf .. re-1 are nonempty
+  // first row in [rf, re) with hi >= c0 (re if none)
+  int a = rf, z = re;
+  while (a < z) {
+    const int m = (a + z) >> 1;
+    if (shi[m] >= c0) z = m; else a = m + 1;
+  }
+  const bool any_doc = a < re && slo[a] <= c1 && c0 <= c1;
+  const bool any_live = any_doc || anchor_col;
+  if (!any_live) return 0;
+  // every row sees every column: BM rows, BN columns, the first row not the
+  // anchor row, lo of the last row at most the first document key of the tile
+  // (c0 + 1 when column 0 is the anchor's), hi of the first row at least c1
+  const bool all_full = nrows == BM && cols_exist && rf == r &&
+                        slo[r + nrows - 1] <= c0 + (anchor_col ? 1 : 0) && shi[r] >= c1;
+  return all_full ? kTileFull : ((anchor_col && !any_doc) ? kTileAnchor : kTilePartial);
+}
+
 // One workgroup per (row b, block of RB rows starting at origin + rb*RB):
 // with cu given, the token tables of its rows (the first block of a row also
 // those of the rows before origin) and its share of the layout checks;
@@ -155,6 +194,18 @@ __global__ __launch_bounds__(256) void k_plan_kinds(
     }
   }
   __syncthreads();
+  // do this block's intervals allow the O(log BM) kinds?  (they do for every
+  // valid layout; the per-row scan is kept for anything else)
+  __shared__ int not_monotone;
+  if (threadIdx.x == 0) not_monotone = 0;
+  __syncthreads();
+  for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
+    if (r + 1 < nrows && (slo[r] > slo[r + 1] || shi[r] > shi[r + 1] || slo[r + 1] > shi[r + 1]))
+      not_monotone = 1;
+    if (anchor && slo[r] < 1) not_monotone = 1;   // column 0 is the anchor's, never a document key
+  }
+  __syncthreads();
+  const bool monotone = not_monotone == 0;
   for (int pl = 0; pl < 2; ++pl) {
     const KindsOut& P = pl ? p1 : p0;
     if (!P.kinds) continue;
@@ -165,7 +216,9 @@ __global__ __launch_bounds__(256) void k_plan_kinds(
       const int n = max(0, min(P.BM, nrows - rr));
       int cnt = 0;
       for (int kt = threadIdx.x; kt < P.nk; kt += blockDim.x) {
-        const uint8_t kind = tile_kind(slo, shi, rr, n, P.BM, origin + kt * P.BN, P.BN, S, anchor);
+        const uint8_t kind =
+            monotone ? tile_kind_monotone(slo, shi, rr, n, P.BM, origin + kt * P.BN, P.BN, S, anchor)
+                     : tile_kind(slo, shi, rr, n, P.BM, origin + kt * P.BN, P.BN, S, anchor);
         if (P.key_major) {
           P.kinds[((size_t)b * P.nk + kt) * P.nq + qt] = kind;
           if (kind) atomicAdd(P.cnt + (size_t)b * P.nk + kt, 1);
