@@ -281,12 +281,31 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ cnt, 
 }
 
 // One wave per row: the live entries of the row, ascending, at ptr[row].
-__global__ void k_row_compact(const uint8_t* __restrict__ m, int rows, int n,
-                              const int32_t* __restrict__ ptr, int32_t* __restrict__ idx,
-                              uint8_t* __restrict__ kind, int32_t* __restrict__ pack) {
-  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+// The rows of two dense kind matrices (a plan's query-major and key-major
+// ones) can go in one launch: waves past the first matrix's rows take the
+// second's (rows2 = 0 for one matrix).
+struct CompactRows {
+  const uint8_t* m;       // [rows][n]
+  int rows, n;
+  const int32_t* ptr;
+  int32_t* idx;
+  uint8_t* kind;
+  int32_t* pack;          // may be null
+};
+__global__ void k_row_compact(CompactRows a, CompactRows c) {
+  int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+  if (row >= a.rows) {   // wave-uniform
+    row -= a.rows;
+    a = c;
+    if (row >= a.rows) return;
+  }
+  const uint8_t* __restrict__ m = a.m;
+  const int n = a.n;
+  const int32_t* __restrict__ ptr = a.ptr;
+  int32_t* __restrict__ idx = a.idx;
+  uint8_t* __restrict__ kind = a.kind;
+  int32_t* __restrict__ pack = a.pack;
   const uint8_t* r = m + (size_t)row * n;
   int w = ptr[row];
   for (int i0 = 0; i0 < n; i0 += 64) {
@@ -310,16 +329,26 @@ __global__ void k_row_compact(const uint8_t* __restrict__ m, int rows, int n,
 // keep the natural order, head after head.
 // With ptr not null, the workgroup after the last one needed for the order
 // also writes the plan's exclusive scan of the counts (ptr, *total_out), so a
-// query-major plan needs no separate scan launch.
+// query-major plan needs no separate scan launch; with cnt2 not null, the
+// workgroup after that one writes the exclusive scan of a second count array
+// (the key-major plan's, ptr2, *total2).
 constexpr int kMaxLptTiles = 16384;
 __global__ __launch_bounds__(256) void k_tile_order(const int32_t* __restrict__ cnt, int n,
                                                    int32_t* __restrict__ order,
                                                    int32_t* __restrict__ ptr,
-                                                   int32_t* __restrict__ total_out) {
+                                                   int32_t* __restrict__ total_out,
+                                                   const int32_t* __restrict__ cnt2, int n2,
+                                                   int32_t* __restrict__ ptr2,
+                                                   int32_t* __restrict__ total2) {
   __shared__ int w[kMaxLptTiles];
   __shared__ int wmax[4], wsum[4];
-  if (ptr && blockIdx.x == gridDim.x - 1) {
+  const int n_order = (n + 255) / 256;   // workgroups of the order
+  if (ptr && (int)blockIdx.x == n_order) {
     block_scan<256>(cnt, n, ptr, total_out, w);
+    return;
+  }
+  if (cnt2 && (int)blockIdx.x == n_order + (ptr ? 1 : 0)) {
+    block_scan<256>(cnt2, n2, ptr2, total2, w);
     return;
   }
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -365,7 +394,8 @@ __global__ __launch_bounds__(256) void k_tile_order(const int32_t* __restrict__ 
 
 hipError_t launch_tile_order(const int32_t* cnt, int n, int32_t* order, hipStream_t st) {
   hipLaunchKernelGGL(k_tile_order, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cnt, n,
-                     order, (int32_t*)nullptr, (int32_t*)nullptr);
+                     order, (int32_t*)nullptr, (int32_t*)nullptr, (const int32_t*)nullptr, 0,
+                     (int32_t*)nullptr, (int32_t*)nullptr);
   return hipGetLastError();
 }
 
@@ -408,25 +438,26 @@ hipError_t launch_plans(const PlanSrc& src, int B, int S, int anchor, const Plan
   hipLaunchKernelGGL(k_plan_kinds, dim3(B * nrb), dim3(256), 0, st, src.cu, src.n_seg, B, S,
                      src.causal, src.mode, anchor, src.tt.pos, src.tt.lo, src.tt.hi, src.status, RB,
                      nrb, origin, o[0], o[1]);
-  if (pq) {
-    const int n = B * pq->nq;
-    if (pq->order) {
-      // work order and scan in one launch (the scan takes the last workgroup)
-      hipLaunchKernelGGL(k_tile_order, dim3((unsigned)((n + 255) / 256) + 1), dim3(256), 0, st,
-                         pq->cntq, n, pq->order, pq->qptr, pq->n_live);
-    } else {
-      hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pq->cntq, n, pq->qptr, pq->n_live);
-    }
-    hipLaunchKernelGGL(k_row_compact, dim3((n + 3) / 4), dim3(256), 0, st, pq->kinds, n, pq->nk,
-                       pq->qptr, pq->kidx, pq->kkind, pq->kpack);
+  const int nq_rows = pq ? B * pq->nq : 0;   // query-major plan: B*nq rows of nk kinds
+  const int nk_rows = pk ? B * pk->nk : 0;   // key-major plan: B*nk rows of nq kinds
+  int32_t* const k_total = pq ? (int32_t*)nullptr : (pk ? pk->n_live : nullptr);
+  if (pq && pq->order) {
+    // the query-major work order, then both plans' scans, in one launch (the
+    // scans take the workgroups after the order's)
+    const unsigned grid = (unsigned)((nq_rows + 255) / 256) + 1 + (pk ? 1 : 0);
+    hipLaunchKernelGGL(k_tile_order, dim3(grid), dim3(256), 0, st, pq->cntq, nq_rows, pq->order,
+                       pq->qptr, pq->n_live, pk ? pk->cntk : (const int32_t*)nullptr, nk_rows,
+                       pk ? pk->kptr : (int32_t*)nullptr, k_total);
+  } else {
+    if (pq) hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pq->cntq, nq_rows, pq->qptr, pq->n_live);
+    if (pk) hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pk->cntk, nk_rows, pk->kptr, k_total);
   }
-  if (pk) {
-    const int n = B * pk->nk;
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, pk->cntk, n, pk->kptr,
-                       pq ? (int32_t*)nullptr : pk->n_live);
-    hipLaunchKernelGGL(k_row_compact, dim3((n + 3) / 4), dim3(256), 0, st, pk->kinds_t, n, pk->nq,
-                       pk->kptr, pk->qidx, pk->qkind, pk->qpack);
-  }
+  // both plans' CSR in one launch, one wave per row
+  CompactRows cq{}, ck{};
+  if (pq) cq = CompactRows{pq->kinds, nq_rows, pq->nk, pq->qptr, pq->kidx, pq->kkind, pq->kpack};
+  if (pk) ck = CompactRows{pk->kinds_t, nk_rows, pk->nq, pk->kptr, pk->qidx, pk->qkind, pk->qpack};
+  const int rows = nq_rows + nk_rows;
+  hipLaunchKernelGGL(k_row_compact, dim3((rows + 3) / 4), dim3(256), 0, st, cq, ck);
   return hipGetLastError();
 }
 
