@@ -214,7 +214,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="64k",
                     help="tiny | 8k | 64k | 128k_gqa | short_docs | 64k_ulysses8 (one GPU's head share of 64K "
                          "over 8 GPUs) (default: 64k, the headline)")
