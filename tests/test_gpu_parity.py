@@ -29,6 +29,7 @@ def _small_cases():
         ("noncausal", 1, 600, 2, 2, 128, [[100, 1, 250, 248]], 1e4, False),
         ("s2", 2, 2, 2, 2, 64, [[1], [1]], 1e4, True),
         ("gqa8", 1, 300, 8, 1, 64, [[150, 149]], 1e4, True),
+        ("b4_mqa_d128", 4, 333, 4, 1, 128, [[332], [1] * 332, [100, 232], [64, 64, 64, 64, 76]], 5e6, True),
     ]
 
 
