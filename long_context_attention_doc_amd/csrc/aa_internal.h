@@ -260,7 +260,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 __device__ __forceinline__ lds_void* lds_ptr(uint32_t a) { return (lds_void*)(uintptr_t)a; }
 
-// Direct global -> LDS copy (global_load_lds_dwordx4) of a [ROWS][D] tile
+// Direct copy of 16 bytes per lane from global memory into LDS
+// (buffer_load_dwordx4 ... lds): lane L reads base + voff and writes the 16
+// bytes at lds + 16 L.  `base` must be wave-uniform (it is read into scalar
+// registers).  The buffer form is used rather than global_load_lds: with a
+// global-segment LDS load in flight the compiler assumes the LDS counter may
+// complete out of order and waits for every outstanding LDS read
+// (lgkmcnt(0)) before using any of them, so no operand read can be issued
+// ahead of its MFMA; the buffer form counts only in the vector-memory
+// counter and leaves the LDS reads' waits exact.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, lds_void* lds) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  // raw buffer: stride 0, 2^31 - 1 bytes addressable from `base`, the data
+  // format word of a plain dword buffer
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(ub, 0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 0, 0);
+}
+
+// Direct global -> LDS copy (dma16 above) of a [ROWS][D] tile
 // into the swizzled layout: lane L of a wave's instruction writes the 16
 // bytes at LDS chunk base + L, so each lane fetches the logical chunk that
 // the swizzle places there.  Global rows row0 .. row0+ROWS-1 are clamped to
@@ -300,8 +320,7 @@ struct DirectTile {
       const char* tbase = (const char*)(gbase + (size_t)row0 * row_stride);
 #pragma unroll
       for (int u = 0; u < ITERS; ++u)
-        __builtin_amdgcn_global_load_lds((const void*)(tbase + off[u]),
-                                         lds_ptr(lds_tile + (wave * ITERS + u) * 64 * 16), 16, 0, 0);
+        dma16(tbase, off[u], lds_ptr(lds_tile + (wave * ITERS + u) * 64 * 16));
     } else {
       const int rb = min(row0, row_max);
       const char* cbase = (const char*)(gbase + (size_t)rb * row_stride);
@@ -310,9 +329,8 @@ struct DirectTile {
         int row, chunk;
         locate(u, row, chunk);
         const int r = min(row0 + row, row_max) - rb;
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(cbase + (uint32_t)((r * row_stride + chunk * 8) * sizeof(bf16))),
-            lds_ptr(lds_tile + (wave * ITERS + u) * 64 * 16), 16, 0, 0);
+        dma16(cbase, (uint32_t)((r * row_stride + chunk * 8) * sizeof(bf16)),
+              lds_ptr(lds_tile + (wave * ITERS + u) * 64 * 16));
       }
     }
   }
@@ -325,9 +343,7 @@ struct DirectTile {
       const char* tbase = (const char*)(gbase + (size_t)row0 * row_stride);
 #pragma unroll
       for (int u = 0; u < ITERS; ++u)
-        __builtin_amdgcn_global_load_lds((const void*)(tbase + off[u]),
-                                         (lds_void*)(lds_tile + (wave * ITERS + u) * 64 * 8), 16, 0,
-                                         0);
+        dma16(tbase, off[u], (lds_void*)(lds_tile + (wave * ITERS + u) * 64 * 8));
     } else {
       // Rows past row_max read row_max.  The offsets are unsigned, so they are
       // taken from min(row0, row_max): a tile may start past the last row
@@ -339,9 +355,8 @@ struct DirectTile {
         int row, chunk;
         locate(u, row, chunk);
         const int r = min(row0 + row, row_max) - rb;
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(cbase + (uint32_t)((r * row_stride + chunk * 8) * sizeof(bf16))),
-            (lds_void*)(lds_tile + (wave * ITERS + u) * 64 * 8), 16, 0, 0);
+        dma16(cbase, (uint32_t)((r * row_stride + chunk * 8) * sizeof(bf16)),
+              (lds_void*)(lds_tile + (wave * ITERS + u) * 64 * 8));
       }
     }
   }

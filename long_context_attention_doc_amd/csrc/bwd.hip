@@ -125,9 +125,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
       // the record index is wave-uniform: keep its arithmetic scalar
       const int ri = __builtin_amdgcn_readfirstlane((b * Hq + hq) * nblk + qt);
       const float* rec = qstats + (size_t)ri * (4 * BM);
-      __builtin_amdgcn_global_load_lds((const void*)(rec + 4 * lane),
-                                       lds_ptr(lds_addr(&s_st[0][0][0]) + buf * (4 * BM * 4)), 16, 0,
-                                       0);
+      dma16(rec, 16 * lane, lds_ptr(lds_addr(&s_st[0][0][0]) + buf * (4 * BM * 4)));
     }
   };
 
