@@ -198,12 +198,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[4 * g + r], scale_log2, -l4[r]));
       if (need_mask) {
-        const int4 lo4 = __builtin_bit_cast(int4, *(const f32x4*)(stc + 2 * BM + q0));
-        const int4 hi4 = __builtin_bit_cast(int4, *(const f32x4*)(stc + 3 * BM + q0));
-        pv[0] = ((key >= lo4.x) & (key <= hi4.x)) ? pv[0] : 0.f;
-        pv[1] = ((key >= lo4.y) & (key <= hi4.y)) ? pv[1] : 0.f;
-        pv[2] = ((key >= lo4.z) & (key <= hi4.z)) ? pv[2] : 0.f;
-        pv[3] = ((key >= lo4.w) & (key <= hi4.w)) ? pv[3] : 0.f;
+        // Read as float vectors and reinterpreted in registers: a typed
+        // vector load keeps its type-based alias information, and without
+        // it the compiler would first wait for the next half tile's direct
+        // loads to land (they may write any LDS it cannot tell apart).
+        const f32x4 lo4 = *(const f32x4*)(stc + 2 * BM + q0);
+        const f32x4 hi4 = *(const f32x4*)(stc + 3 * BM + q0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          pv[r] = ((key >= __float_as_int(lo4[r])) & (key <= __float_as_int(hi4[r]))) ? pv[r] : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
