@@ -252,6 +252,33 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int r0, int f0) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The same operand addressed by XOR.  In a swizzled row the byte offset of
+// chunk c is that of chunk (c mod 4) XOR 16 (c - c mod 4): the chunk's high
+// bits only flip address bits 4.. of the chunk field, which the row part
+// (a multiple of 2D bytes) and the low chunk bits never touch.  So one
+// register per lane, tile_off + the offset of (r0 = 0, f0 = 0), serves every
+// 32-feature block f0 with one XOR, instead of one precomputed register per
+// block.  o0, o8: this lane's byte offsets of the two 8-row pieces
+// (tr_lane_offsets); tile: the tile's LDS object; r0 a multiple of 16, f0 of
+// 32.
+template <int D>
+__device__ __forceinline__ void tr_lane_offsets(uint32_t& o0, uint32_t& o8) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, t = lane & 15;
+  const int row = 4 * (g >> 1) + (t >> 2);
+  const int f = 16 * (g & 1) + 4 * (t & 3);
+  o0 = 2u * SwzTile<D>::off(row, f);
+  o8 = 2u * SwzTile<D>::off(row + 8, f);
+}
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand_x(const char* tile, uint32_t b0, uint32_t b8, int r0,
+                                               int f0) {
+  const uint32_t x = 2u * f0, rb = 2u * r0 * D;
+  const bf16x4 a = __builtin_bit_cast(bf16x4, ds_read_tr((const bf16*)(tile + ((b0 ^ x) + rb))));
+  const bf16x4 b = __builtin_bit_cast(bf16x4, ds_read_tr((const bf16*)(tile + ((b8 ^ x) + rb))));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // 32-bit LDS address of a __shared__ location, and back.

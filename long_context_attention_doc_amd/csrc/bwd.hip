@@ -158,6 +158,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   if (hq < h_end) issue(0, hq, packed_idx(qpack[e]), 0);
   // one step per half tile, unrolled by buffer
   int kro = (32 * wave + col) * KLD + 8 * h;
+  // Byte offsets inside a buffer of QG: row reads of (row col, chunk h),
+  // the chunk 2kk + h being that offset XOR 32 kk (see tr_operand_x), and
+  // the transposing reads' two pieces.
+  const uint32_t o_row = 2u * T::chunk_off(col, h);
+  uint32_t o_tr0, o_tr8;
+  tr_lane_offsets<D>(o_tr0, o_tr8);
+  const char* qg = (const char*)&QG[0][0];
   int cur = 0;
   while (hq < h_end) {
     const bool need_mask =
@@ -172,8 +179,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     // eight reads below stay one register plus immediate offsets (hoisted out
     // of the loop they would take eight registers)
     asm volatile("" : "+v"(kro));
-    const bf16* Qc = QG[cur];
-    const bf16* Gc = Qc + BH * D;
+    // this step's buffer: the Q half tile, then the dO half tile
+    constexpr uint32_t kBuf = 2 * 2 * BH * D, kG = 2 * BH * D;   // bytes
+    uint32_t b_row = cur * kBuf + o_row, b_tr0 = cur * kBuf + o_tr0, b_tr8 = cur * kBuf + o_tr8;
+    // opaque per step, so that the compiler keeps three registers and one
+    // XOR per read instead of hoisting every XORed offset out of the loop
+    asm volatile("" : "+v"(b_row), "+v"(b_tr0), "+v"(b_tr8));
     const float* stc = &s_st[cur][0][0] + half * BH;
 
     // S = Q K^T, dP = dO V^T for the 32 queries: columns = this wave's keys.
@@ -182,10 +193,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     for (int j = 0; j < 16; ++j) { sp[j] = 0.f; dp[j] = 0.f; }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const int off = T::chunk_off(col, 2 * kk + h);
+      const uint32_t o = b_row ^ (32u * kk);
       const bf16x8 kb = *(const bf16x8*)(Ks + kro + 16 * kk);
-      sp = mfma32(*(const bf16x8*)(Qc + off), kb, sp);
-      dp = mfma32(*(const bf16x8*)(Gc + off), vf[kk], dp);
+      sp = mfma32(*(const bf16x8*)(qg + o), kb, sp);
+      dp = mfma32(*(const bf16x8*)(qg + o + kG), vf[kk], dp);
     }
     // P = exp2(s * scale_log2 - lse_log2), dS = P (dP - Dv).
     bf16x8 pb[2], db_[2];
@@ -220,9 +231,19 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     for (int dblk = 0; dblk < NDB; ++dblk)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        dva[dblk] = mfma32(tr_operand<D>(Gc, 16 * c, 32 * dblk), pb[c], dva[dblk]);
-        dka[dblk] = mfma32(tr_operand<D>(Qc, 16 * c, 32 * dblk), db_[c], dka[dblk]);
+        dva[dblk] = mfma32(tr_operand_x<D>(qg + kG, b_tr0, b_tr8, 16 * c, 32 * dblk), pb[c], dva[dblk]);
+        dka[dblk] = mfma32(tr_operand_x<D>(qg, b_tr0, b_tr8, 16 * c, 32 * dblk), db_[c], dka[dblk]);
       }
+    // Schedule of these products: the first two operands' reads, then each
+    // MFMA followed by the reads of the operand two MFMAs later, so that two
+    // reads are in flight behind every product (left to itself the compiler
+    // reads each operand right before its MFMA and waits for it).
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // 4 LDS reads
+#pragma unroll
+    for (int i = 0; i < 4 * NDB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // 1 MFMA
+      if (i + 2 < 4 * NDB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+    }
     e = e1; hq = h1; half = half1;
     cur ^= 1;
   }
