@@ -359,6 +359,12 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_bwd_dq(
   if (e_first < e_end && packed_kind(kpack[e_first]) == kTileAnchor) ++e_first;
   const int n_tiles = e_end - e_first;
   if (n_tiles > 0) issue(0, packed_idx(kpack[e_first]));
+  // Byte offsets inside a K/V tile: row reads of (row col, chunk h), chunk
+  // 2kk + h being that offset XOR 32 kk (see tr_operand_x), and the
+  // transposing reads' two pieces.
+  const uint32_t o_row = 2u * T::chunk_off(col, h);
+  uint32_t o_tr0, o_tr8;
+  tr_lane_offsets<D>(o_tr0, o_tr8);
   // tile loop unrolled by two: every LDS address of a buffer is base + constant
   auto step = [&](auto bufc, int i) {
     constexpr int BUF = decltype(bufc)::value;
@@ -371,8 +377,12 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_bwd_dq(
     wait_direct_loads();
     __syncthreads();                 // tile i visible; the other buffer is free
     if (more) issue(BUF ^ 1, packed_idx(ent_next));
-    const bf16* Kc = BUF ? Ks1 : Ks0;
-    const bf16* Vc = BUF ? Vs1 : Vs0;
+    const char* Kc = (const char*)(BUF ? Ks1 : Ks0);
+    const char* Vc = (const char*)(BUF ? Vs1 : Vs0);
+    // opaque per step, so that the compiler keeps three registers and one
+    // XOR per read instead of hoisting every XORed offset out of the loop
+    uint32_t b_row = o_row, b_tr0 = o_tr0, b_tr8 = o_tr8;
+    asm volatile("" : "+v"(b_row), "+v"(b_tr0), "+v"(b_tr8));
 
     // One 32-key block at a time: S^T = K Q^T, dP^T = V dO^T (rows = keys,
     // columns = this wave's queries), dS^T, then dQ^T += K^T dS^T.
@@ -386,9 +396,9 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_bwd_dq(
       for (int j = 0; j < 16; ++j) { st[j] = 0.f; dpt[j] = 0.f; }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const int off = T::chunk_off(kb * 32 + col, 2 * kk + h);
-        st = mfma32(*(const bf16x8*)(Kc + off), qf[kk], st);
-        dpt = mfma32(*(const bf16x8*)(Vc + off), gf[kk], dpt);
+        const uint32_t o = (b_row ^ (32u * kk)) + 2u * 32 * kb * D;
+        st = mfma32(*(const bf16x8*)(Kc + o), qf[kk], st);
+        dpt = mfma32(*(const bf16x8*)(Vc + o), gf[kk], dpt);
       }
       // P^T = exp2(s * scale_log2 - lse_log2) in place of the scores
 #pragma unroll
@@ -408,7 +418,7 @@ __global__ __launch_bounds__(kFwdThreads, kFwdBlocksPerCU) void k_bwd_dq(
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          acc[db] = mfma32(tr_operand<D>(Kc, 32 * kb + 16 * c, 32 * db), dsb[c], acc[db]);
+          acc[db] = mfma32(tr_operand_x<D>(Kc, b_tr0, b_tr8, 32 * kb + 16 * c, 32 * db), dsb[c], acc[db]);
     }
   };
   for (int i = 0; i < n_tiles; i += 2) {
