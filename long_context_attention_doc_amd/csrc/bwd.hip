@@ -234,15 +234,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
         dva[dblk] = mfma32(tr_operand_x<D>(qg + kG, b_tr0, b_tr8, 16 * c, 32 * dblk), pb[c], dva[dblk]);
         dka[dblk] = mfma32(tr_operand_x<D>(qg, b_tr0, b_tr8, 16 * c, 32 * dblk), db_[c], dka[dblk]);
       }
-    // Schedule of these products: the first two operands' reads, then each
-    // MFMA followed by the reads of the operand two MFMAs later, so that two
-    // reads are in flight behind every product (left to itself the compiler
-    // reads each operand right before its MFMA and waits for it).
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // 4 LDS reads
+    // Schedule of these products: the first three operands' reads, then each
+    // MFMA followed by the reads of the operand three MFMAs later, so that
+    // three operands are in flight behind every product (left to itself the
+    // compiler reads each operand right before its MFMA and waits for it).
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // 6 LDS reads
 #pragma unroll
     for (int i = 0; i < 4 * NDB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // 1 MFMA
-      if (i + 2 < 4 * NDB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+      if (i + 3 < 4 * NDB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
     }
     e = e1; hq = h1; half = half1;
     cur ^= 1;
