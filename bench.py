@@ -37,13 +37,25 @@ KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4.0, "bwd_dkdv": 8.0, "bwd_dq": 6.0}
 KERNEL_SOURCE = {"fwd": "fwd.hip", "bwd_dkdv": "bwd.hip", "bwd_dq": "bwd.hip"}
 
 
+def _code_text(path: str) -> bytes:
+    """A source file's code without its comments, whitespace runs collapsed:
+    editing a comment leaves it (and so the hash below) unchanged."""
+    t = open(path, encoding="utf-8").read()
+    t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+    t = re.sub(r"//[^\n]*", " ", t)
+    return " ".join(t.split()).encode()
+
+
 def _src_hash(kernel: str) -> str:
-    """Hash of the kernel's source file followed by its extra build flags (none
-    for most sources), so a counter summary goes stale when either changes."""
+    """Hash of the code of the kernel's source file and of the header its
+    kernels inline (aa_internal.h), followed by the file's extra build flags
+    (none for most sources), so a counter summary goes stale when any of them
+    changes."""
     from long_context_attention_doc_amd.build import SOURCE_FLAGS
     name = KERNEL_SOURCE[kernel]
-    p = os.path.join(ROOT, "long_context_attention_doc_amd", "csrc", name)
-    h = hashlib.sha256(open(p, "rb").read())
+    csrc = os.path.join(ROOT, "long_context_attention_doc_amd", "csrc")
+    h = hashlib.sha256(_code_text(os.path.join(csrc, name)))
+    h.update(b"\0" + _code_text(os.path.join(csrc, "aa_internal.h")))
     h.update(" ".join(SOURCE_FLAGS.get(name, [])).encode())
     return h.hexdigest()[:16]
 

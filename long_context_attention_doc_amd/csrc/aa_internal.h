@@ -362,7 +362,8 @@ struct DirectTile {
     }
   }
   // The tile base is uniform and the offsets are 32-bit, so every load takes
-  // the scalar-base + vector-offset form with its LDS address in M0.
+  // the buffer descriptor (scalar) + vector-offset form with its LDS address
+  // in M0.
   __device__ __forceinline__ void load(bf16* lds_tile, const bf16* gbase, size_t row_stride,
                                        int row0, int row_max) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -22,7 +22,7 @@
 //     is streamed (every query tile reads it again), so it is rotated once
 //     by the RoPE pass before this kernel.
 //   * K and V tiles go straight from global memory into a ring of LDS
-//     buffers (global_load_lds) in a row-major layout with an XOR swizzle; K
+//     buffers (direct buffer loads to LDS) in a row-major layout with an XOR swizzle; K
 //     is read row-wise (A operand of S^T), V with transposing LDS reads
 //     (A operand V^T of O^T = V^T P^T).  Up to kFwdStages-1 tiles are in
 //     flight while the current tile is computed.

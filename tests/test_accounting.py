@@ -53,14 +53,16 @@ def test_bench_workloads_bound(name, bound):
 
 def test_counter_summary_goes_stale_with_source_or_build_flags(monkeypatch, tmp_path):
     """bench.py reports a kernel's HBM traffic from a committed counter summary
-    only while the summary's recorded hash matches the kernel's source file
-    and its extra build flags; a change of either makes it null."""
+    only while the summary's recorded hash matches the code of the kernel's
+    source file and of the shared kernel header, and its extra build flags; a
+    change of any of them makes it null, an edited comment does not."""
     import bench
     from long_context_attention_doc_amd import build as B
     csrc = tmp_path / "long_context_attention_doc_amd" / "csrc"
     csrc.mkdir(parents=True)
     (tmp_path / "profiles").mkdir()
-    (csrc / "bwd.hip").write_text("// kernel source v1\n")
+    (csrc / "bwd.hip").write_text("// kernel source\nint x = 1;\n")
+    (csrc / "aa_internal.h").write_text("/* shared header */ int y = 1;\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(B, "SOURCE_FLAGS", {"bwd.hip": ["-mllvm", "-some-option"]})
     h = bench._src_hash("bwd_dkdv")
@@ -72,6 +74,11 @@ def test_counter_summary_goes_stale_with_source_or_build_flags(monkeypatch, tmp_
     assert bench._src_hash("bwd_dkdv") != h
     assert bench._traffic("bwd_dkdv", "64k") is None
     monkeypatch.setattr(B, "SOURCE_FLAGS", {"bwd.hip": ["-mllvm", "-some-option"]})
-    (csrc / "bwd.hip").write_text("// kernel source v2\n")          # source changed
+    (csrc / "bwd.hip").write_text("// kernel source, comment edited\nint  x = 1;\n")
+    assert bench._traffic("bwd_dkdv", "64k") == 1.5e9              # comments and spacing only
+    (csrc / "aa_internal.h").write_text("/* shared header */ int y = 2;\n")
+    assert bench._traffic("bwd_dkdv", "64k") is None                # header code changed
+    (csrc / "aa_internal.h").write_text("/* shared header */ int y = 1;\n")
+    (csrc / "bwd.hip").write_text("// kernel source\nint x = 2;\n")  # source code changed
     assert bench._traffic("bwd_dkdv", "64k") is None
 
