@@ -156,7 +156,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
   int e, hq, half = 0;
   first(e, hq);
   if (hq < h_end) issue(0, hq, packed_idx(qpack[e]), 0);
-  // one step per half tile, unrolled by buffer
+  // one step per half tile; the buffer of a step is `cur` (unrolling the loop
+  // by buffer would need a second set of address registers and spills)
   int kro = (32 * wave + col) * KLD + 8 * h;
   // Byte offsets inside a buffer of QG: row reads of (row col, chunk h),
   // the chunk 2kk + h being that offset XOR 32 kk (see tr_operand_x), and
