@@ -254,13 +254,14 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int r0, int f0) {
 
 // The same operand addressed by XOR.  In a swizzled row the byte offset of
 // chunk c is that of chunk (c mod 4) XOR 16 (c - c mod 4): the chunk's high
-// bits only flip address bits 4.. of the chunk field, which the row part
-// (a multiple of 2D bytes) and the low chunk bits never touch.  So one
-// register per lane, tile_off + the offset of (r0 = 0, f0 = 0), serves every
-// 32-feature block f0 with one XOR, instead of one precomputed register per
-// block.  o0, o8: this lane's byte offsets of the two 8-row pieces
-// (tr_lane_offsets); tile: the tile's LDS object; r0 a multiple of 16, f0 of
-// 32.
+// bits only flip address bits of the chunk field that the row part (a
+// multiple of 2D bytes) and the low chunk bits never touch.  So one register
+// per lane and piece serves every 32-feature block f0 with one XOR, instead
+// of one precomputed register per block.  o0, o8 (tr_lane_offsets): this
+// lane's byte offsets of the two 8-row pieces for r0 = 0, f0 = 0.  b0, b8:
+// o0, o8 plus the byte offset of the tile inside `tile`, which must be a
+// multiple of 2D (a whole row) so that the XOR only meets the lane's own
+// chunk bits.  r0 a multiple of 16, f0 of 32.
 template <int D>
 __device__ __forceinline__ void tr_lane_offsets(uint32_t& o0, uint32_t& o8) {
   const int lane = threadIdx.x & 63;
