@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
         const f32x4 hi4 = *(const f32x4*)(stc + 3 * BM + q0);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          pv[r] = ((key >= __float_as_int(lo4[r])) & (key <= __float_as_int(hi4[r]))) ? pv[r] : 0.f;
+          pv[r] = ((int)(key >= __float_as_int(lo4[r])) & (int)(key <= __float_as_int(hi4[r]))) ? pv[r] : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
