@@ -318,6 +318,42 @@ def test_full_size_sampled(gpu_lib, wname):
     assert max(e_dq, e_dk, e_dv) <= G_TOL
 
 
+@pytest.mark.parametrize("seed,median,sigma", [(31, 256, 1.3), (32, 1024, 1.2), (33, 3000, 1.0)],
+                         ids=["median256", "median1024", "median3000"])
+def test_random_partitions_sampled(gpu_lib, seed, median, sigma):
+    """Seeded lognormal partitions other than the benchmark's (two rows with
+    different documents, GQA 8:2, 16K tokens), both tile grids against one
+    oracle evaluation; sampled rows and keys, as at full size."""
+    B, S, Hq, Hkv, D, base = 2, 16384, 8, 2, 128, 5e6
+    rows_len = tuple(tuple(W.sample_doc_lengths(S, median, sigma, 1, S - 1, seed * 10 + b)) for b in range(B))
+    w = W.Workload("random", B, S, Hq, Hkv, D, base, True, rows_len, 1100 + seed)
+    cu = w.cu_doc_lens
+    say(f"[random] seed {seed} median {median}: {[len(r) for r in rows_len]} documents")
+    q, k, v, do = W.make_tensors(B, S, Hq, Hkv, D, w.tensor_seed)
+    rng = np.random.default_rng(seed)
+    heads = list(range(Hq // Hkv))          # all query heads of kv group 0
+    rows = _sample_rows(w, rng, 24)
+    keys = _sample_keys(w, rng, 16)
+    say(f"[random] seed {seed} oracle on {len(rows)} rows, {len(keys)} keys")
+    o_ref, lse_ref, _, _ = oracle.forward(q, k, v, cu, base, heads=heads, rows=rows)
+    dq_r, dk_r, dv_r, _, _ = oracle.backward(q, k, v, do, cu, base, heads=heads, q_rows=rows, k_cols=keys)
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    for grid in (0, 16):                    # from the first token; after the anchor
+        o, lse = gpu_lib.anchor_attn_fwd(qc, kc, vc, cu, base, flags=grid)
+        dq, dk, dv = gpu_lib.anchor_attn_bwd(qc, kc, vc, o, lse, doc, cu, base, flags=grid)
+        torch.cuda.synchronize()
+        o_g = f64(o).reshape(B * S, Hq, D)[rows][:, heads]
+        lse_g = f64(lse).transpose(1, 0, 2).reshape(Hq, B * S)[heads][:, rows]
+        e_o = o_err(o_g, o_ref)
+        e_dq = rel_frob(f64(dq).reshape(B * S, Hq, D)[rows][:, heads], dq_r)
+        e_dk = rel_frob(f64(dk).reshape(B * S, Hkv, D)[keys][:, [0]], dk_r[:, [0]])
+        e_dv = rel_frob(f64(dv).reshape(B * S, Hkv, D)[keys][:, [0]], dv_r[:, [0]])
+        say(f"[random] seed {seed} grid {grid} O {e_o:.2e} dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
+        assert e_o <= O_TOL
+        assert np.abs(lse_g - lse_ref).max() <= LSE_TOL
+        assert max(e_dq, e_dk, e_dv) <= G_TOL
+
+
 def _long_doc_keys(w):
     """Keys of the row's longest document: its first tokens, the start of
     its second and third 128-key tiles, its middle and its last token."""
