@@ -318,13 +318,15 @@ def test_full_size_sampled(gpu_lib, wname):
     assert max(e_dq, e_dk, e_dv) <= G_TOL
 
 
-@pytest.mark.parametrize("seed,median,sigma", [(31, 256, 1.3), (32, 1024, 1.2), (33, 3000, 1.0)],
-                         ids=["median256", "median1024", "median3000"])
-def test_random_partitions_sampled(gpu_lib, seed, median, sigma):
+@pytest.mark.parametrize("seed,median,sigma,D", [(31, 256, 1.3, 128), (32, 1024, 1.2, 128),
+                                                 (33, 3000, 1.0, 128), (34, 700, 1.2, 64)],
+                         ids=["median256", "median1024", "median3000", "median700_d64"])
+def test_random_partitions_sampled(gpu_lib, seed, median, sigma, D):
     """Seeded lognormal partitions other than the benchmark's (two rows with
-    different documents, GQA 8:2, 16K tokens), both tile grids against one
-    oracle evaluation; sampled rows and keys, as at full size."""
-    B, S, Hq, Hkv, D, base = 2, 16384, 8, 2, 128, 5e6
+    different documents, GQA 8:2, 16K tokens, head_dim 128 and 64), both tile
+    grids against one oracle evaluation; sampled rows and keys, as at full
+    size."""
+    B, S, Hq, Hkv, base = 2, 16384, 8, 2, 5e6
     rows_len = tuple(tuple(W.sample_doc_lengths(S, median, sigma, 1, S - 1, seed * 10 + b)) for b in range(B))
     w = W.Workload("random", B, S, Hq, Hkv, D, base, True, rows_len, 1100 + seed)
     cu = w.cu_doc_lens
